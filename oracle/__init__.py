@@ -1,0 +1,318 @@
+"""Reference oracle for fused CSR neighbourhood attention.
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The HIP library never imports,
+links or calls it, and it imports nothing from the library.
+
+Two halves:
+
+* integer structure (plain numpy, exact): CSR by destination, degree
+  bucketing into light/heavy nodes with the heavy chunk table, the transposed
+  adjacency (CSC), and the 16x16 dense-tile census. These are the definitions
+  the preprocessor must reproduce bit for bit.
+* floating point (``oracle.c``, fp64, OpenMP over rows): Graph-Transformer
+  forward and backward and GATv2 forward, each materialising per-row edge
+  logits and using a two-pass softmax.
+
+Source: "On Efficient Scaling of GNNs via IO-Aware Layers Implementations",
+technical summary, Methodology (degree-aware tiling with a light/heavy split;
+fused CSR attention with an online-softmax forward and a log-sum-exp
+recompute backward; cached transposed adjacency; 16x16 block-sparse tiles).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (fp64, no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+               "-ffp-contract=off", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = C.CDLL(_LIB)
+        P = C.c_void_p
+        i64, i32, f64 = C.c_int64, C.c_int, C.c_double
+        lib.orc_gt_fwd.argtypes = [i64, P, P, i32, i32, P, P, P, f64, i64, P, P, P, P, P]
+        lib.orc_gatv2_fwd.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, i64, P, P, P, P, P]
+        lib.orc_gt_bwd_rows.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, i64, P, P, P, P, P, P]
+        lib.orc_gt_bwd_srcs.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, P, P, P, P, i64, P, P, P, P, P]
+        for f in (lib.orc_gt_fwd, lib.orc_gatv2_fwd, lib.orc_gt_bwd_rows, lib.orc_gt_bwd_srcs):
+            f.restype = C.c_int
+        lib.orc_num_threads.restype = C.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# integer structure
+# ---------------------------------------------------------------------------
+
+def csr_build(src, dst, n_nodes: int, add_self_loops: bool = True):
+    """CSR by destination from a COO edge list (edge src -> dst).
+
+    Row i holds the sources of i's in-edges in ascending order; duplicate
+    pairs are removed; with add_self_loops, (i, i) is present exactly once in
+    every row. Returns (indptr int32 [N+1], indices int32 [E])."""
+    n = int(n_nodes)
+    s = np.asarray(src, np.int64).ravel()
+    d = np.asarray(dst, np.int64).ravel()
+    if s.size and (s.min() < 0 or s.max() >= n or d.min() < 0 or d.max() >= n):
+        raise ValueError("edge endpoint out of range")
+    if add_self_loops:
+        s = np.concatenate([s, np.arange(n, dtype=np.int64)])
+        d = np.concatenate([d, np.arange(n, dtype=np.int64)])
+    keys = np.unique(d * n + s)
+    rows = keys // n
+    indices = (keys - rows * n).astype(np.int32)
+    indptr = np.zeros(n + 1, np.int64)
+    np.cumsum(np.bincount(rows, minlength=n), out=indptr[1:])
+    return indptr.astype(np.int32), indices
+
+
+def degrees(indptr) -> np.ndarray:
+    return np.diff(np.asarray(indptr, np.int64))
+
+
+def bucketing(indptr, threshold: int, chunk: int, waves: int):
+    """Degree-aware light/heavy split and heavy chunk-group table.
+
+    light = nodes with degree <= threshold, heavy = the rest, each ascending.
+    Each heavy node's edge range is cut into groups of chunk*waves edges (the
+    last may be short); a group is one workgroup whose waves each take one
+    chunk of <= chunk edges. partial_ofs[k]..partial_ofs[k+1] are the groups
+    (and partial-result slots) of heavy node k.
+
+    Returns dict: light int32 [n_light], heavy int32 [n_heavy],
+    groups int32 [n_groups, 3] = (node, e0, e1), partial_ofs int32 [n_heavy+1]."""
+    ip = np.asarray(indptr, np.int64)
+    deg = np.diff(ip)
+    light = np.nonzero(deg <= threshold)[0]
+    heavy = np.nonzero(deg > threshold)[0]
+    span = int(chunk) * int(waves)
+    ng = (deg[heavy] + span - 1) // span
+    partial_ofs = np.zeros(heavy.size + 1, np.int64)
+    np.cumsum(ng, out=partial_ofs[1:])
+    node = np.repeat(heavy, ng)
+    k = np.arange(node.size) - np.repeat(partial_ofs[:-1], ng)
+    e0 = ip[node] + k * span
+    e1 = np.minimum(e0 + span, ip[node + 1])
+    groups = np.stack([node, e0, e1], axis=1) if node.size else np.zeros((0, 3), np.int64)
+    return dict(light=light.astype(np.int32), heavy=heavy.astype(np.int32),
+                groups=groups.astype(np.int32), partial_ofs=partial_ofs.astype(np.int32))
+
+
+def csc(indptr, indices, n_nodes: int):
+    """Transposed adjacency: for each source j, the destinations i of its
+    out-edges j -> i in ascending order (with multiplicity).
+    Returns (cindptr int32 [N+1], cindices int32 [E])."""
+    n = int(n_nodes)
+    ip = np.asarray(indptr, np.int64)
+    dst = np.repeat(np.arange(n, dtype=np.int64), np.diff(ip))
+    src = np.asarray(indices, np.int64)
+    keys = np.sort(src * n + dst)
+    cols = keys // n
+    cindices = (keys - cols * n).astype(np.int32)
+    cindptr = np.zeros(n + 1, np.int64)
+    np.cumsum(np.bincount(cols, minlength=n), out=cindptr[1:])
+    return cindptr.astype(np.int32), cindices
+
+
+def tile_census(indptr, indices, n_nodes: int, min_nnz: int):
+    """16x16 dense-tile census.
+
+    Node ids are grouped into aligned blocks of 16. Every (destination block,
+    source block) pair holding at least min_nnz edges becomes a tile with a
+    256-bit presence mask: bit (dst % 16) * 16 + (src % 16), stored as four
+    uint64 words, word w holding bits 64w..64w+63 (bit b of the word is
+    position 64w + b). Tiles are listed by (row block, col block) ascending.
+    Every edge not inside a tile goes to the residual CSR, in CSR order.
+
+    Returns dict: tile_rc int32 [n_tiles, 2], tile_mask uint64 [n_tiles, 4],
+    tile_ptr int32 [n_rowblk+1] (tiles of each row block), rindptr int32 [N+1],
+    rindices int32 [E_res]."""
+    n = int(n_nodes)
+    ip = np.asarray(indptr, np.int64)
+    src = np.asarray(indices, np.int64)
+    dst = np.repeat(np.arange(n, dtype=np.int64), np.diff(ip))
+    nb = (n + 15) // 16
+    pair = (dst // 16) * nb + (src // 16)
+    upair, cnt = np.unique(pair, return_counts=True)
+    tiles = upair[cnt >= min_nnz]
+    in_tile = np.isin(pair, tiles)
+    mask = np.zeros((tiles.size, 4), np.uint64)
+    if tiles.size:
+        t = np.searchsorted(tiles, pair[in_tile])
+        bit = (dst[in_tile] % 16) * 16 + (src[in_tile] % 16)
+        word = bit // 64
+        val = np.left_shift(np.uint64(1), (bit % 64).astype(np.uint64))
+        np.bitwise_or.at(mask, (t, word), val)
+    rc = np.stack([tiles // nb, tiles % nb], axis=1) if tiles.size else np.zeros((0, 2), np.int64)
+    tile_ptr = np.zeros(nb + 1, np.int64)
+    np.cumsum(np.bincount(rc[:, 0], minlength=nb), out=tile_ptr[1:])
+    keep = ~in_tile
+    rindptr = np.zeros(n + 1, np.int64)
+    np.cumsum(np.bincount(dst[keep], minlength=n), out=rindptr[1:])
+    return dict(tile_rc=rc.astype(np.int32), tile_mask=mask, tile_ptr=tile_ptr.astype(np.int32),
+                rindptr=rindptr.astype(np.int32), rindices=src[keep].astype(np.int32))
+
+
+# ---------------------------------------------------------------------------
+# floating point (fp64)
+# ---------------------------------------------------------------------------
+
+def _rows(rows, n):
+    if rows is None:
+        return None, n
+    r = np.ascontiguousarray(rows, np.int64)
+    if r.size and (r.min() < 0 or r.max() >= n):
+        raise ValueError("row out of range")
+    return r, r.size
+
+
+def _graph(indptr, indices):
+    return np.ascontiguousarray(indptr, np.int64), np.ascontiguousarray(indices, np.int32)
+
+
+def gt_fwd(indptr, indices, Q, K, V, scale: Optional[float] = None, rows=None):
+    """Graph-Transformer forward in fp64.
+
+    s_ij = scale * <q_i, k_j> per head (scale = 1/sqrt(D) by default);
+    alpha_ij = softmax over j in N(i); O_i = sum_j alpha_ij v_j;
+    LSE_i = m_i + ln sum_j exp(s_ij - m_i).
+    Returns dict O [r,H,D], LSE [r,H], SO [r,H,D], SL [r,H] (scales)."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    N, H, D = Q.shape
+    ip, ix = _graph(indptr, indices)
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    r, nr = _rows(rows, N)
+    O = np.empty((nr, H, D)); LSE = np.empty((nr, H)); SO = np.empty((nr, H, D)); SL = np.empty((nr, H))
+    rc = _load().orc_gt_fwd(N, _p(ip), _p(ix), H, D, _p(Q), _p(K), _p(V), sc, nr, _p(r),
+                            _p(O), _p(LSE), _p(SO), _p(SL))
+    if rc:
+        raise MemoryError("oracle row buffer")
+    return dict(O=O, LSE=LSE, SO=SO, SL=SL)
+
+
+def gatv2_fwd(indptr, indices, XD, XS, att, V=None, slope: float = 0.2, rows=None):
+    """GATv2 forward in fp64.
+
+    s_ij = sum_d a[h,d] * LeakyReLU_slope(xs_j + xd_i) per head (no scale);
+    the same softmax; O_i = sum_j alpha_ij v_j with v = xs unless V is given."""
+    XD, XS = _f64(XD), _f64(XS)
+    Vv = XS if V is None else _f64(V)
+    a = _f64(att)
+    N, H, D = XD.shape
+    ip, ix = _graph(indptr, indices)
+    r, nr = _rows(rows, N)
+    O = np.empty((nr, H, D)); LSE = np.empty((nr, H)); SO = np.empty((nr, H, D)); SL = np.empty((nr, H))
+    rc = _load().orc_gatv2_fwd(N, _p(ip), _p(ix), H, D, _p(XD), _p(XS), _p(Vv), _p(a), float(slope),
+                               nr, _p(r), _p(O), _p(LSE), _p(SO), _p(SL))
+    if rc:
+        raise MemoryError("oracle row buffer")
+    return dict(O=O, LSE=LSE, SO=SO, SL=SL)
+
+
+def gt_bwd(indptr, indices, Q, K, V, dO, scale: Optional[float] = None, rows=None, srcs=None,
+           csc_arrays=None, want_src: bool = True):
+    """Graph-Transformer backward in fp64, from the definition.
+
+    dQ (and Delta) for the destination rows `rows` (None = all); dK, dV for
+    the sources `srcs` (None = all) over the transposed adjacency. The
+    destination statistics the source side needs are computed for exactly the
+    rows it touches. Returns dict dQ, Delta, SdQ [rows] and dK, dV, SdK, SdV
+    [srcs]."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    N, H, D = Q.shape
+    ip, ix = _graph(indptr, indices)
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    lib = _load()
+    out = {}
+    r, nr = _rows(rows, N)
+    dQ = np.empty((nr, H, D)); Dl = np.empty((nr, H)); M = np.empty((nr, H)); Z = np.empty((nr, H))
+    SdQ = np.empty((nr, H, D))
+    rc = lib.orc_gt_bwd_rows(N, _p(ip), _p(ix), H, D, _p(Q), _p(K), _p(V), _p(dO), sc, nr, _p(r),
+                             _p(dQ), _p(Dl), _p(M), _p(Z), _p(SdQ))
+    if rc:
+        raise MemoryError("oracle row buffer")
+    out.update(dQ=dQ, Delta=Dl, SdQ=SdQ)
+    if not want_src:
+        return out
+    cip, cix = csc(ip, ix, N) if csc_arrays is None else csc_arrays
+    cip = np.ascontiguousarray(cip, np.int64)
+    cix = np.ascontiguousarray(cix, np.int32)
+    s, ns = _rows(srcs, N)
+    # destination rows touched by the listed sources
+    if s is None:
+        need = np.arange(N, dtype=np.int64)
+    else:
+        parts = [cix[cip[j]:cip[j + 1]] for j in s]
+        need = np.unique(np.concatenate(parts).astype(np.int64)) if parts else np.zeros(0, np.int64)
+    if r is None and s is None:
+        M2, Z2, D2 = M, Z, Dl
+    else:
+        n2 = need.size
+        tmp_dq = np.empty((n2, H, D)); D2 = np.empty((n2, H)); M2 = np.empty((n2, H)); Z2 = np.empty((n2, H))
+        rc = lib.orc_gt_bwd_rows(N, _p(ip), _p(ix), H, D, _p(Q), _p(K), _p(V), _p(dO), sc, n2, _p(need),
+                                 _p(tmp_dq), _p(D2), _p(M2), _p(Z2), None)
+        if rc:
+            raise MemoryError("oracle row buffer")
+    slot = np.full(N, -1, np.int64)
+    slot[need] = np.arange(need.size)
+    dK = np.empty((ns, H, D)); dV = np.empty((ns, H, D)); SdK = np.empty((ns, H, D)); SdV = np.empty((ns, H, D))
+    rc = lib.orc_gt_bwd_srcs(N, _p(cip), _p(cix), H, D, _p(Q), _p(K), _p(V), _p(dO), sc, _p(slot),
+                             _p(M2), _p(Z2), _p(D2), ns, _p(s), _p(dK), _p(dV), _p(SdK), _p(SdV))
+    if rc:
+        raise RuntimeError("oracle source pass: missing destination statistics")
+    out.update(dK=dK, dV=dV, SdK=SdK, SdV=SdV)
+    return out
+
+
+def scaled_error(x, ref, scale) -> float:
+    """max_e |x_e - r_e| / max(|r_e|, S_e), S_e the oracle's summation scale.
+
+    Entries where both are -inf (empty rows' LSE) count as exact."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    s = np.maximum(np.abs(ref), np.asarray(scale, np.float64))
+    both_inf = np.isinf(x) & np.isinf(ref) & (np.sign(x) == np.sign(ref))
+    diff = np.where(both_inf, 0.0, np.abs(x - ref))
+    den = np.where(both_inf, 1.0, np.where(s > 0, s, 1.0))
+    e = diff / den
+    if e.size == 0:
+        return 0.0
+    return float(np.max(e))

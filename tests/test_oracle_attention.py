@@ -1,0 +1,357 @@
+"""Pins for the oracle's floating-point attention (GT forward/backward, GATv2).
+
+The oracle is checked against things other than itself:
+  * hand-worked examples under tests/golden/ (derivations in the files),
+  * an independent dense masked-softmax brute force (numpy, below),
+  * a library routine: torch's scaled_dot_product_attention on CPU in fp64
+    with a boolean adjacency mask, and torch.autograd through it,
+  * closed forms and invariants of softmax attention,
+  * central finite differences of the oracle's own forward for its backward.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import dense_adjacency, random_graph, read_golden
+
+
+# ---------------------------------------------------------------- fixtures
+
+def _graph(seed, n, p=0.3):
+    rng = np.random.default_rng(seed)
+    src, dst, _ = random_graph(rng, n, p=p)
+    ip, ix = oracle.csr_build(src, dst, n)
+    return rng, ip, ix
+
+
+def _feats(rng, n, h, d, k=3):
+    return [rng.standard_normal((n, h, d)) for _ in range(k)]
+
+
+# ---------------------------------------------------- independent references
+
+def dense_gt(A, Q, K, V, scale):
+    """Dense masked softmax attention (A[i, j] true iff j -> i)."""
+    S = scale * np.einsum("ihd,jhd->hij", Q, K)
+    S = np.where(A[None], S, -np.inf)
+    m = S.max(axis=2, keepdims=True)
+    P = np.exp(S - m)
+    Z = P.sum(axis=2, keepdims=True)
+    O = np.einsum("hij,jhd->ihd", P / Z, V)
+    LSE = (m + np.log(Z))[:, :, 0].T
+    return O, LSE
+
+
+def dense_gatv2(A, XD, XS, att, slope, V):
+    Zs = XS[None, :, :, :] + XD[:, None, :, :]             # [i, j, h, d]
+    L = np.where(Zs >= 0, Zs, slope * Zs)
+    S = np.einsum("ijhd,hd->hij", L, att)
+    S = np.where(A[None], S, -np.inf)
+    m = S.max(axis=2, keepdims=True)
+    P = np.exp(S - m)
+    Z = P.sum(axis=2, keepdims=True)
+    O = np.einsum("hij,jhd->ihd", P / Z, V)
+    return O, (m + np.log(Z))[:, :, 0].T
+
+
+def torch_sdpa(A, Q, K, V, scale, dO=None):
+    q = torch.tensor(Q.transpose(1, 0, 2), dtype=torch.float64, requires_grad=dO is not None)
+    k = torch.tensor(K.transpose(1, 0, 2), dtype=torch.float64, requires_grad=dO is not None)
+    v = torch.tensor(V.transpose(1, 0, 2), dtype=torch.float64, requires_grad=dO is not None)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=torch.tensor(A), scale=scale)
+    if dO is None:
+        return o.detach().numpy().transpose(1, 0, 2)
+    o.backward(torch.tensor(dO.transpose(1, 0, 2)))
+    return [t.grad.numpy().transpose(1, 0, 2) for t in (q, k, v)]
+
+
+# ------------------------------------------------------------------ golden
+
+def test_golden_gt_fwd():
+    g = read_golden("gt_fwd_3node.txt")
+    N, H, D = int(g["N"][0]), int(g["H"][0]), int(g["D"][0])
+    r = oracle.gt_fwd(g["indptr"].astype(np.int32), g["indices"].astype(np.int32),
+                      g["Q"].reshape(N, H, D), g["K"].reshape(N, H, D), g["V"].reshape(N, H, D))
+    assert np.allclose(r["O"].ravel(), g["O"], atol=1e-14, rtol=1e-14)
+    assert np.allclose(r["LSE"].ravel(), g["LSE"], atol=1e-14, rtol=1e-14)
+
+
+def test_golden_gatv2_fwd():
+    g = read_golden("gatv2_fwd_3node.txt")
+    N, H, D = int(g["N"][0]), int(g["H"][0]), int(g["D"][0])
+    r = oracle.gatv2_fwd(g["indptr"].astype(np.int32), g["indices"].astype(np.int32),
+                         g["XD"].reshape(N, H, D), g["XS"].reshape(N, H, D), g["att"].reshape(H, D),
+                         slope=float(g["slope"][0]))
+    assert np.allclose(r["O"].ravel(), g["O"], atol=1e-14, rtol=1e-14)
+    assert np.allclose(r["LSE"].ravel(), g["LSE"], atol=1e-14, rtol=1e-14)
+
+
+def test_golden_gt_bwd():
+    g = read_golden("gt_bwd_2node.txt")
+    N, H, D = int(g["N"][0]), int(g["H"][0]), int(g["D"][0])
+    sh = (N, H, D)
+    r = oracle.gt_bwd(g["indptr"].astype(np.int32), g["indices"].astype(np.int32), g["Q"].reshape(sh),
+                      g["K"].reshape(sh), g["V"].reshape(sh), g["dO"].reshape(sh), scale=float(g["scale"][0]))
+    for k in ("dQ", "dK", "dV", "Delta"):
+        assert np.allclose(r[k].ravel(), g[k], atol=1e-14, rtol=1e-14), k
+
+
+# --------------------------------------------------------- GT forward pins
+
+@pytest.mark.parametrize("seed,n,h,d", [(0, 20, 1, 16), (1, 33, 2, 8), (2, 64, 4, 4), (3, 7, 3, 5)])
+def test_gt_fwd_dense_brute_force_and_sdpa(seed, n, h, d):
+    rng, ip, ix = _graph(seed, n)
+    Q, K, V = _feats(rng, n, h, d)
+    sc = 1 / np.sqrt(d)
+    r = oracle.gt_fwd(ip, ix, Q, K, V)
+    A = dense_adjacency(ip, ix, n)
+    O, LSE = dense_gt(A, Q, K, V, sc)
+    assert np.max(np.abs(r["O"] - O)) < 1e-12
+    assert np.max(np.abs(r["LSE"] - LSE)) < 1e-12
+    assert np.max(np.abs(r["O"] - torch_sdpa(A, Q, K, V, sc))) < 1e-12
+
+
+def test_gt_fwd_complete_graph_is_unmasked_sdpa():
+    n, h, d = 24, 2, 8
+    rng = np.random.default_rng(9)
+    a = np.ones((n, n), bool)
+    dst, src = np.nonzero(a)
+    ip, ix = oracle.csr_build(src, dst, n)
+    Q, K, V = _feats(rng, n, h, d)
+    q, k, v = (torch.tensor(x.transpose(1, 0, 2)) for x in (Q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v).numpy().transpose(1, 0, 2)
+    assert np.max(np.abs(oracle.gt_fwd(ip, ix, Q, K, V)["O"] - ref)) < 1e-12
+
+
+def test_gt_fwd_closed_forms():
+    rng, ip, ix = _graph(11, 40)
+    n, h, d = 40, 2, 8
+    Q, K, V = _feats(rng, n, h, d)
+    deg = np.diff(ip)
+    # Q = 0: uniform weights -> O = neighbour mean, LSE = ln deg
+    r = oracle.gt_fwd(ip, ix, np.zeros_like(Q), K, V)
+    mean = np.stack([V[ix[ip[i]:ip[i + 1]]].mean(axis=0) for i in range(n)])
+    assert np.max(np.abs(r["O"] - mean)) < 1e-13
+    assert np.max(np.abs(r["LSE"] - np.log(deg)[:, None])) < 1e-13
+    # V constant: weights sum to one -> O = that constant
+    r = oracle.gt_fwd(ip, ix, Q, K, np.full_like(V, 2.5))
+    assert np.max(np.abs(r["O"] - 2.5)) < 1e-13
+    # self-loop-only nodes: O_i = v_i, LSE_i = <q_i, k_i>/sqrt(D)
+    sip, six = oracle.csr_build(np.zeros(0, np.int32), np.zeros(0, np.int32), n)
+    r = oracle.gt_fwd(sip, six, Q, K, V)
+    assert np.max(np.abs(r["O"] - V)) < 1e-15
+    assert np.max(np.abs(r["LSE"] - np.einsum("ihd,ihd->ih", Q, K) / np.sqrt(d))) < 1e-13
+
+
+def test_gt_fwd_invariants():
+    rng, ip, ix = _graph(12, 30)
+    n, h, d = 30, 2, 8
+    Q, K, V = _feats(rng, n, h, d)
+    base = oracle.gt_fwd(ip, ix, Q, K, V)
+    # shifting every key by the same u leaves O alone, LSE moves by <q_i, u>/sqrt(D)
+    u = rng.standard_normal((h, d))
+    r = oracle.gt_fwd(ip, ix, Q, K + u[None], V)
+    assert np.max(np.abs(r["O"] - base["O"])) < 1e-12
+    assert np.max(np.abs(r["LSE"] - base["LSE"] - np.einsum("ihd,hd->ih", Q, u) / np.sqrt(d))) < 1e-12
+    # affine in V
+    r = oracle.gt_fwd(ip, ix, Q, K, 3.0 * V - 1.25)
+    assert np.max(np.abs(r["O"] - (3.0 * base["O"] - 1.25))) < 1e-12
+    # permutation equivariance under relabelling
+    perm = rng.permutation(n)
+    inv = np.argsort(perm)
+    src = ix
+    dst = np.repeat(np.arange(n), np.diff(ip))
+    pip, pix = oracle.csr_build(perm[src], perm[dst], n)
+    Qp, Kp, Vp = (np.empty_like(x) for x in (Q, K, V))
+    Qp[perm], Kp[perm], Vp[perm] = Q, K, V
+    r = oracle.gt_fwd(pip, pix, Qp, Kp, Vp)
+    assert np.max(np.abs(r["O"][perm] - base["O"])) < 1e-12
+    assert np.max(np.abs(r["LSE"][perm] - base["LSE"])) < 1e-12
+    assert np.array_equal(inv[perm], np.arange(n))
+
+
+def test_gt_fwd_empty_rows_and_row_subsets():
+    n, h, d = 10, 2, 4
+    rng = np.random.default_rng(5)
+    src = np.array([1, 2, 3], np.int32)
+    dst = np.array([0, 0, 5], np.int32)
+    ip, ix = oracle.csr_build(src, dst, n, add_self_loops=False)
+    Q, K, V = _feats(rng, n, h, d)
+    r = oracle.gt_fwd(ip, ix, Q, K, V)
+    empty = np.diff(ip) == 0
+    assert np.all(r["O"][empty] == 0) and np.all(np.isneginf(r["LSE"][empty]))
+    rows = np.array([5, 0, 9])
+    s = oracle.gt_fwd(ip, ix, Q, K, V, rows=rows)
+    assert np.array_equal(s["O"], r["O"][rows]) and np.array_equal(s["LSE"], r["LSE"][rows])
+
+
+def test_gt_fwd_scale_bounds_error():
+    # SO = sum_j alpha |v| dominates |O|; SL = 1 + max |s| dominates |LSE - ln deg| bounds
+    rng, ip, ix = _graph(13, 30)
+    Q, K, V = _feats(rng, 30, 2, 8)
+    r = oracle.gt_fwd(ip, ix, Q, K, V)
+    assert np.all(r["SO"] >= np.abs(r["O"]) - 1e-15)
+    assert np.all(r["SL"] >= 1.0)
+
+
+# ------------------------------------------------------------- GATv2 pins
+
+@pytest.mark.parametrize("seed,n,h,d,slope", [(0, 20, 1, 16, 0.2), (1, 31, 2, 8, 0.2), (2, 50, 8, 4, 0.01)])
+def test_gatv2_dense_brute_force(seed, n, h, d, slope):
+    rng, ip, ix = _graph(seed, n)
+    XD, XS = _feats(rng, n, h, d, 2)
+    att = rng.standard_normal((h, d)) / np.sqrt(d)
+    r = oracle.gatv2_fwd(ip, ix, XD, XS, att, slope=slope)
+    O, LSE = dense_gatv2(dense_adjacency(ip, ix, n), XD, XS, att, slope, XS)
+    assert np.max(np.abs(r["O"] - O)) < 1e-12
+    assert np.max(np.abs(r["LSE"] - LSE)) < 1e-12
+    # separate V
+    V = rng.standard_normal((n, h, d))
+    r = oracle.gatv2_fwd(ip, ix, XD, XS, att, V=V, slope=slope)
+    O, _ = dense_gatv2(dense_adjacency(ip, ix, n), XD, XS, att, slope, V)
+    assert np.max(np.abs(r["O"] - O)) < 1e-12
+
+
+def test_gatv2_closed_forms():
+    rng, ip, ix = _graph(21, 40)
+    n, h, d = 40, 2, 8
+    XD, XS = _feats(rng, n, h, d, 2)
+    att = rng.standard_normal((h, d)) / np.sqrt(d)
+    # a = 0: uniform weights
+    r = oracle.gatv2_fwd(ip, ix, XD, XS, np.zeros_like(att))
+    mean = np.stack([XS[ix[ip[i]:ip[i + 1]]].mean(axis=0) for i in range(n)])
+    assert np.max(np.abs(r["O"] - mean)) < 1e-13
+    # slope 1: LeakyReLU is the identity, s_ij = <a, xs_j> + <a, xd_i>; the xd
+    # term is constant over the row, so alpha_ij ∝ exp(<a, xs_j>)
+    r = oracle.gatv2_fwd(ip, ix, XD, XS, att, slope=1.0)
+    sj = np.einsum("jhd,hd->jh", XS, att)
+    si = np.einsum("ihd,hd->ih", XD, att)
+    for i in range(n):
+        nb = ix[ip[i]:ip[i + 1]]
+        w = np.exp(sj[nb] - sj[nb].max(axis=0))
+        w /= w.sum(axis=0)
+        assert np.max(np.abs(r["O"][i] - np.einsum("jh,jhd->hd", w, XS[nb]))) < 1e-13
+        lse = si[i] + sj[nb].max(axis=0) + np.log(np.exp(sj[nb] - sj[nb].max(axis=0)).sum(axis=0))
+        assert np.max(np.abs(r["LSE"][i] - lse)) < 1e-12
+    # constant V
+    r = oracle.gatv2_fwd(ip, ix, XD, XS, att, V=np.full_like(XS, -0.5))
+    assert np.max(np.abs(r["O"] + 0.5)) < 1e-13
+
+
+def test_gatv2_permutation_equivariance():
+    rng, ip, ix = _graph(22, 30)
+    n, h, d = 30, 2, 4
+    XD, XS = _feats(rng, n, h, d, 2)
+    att = rng.standard_normal((h, d))
+    base = oracle.gatv2_fwd(ip, ix, XD, XS, att)
+    perm = rng.permutation(n)
+    dst = np.repeat(np.arange(n), np.diff(ip))
+    pip, pix = oracle.csr_build(perm[ix], perm[dst], n)
+    XDp, XSp = np.empty_like(XD), np.empty_like(XS)
+    XDp[perm], XSp[perm] = XD, XS
+    r = oracle.gatv2_fwd(pip, pix, XDp, XSp, att)
+    assert np.max(np.abs(r["O"][perm] - base["O"])) < 1e-12
+
+
+# ---------------------------------------------------------- GT backward pins
+
+@pytest.mark.parametrize("seed,n,h,d", [(0, 9, 1, 4), (1, 12, 2, 3)])
+def test_gt_bwd_finite_differences(seed, n, h, d):
+    rng, ip, ix = _graph(seed, n, p=0.4)
+    Q, K, V, dO = _feats(rng, n, h, d, 4)
+    g = oracle.gt_bwd(ip, ix, Q, K, V, dO)
+    eps = 1e-6
+
+    def f(Qx, Kx, Vx):
+        return float(np.sum(dO * oracle.gt_fwd(ip, ix, Qx, Kx, Vx)["O"]))
+
+    for name, X, G in (("Q", Q, g["dQ"]), ("K", K, g["dK"]), ("V", V, g["dV"])):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            Xp = X.copy(); Xp[idx] += eps
+            Xm = X.copy(); Xm[idx] -= eps
+            args = {"Q": Q, "K": K, "V": V}
+            args[name] = Xp
+            fp = f(args["Q"], args["K"], args["V"])
+            args[name] = Xm
+            fm = f(args["Q"], args["K"], args["V"])
+            num[idx] = (fp - fm) / (2 * eps)
+        err = np.max(np.abs(num - G)) / max(1.0, np.max(np.abs(G)))
+        assert err < 1e-7, (name, err)
+
+
+@pytest.mark.parametrize("seed,n,h,d", [(3, 25, 2, 8), (4, 40, 4, 16)])
+def test_gt_bwd_torch_autograd(seed, n, h, d):
+    rng, ip, ix = _graph(seed, n)
+    Q, K, V, dO = _feats(rng, n, h, d, 4)
+    g = oracle.gt_bwd(ip, ix, Q, K, V, dO)
+    tq, tk, tv = torch_sdpa(dense_adjacency(ip, ix, n), Q, K, V, 1 / np.sqrt(d), dO=dO)
+    assert np.max(np.abs(g["dQ"] - tq)) < 1e-12
+    assert np.max(np.abs(g["dK"] - tk)) < 1e-12
+    assert np.max(np.abs(g["dV"] - tv)) < 1e-12
+
+
+def test_gt_bwd_identities_and_subsets():
+    rng, ip, ix = _graph(31, 50)
+    n, h, d = 50, 2, 8
+    Q, K, V, dO = _feats(rng, n, h, d, 4)
+    g = oracle.gt_bwd(ip, ix, Q, K, V, dO)
+    O = oracle.gt_fwd(ip, ix, Q, K, V)["O"]
+    # shift invariance of softmax: sum over sources of dK vanishes
+    assert np.max(np.abs(g["dK"].sum(axis=0))) < 1e-12
+    # weights sum to one: sum over sources of dV equals the sum of dO over non-empty rows
+    assert np.max(np.abs(g["dV"].sum(axis=0) - dO[np.diff(ip) > 0].sum(axis=0))) < 1e-12
+    # Delta from the weights equals <dO_i, O_i>
+    assert np.max(np.abs(g["Delta"] - np.einsum("ihd,ihd->ih", dO, O))) < 1e-12
+    # subsets reproduce the full result
+    rows = np.array([7, 3, 49, 0])
+    srcs = np.array([2, 2, 40, 11])
+    s = oracle.gt_bwd(ip, ix, Q, K, V, dO, rows=rows, srcs=srcs)
+    for k, sel in (("dQ", rows), ("Delta", rows), ("dK", srcs), ("dV", srcs)):
+        assert np.array_equal(s[k], g[k][sel]), k
+
+
+def test_gt_bwd_empty_rows():
+    n, h, d = 6, 1, 4
+    rng = np.random.default_rng(7)
+    ip, ix = oracle.csr_build(np.array([1, 2], np.int32), np.array([0, 0], np.int32), n, add_self_loops=False)
+    Q, K, V, dO = _feats(rng, n, h, d, 4)
+    g = oracle.gt_bwd(ip, ix, Q, K, V, dO)
+    assert np.all(g["dQ"][1:] == 0)
+    assert np.all(g["dK"][[0, 3, 4, 5]] == 0) and np.all(g["dV"][[0, 3, 4, 5]] == 0)
+
+
+# --------------------------------------------- online-softmax merge algebra
+
+def test_partial_merge_equals_two_pass_softmax():
+    """Merging (m, l, acc) partials of a split neighbour list, in fp64, equals
+    the oracle's single two-pass result: the algebra the heavy-node path of the
+    fused kernel relies on (chunked neighbour lists reduced in parallel)."""
+    rng = np.random.default_rng(41)
+    n, h, d = 1, 1, 6
+    deg = 300
+    ip = np.array([0, deg], np.int32)
+    ix = rng.integers(0, deg, deg).astype(np.int32)
+    ix.sort()
+    Q = rng.standard_normal((deg, h, d)) * 3
+    K, V = rng.standard_normal((deg, h, d)), rng.standard_normal((deg, h, d))
+    ref = oracle.gt_fwd(np.array([0, deg] + [deg] * (deg - 1), np.int32), ix, Q, K, V, rows=[0])
+    s = (K[ix, 0] @ Q[0, 0]) / np.sqrt(d)
+    for cuts in ([0, deg], [0, 1, deg], [0, 7, 100, 299, deg], list(range(0, deg + 1, 37)) + [deg]):
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            if a == b:
+                parts.append((-np.inf, 0.0, np.zeros(d)))
+                continue
+            m = s[a:b].max()
+            p = np.exp(s[a:b] - m)
+            parts.append((m, p.sum(), p @ V[ix[a:b], 0]))
+        m, l, acc = -np.inf, 0.0, np.zeros(d)
+        for (m2, l2, a2) in parts:
+            mm = max(m, m2)
+            c1 = 0.0 if m == -np.inf else np.exp(m - mm)
+            c2 = 0.0 if m2 == -np.inf else np.exp(m2 - mm)
+            m, l, acc = mm, l * c1 + l2 * c2, acc * c1 + a2 * c2
+        assert np.max(np.abs(acc / l - ref["O"][0, 0])) < 1e-13
+        assert abs(m + np.log(l) - ref["LSE"][0, 0]) < 1e-13
