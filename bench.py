@@ -1,0 +1,409 @@
+#!/usr/bin/env python3
+"""Benchmark of fused CSR neighbourhood attention on one MI355X.
+
+A step is one pass of the attention hot path over the workload's graph with
+inputs resident in HBM: the forward (Graph Transformer or GATv2, light and
+heavy kernels plus the heavy merge), and for workloads that carry an upstream
+gradient also the LSE-recompute backward (destination and source passes).
+Graph preprocessing (CSR build, bucketing, transposed adjacency) runs once
+before timing and is reported separately.
+
+Default workload: GATv2 forward on the Zipf(2.1) in-degree graph
+(N = 100,000, mean in-degree 50, H = 8, D = 16, fp32).
+
+Output: one JSON line on stdout (metric GEdges/s = edges incl. self-loops per
+second of step time), with a roofline object for the dominant kernel and the
+fp64 CPU oracle timed on a bounded sample as a baseline.
+
+Other modes:
+  --copy-probe          run only a plain device copy of known size (counter
+                        calibration runs under rocprofv3 --pmc)
+  --summarize DIR ...   turn rocprofv3 CSV output in DIR into a short text
+                        summary (see --help)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEdges/s and achieved HBM GB/s (% of peak) for fused CSR attention fwd/bwd"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "gatv2_zipf21_n100k"
+KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_sparse_amd", "csrc", f) for f in ("attn.hip", "device.h")]
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------- byte model
+
+def kernel_bytes(kind, N, E, H, D, s, n_light, n_heavy, c_n_light, c_n_heavy, v_alias=True):
+    """Algorithmic HBM bytes one launch of kernel `kind` must move.
+
+    R = H*D*s is one node's feature row. Counted: CSR structure once, one
+    gathered row per edge per gathered table, per-node rows read or written
+    once, per-node statistics. Not counted: heavy partials (workspace) and
+    any re-read a cache would serve."""
+    R = H * D * s
+    if kind in ("gt_fwd_main", "gatv2_fwd_main"):
+        rows = R * E * (1 if (kind == "gatv2_fwd_main" and v_alias) else 2)
+        extra = 4 * H * D if kind == "gatv2_fwd_main" else 0
+        return 4 * (N + 1) + 4 * E + rows + R * N + (R + 4 * H) * n_light + extra
+    if kind in ("gt_fwd_merge", "gatv2_fwd_merge"):
+        return (R + 4 * H) * n_heavy
+    if kind == "gt_bwd_dst_main":     # reads Q, dO, LSE; gathers K, V; writes dQ and (lse, Delta)
+        return 4 * (N + 1) + 4 * E + 2 * R * E + (2 * R + 4 * H) * N + (R + 8 * H) * n_light
+    if kind == "gt_bwd_dst_merge":
+        return (R + 8 * H) * n_heavy
+    if kind == "gt_bwd_src_main":     # reads K, V; gathers Q, dO and (lse, Delta); writes dK, dV
+        return 4 * (N + 1) + 4 * E + (2 * R + 8 * H) * E + 2 * R * N + 2 * R * c_n_light
+    if kind == "gt_bwd_src_merge":
+        return 2 * R * c_n_heavy
+    return 0
+
+
+# ---------------------------------------------------------------- profiles
+
+def read_traffic(kernel: str, workload: str):
+    """Scaled HBM bytes per launch from a committed counter summary, or None
+    if there is none or it was taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"{kernel}__{workload}__counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize(args) -> int:
+    """Summarise rocprofv3 output (kernel stats or counters) into text."""
+    out = []
+    stats = glob.glob(os.path.join(args.summarize, "**", "*kernel_stats.csv"), recursive=True)
+    counters = glob.glob(os.path.join(args.summarize, "**", "*counter_collection.csv"), recursive=True)
+    out.append(f"# rocprofv3 summary of {args.summarize}")
+    if args.command:
+        out.append(f"# command: {args.command}")
+    out.append(f"source_sha256: {kernel_source_hash()}")
+    for fn in stats:
+        out.append(f"## kernel stats ({os.path.basename(fn)})")
+        with open(fn) as f:
+            rows = list(csv.DictReader(f))
+        rows.sort(key=lambda r: -float(r.get("TotalDurationNs", 0) or 0))
+        out.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}  kernel")
+        for r in rows[:25]:
+            out.append(f"{r['Calls']:>6} {float(r['AverageNs'])/1e3:10.2f} {float(r['MinNs'])/1e3:10.2f} "
+                       f"{float(r['MaxNs'])/1e3:10.2f} {float(r['TotalDurationNs'])/1e6:10.3f} "
+                       f"{float(r['Percentage']):6.2f}  {r['Name'][:140]}")
+    for fn in counters:
+        out.append(f"## counters ({os.path.basename(fn)}), per dispatch")
+        with open(fn) as f:
+            rows = list(csv.DictReader(f))
+        agg = {}
+        for r in rows:
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            agg.setdefault(key, []).append(float(r["Counter_Value"]))
+        for (k, c), v in sorted(agg.items()):
+            out.append(f"{c:>14} n={len(v):4d} mean={sum(v)/len(v):16.1f} min={min(v):16.1f} max={max(v):16.1f}  {k[:120]}")
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
+
+
+# ----------------------------------------------------------------- workload
+
+def setup(name, plan_opts):
+    import numpy as np
+    import torch
+
+    import io_aware_sparse_amd as g
+    import workloads
+
+    t0 = time.time()
+    wl = workloads.make(name)
+    t_gen = time.time() - t0
+    n, H, D = wl.n_nodes, wl.heads, wl.dim
+    dev = torch.device("cuda:0")
+
+    def feat(nm):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(wl.bits[nm].view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(wl.feats[nm]).to(dev)
+
+    src = torch.from_numpy(wl.src).to(dev)
+    dst = torch.from_numpy(wl.dst).to(dev)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    indptr, indices = g.gnn_csr_build(src, dst, n)
+    torch.cuda.synchronize()
+    t_csr = time.time() - t0
+    del src, dst
+    t0 = time.time()
+    plan = g.gnn_plan_create(indptr, indices, want_csc=wl.backward, **plan_opts)
+    torch.cuda.synchronize()
+    t_plan = time.time() - t0
+    tensors = {}
+    if wl.kind == "gt":
+        for nm in ("Q", "K", "V"):
+            tensors[nm] = feat(nm)
+        if wl.backward:
+            tensors["dO"] = feat("dO")
+    else:
+        tensors["XD"], tensors["XS"] = feat("XD"), feat("XS")
+        tensors["att"] = torch.from_numpy(wl.att).to(dev)
+    E = int(indices.numel())
+    tensors["O"] = torch.empty_like(tensors["Q"] if wl.kind == "gt" else tensors["XD"])
+    tensors["LSE"] = torch.empty((n, H), dtype=torch.float32, device=dev)
+    if wl.backward:
+        for nm in ("dQ", "dK", "dV"):
+            tensors[nm] = torch.empty_like(tensors["Q"])
+    torch.cuda.synchronize()
+    prep = dict(generate_s=round(t_gen, 3), csr_build_ms=round(1e3 * t_csr, 3), plan_create_ms=round(1e3 * t_plan, 3))
+    return wl, indptr, indices, plan, tensors, E, prep
+
+
+def make_step(g, wl, indptr, indices, plan, T):
+    if wl.kind == "gatv2":
+        def step():
+            g.gatv2_attn_fwd(plan, indptr, indices, T["XD"], T["XS"], T["att"], negative_slope=0.2, O=T["O"],
+                             LSE=T["LSE"])
+    elif not wl.backward:
+        def step():
+            g.gnn_attn_fwd(plan, indptr, indices, T["Q"], T["K"], T["V"], O=T["O"], LSE=T["LSE"])
+    else:
+        def step():
+            g.gnn_attn_fwd(plan, indptr, indices, T["Q"], T["K"], T["V"], O=T["O"], LSE=T["LSE"])
+            g.gnn_attn_bwd(plan, indptr, indices, T["Q"], T["K"], T["V"], T["O"], T["dO"], T["LSE"],
+                           dQ=T["dQ"], dK=T["dK"], dV=T["dV"])
+    return step
+
+
+def cpu_baseline(wl, rp, rx, target_s):
+    """fp64 oracle on a seeded sample of destination rows (and the same nodes
+    as sources for the gradient), sized to about target_s seconds."""
+    import numpy as np
+
+    import oracle
+
+    n = wl.n_nodes
+    deg = np.diff(rp.astype(np.int64))
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(n)
+    csum = np.cumsum(deg[order])
+
+    if wl.kind == "gt":
+        Q, K, V = (np.asarray(wl.feats[k], np.float64) for k in ("Q", "K", "V"))
+        dO = np.asarray(wl.feats["dO"], np.float64) if wl.backward else None
+    else:
+        XD, XS = (np.asarray(wl.feats[k], np.float64) for k in ("XD", "XS"))
+    csc = oracle.csc(rp, rx, n) if wl.backward else None
+
+    def run(edges):
+        k = int(np.searchsorted(csum, edges)) + 1
+        rows = np.sort(order[:min(k, n)])
+        t0 = time.perf_counter()
+        if wl.kind == "gatv2":
+            oracle.gatv2_fwd(rp, rx, XD, XS, wl.att, slope=0.2, rows=rows)
+        else:
+            oracle.gt_fwd(rp, rx, Q, K, V, rows=rows)
+            if wl.backward:
+                oracle.gt_bwd(rp, rx, Q, K, V, dO, rows=rows, srcs=rows, csc_arrays=csc)
+        return time.perf_counter() - t0, int(deg[rows].sum()), rows.size
+
+    e_try = min(int(csum[-1]), 200_000)
+    t, e, r = run(e_try)
+    if t < target_s and e < csum[-1]:
+        e_try = min(int(csum[-1]), int(e * target_s / max(t, 1e-3)))
+        t, e, r = run(e_try)
+    return dict(value=round(e / t / 1e9, 6), unit="GEdges/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{r} destination rows drawn uniformly (seed 12345) covering {e} of {int(csum[-1])} edges"
+                       + (" (forward + backward, the same nodes as sources)" if wl.backward else " (forward)")
+                       + f", {t:.2f} s")
+
+
+def bench(args) -> int:
+    import numpy as np
+    import torch
+
+    import io_aware_sparse_amd as g
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        return 2
+    g.lib()
+    torch.cuda.set_device(0)
+    opts = dict(light_threshold=args.light_threshold, chunk=args.chunk, waves_per_group=args.waves)
+    log(f"[bench] workload {args.workload}: generating and building the graph")
+    wl, indptr, indices, plan, T, E, prep = setup(args.workload, opts)
+    info = g.gnn_plan_export(plan)
+    N, H, D = wl.n_nodes, wl.heads, wl.dim
+    s = 4 if wl.dtype == "f32" else 2
+    log(f"[bench] N={N} E={E} H={H} D={D} dtype={wl.dtype} light={info['n_light']} heavy={info['n_heavy']} "
+        f"groups={info['n_groups']} prep={prep}")
+    step = make_step(g, wl, indptr, indices, plan, T)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    g.gnn_plan_timing_read(plan)
+    g.gnn_plan_set_timing(plan, True)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    wall0 = time.perf_counter()
+    if flush is None:
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            step()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms_total = ev[0].elapsed_time(ev[1])
+    else:
+        for k in range(args.steps):
+            flush.fill_(k & 0xFF)
+            ev[2 * k].record(stream)
+            step()
+            ev[2 * k + 1].record(stream)
+        torch.cuda.synchronize()
+        ms_total = sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps))
+    wall = time.perf_counter() - wall0
+    g.gnn_plan_set_timing(plan, False)
+    kt = g.gnn_plan_timing_read(plan)
+    ms_step = ms_total / args.steps
+    value = E / (ms_step * 1e-3) / 1e9
+
+    v_alias = True
+    counts = dict(n_light=info["n_light"], n_heavy=info["n_heavy"], c_n_light=info["c_n_light"],
+                  c_n_heavy=info["c_n_heavy"])
+    kernels = {}
+    for name, (launches, tot_ms) in kt.items():
+        avg_ms = tot_ms / max(1, launches)
+        b = kernel_bytes(name, N, E, H, D, s, v_alias=v_alias, **counts)
+        kernels[name] = dict(launches=launches, avg_us=round(1e3 * avg_ms, 3), alg_bytes=b,
+                             GBps=round(b / (avg_ms * 1e-3) / 1e9, 1) if avg_ms > 0 else None)
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    dk = kernels[dom]
+    achieved = dk["GBps"]
+    traffic = read_traffic(dom, args.workload)
+    step_bytes = sum(kernel_bytes(k, N, E, H, D, s, v_alias=v_alias, **counts) for k in kernels)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "GEdges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "pass": "GATv2 forward" if wl.kind == "gatv2" else
+                    ("GT forward + LSE-recompute backward" if wl.backward else "GT forward"),
+            "n_nodes": N, "n_edges": E, "heads": H, "dim": D,
+            "storage": wl.dtype, "math": "f32",
+            "light_threshold": args.light_threshold, "chunk": args.chunk, "waves_per_group": args.waves,
+            "cache": "flushed 512 MiB between steps" if args.flush else "warm (back-to-back steps)",
+            "parallelism": "single GPU",
+        },
+        "step_model_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_model_frac_of_8TBps": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
+            "traffic": traffic,
+            "alg_bytes_per_launch": dk["alg_bytes"],
+            "avg_launch_us": dk["avg_us"],
+        },
+        "kernels": kernels,
+        "preprocess": prep,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rp = indptr.cpu().numpy()
+        rx = indices.cpu().numpy()
+        log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        rec["cpu_baseline"] = cpu_baseline(wl, rp, rx, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def copy_probe(args) -> int:
+    import torch
+    nbytes = args.copy_mib << 20
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
+    return 0
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--light-threshold", type=int, default=512)
+    ap.add_argument("--chunk", type=int, default=512)
+    ap.add_argument("--waves", type=int, default=4)
+    ap.add_argument("--flush", action="store_true", help="flush caches with a 512 MiB write between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--out", help="summary output file")
+    args = ap.parse_args()
+    if args.summarize:
+        return summarize(args)
+    if args.copy_probe:
+        return copy_probe(args)
+    return bench(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,219 @@
+/*
+ * gnn_attn.h — C ABI of the fused CSR neighbourhood-attention library for
+ * AMD MI355X (gfx950).
+ *
+ * The operations follow "On Efficient Scaling of GNNs via IO-Aware Layers
+ * Implementations" (technical summary, Methodology):
+ *   - attention-based layers (Graph Transformer, GATv2) computed by fused CSR
+ *     kernels that score, softmax-normalise and aggregate in one streaming
+ *     pass over each node's neighbours;
+ *   - the forward pass keeps running softmax statistics in registers (online
+ *     softmax) so no edge-wise logits are written;
+ *   - the backward pass caches a compact per-node statistic (log-sum-exp)
+ *     instead of edge weights and recomputes the weights on the fly;
+ *   - degree-aware tiling: nodes split into light and heavy sets by a degree
+ *     threshold, heavy neighbour lists cut into edge chunks reduced in
+ *     parallel;
+ *   - graph metadata (buckets, transposed adjacency) built once and cached
+ *     for reuse in a plan.
+ *
+ * Conventions for every call below
+ *   - Pointers are DEVICE pointers owned by the caller unless marked "host".
+ *     The library never frees caller memory and keeps no caller pointer past
+ *     the call, except that a plan does not copy indptr/indices: the arrays
+ *     passed to gnn_plan_create must stay alive and unchanged while the plan
+ *     is used with them.
+ *   - Graphs are CSR by destination: row i (indices[indptr[i] .. indptr[i+1]))
+ *     lists the sources j of the edges j -> i; the softmax of node i runs
+ *     over those in-neighbours. indptr is int32 [N+1] with indptr[0] = 0 and
+ *     indptr[N] = E; indices is int32 [E], each in [0, N). Multigraph entries
+ *     are each counted.
+ *   - Node features Q, K, V, O and every gradient are [N, H, D] contiguous
+ *     row-major: element (i, h, d) at offset (i*H + h)*D + d, all in one
+ *     dtype (fp32 or bf16). Arithmetic is fp32; bf16 results are rounded to
+ *     nearest-even. LSE is fp32 [N, H] in natural-log units.
+ *   - D must be 16, 32, 64 or 128; H >= 1. Feature pointers must be 16-byte
+ *     aligned. E < 2^31.
+ *   - A node with no in-edges gets O = 0, LSE = -inf and zero gradients.
+ *   - Attention calls are asynchronous on `stream` and never synchronise the
+ *     host. gnn_csr_build and gnn_plan_create synchronise `stream` once to
+ *     read back counts.
+ *   - Every call returns a gnn_status_t; argument errors are detected on the
+ *     host before any HIP call is made. No exception crosses the ABI.
+ *   - A plan may be used by one stream at a time (it owns reusable
+ *     workspace); different plans are independent.
+ */
+#ifndef GNN_ATTN_H
+#define GNN_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GNN_F32 = 0, GNN_BF16 = 1 } gnn_dtype_t;
+
+typedef enum {
+    GNN_OK = 0,
+    GNN_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent sizes   */
+    GNN_ERR_UNSUPPORTED = -2,  /* D not in {16,32,64,128}, unknown dtype, plan lacks a part */
+    GNN_ERR_ALIGNMENT = -3,    /* feature pointer not 16-byte aligned                 */
+    GNN_ERR_OOM = -4,          /* device allocation failed                            */
+    GNN_ERR_HIP = -5,          /* a HIP runtime call failed (see gnn_status_string)   */
+    GNN_ERR_BAD_GRAPH = -6     /* indptr/indices inconsistent or out of range         */
+} gnn_status_t;
+
+typedef struct gnn_plan_s *gnn_plan_t;   /* opaque; owns its device arrays */
+
+/*
+ * Plan options (degree-aware tiling, technical summary, Methodology).
+ * The pages name a degree threshold but give no value; these are tunables.
+ */
+typedef struct {
+    int32_t light_threshold; /* T: in-degree <= T is light (one wave per node); default 512   */
+    int32_t chunk;           /* C: edges per wave on a heavy row; default 512, >= 1             */
+    int32_t waves_per_group; /* W: waves per heavy workgroup, merged in LDS; 1, 2, 4 or 8; default 4 */
+    float tile_density;      /* tau: a 16x16 block with >= tau*256 edges becomes a dense tile;
+                                <= 0 disables the tile path; default 0                         */
+    int32_t want_csc;        /* build the transposed adjacency and its out-degree buckets,
+                                needed by gnn_attn_bwd; default 0                               */
+} gnn_plan_opts;
+
+/* Fill *opts with the defaults above. Returns GNN_ERR_INVALID_ARG if opts is NULL. */
+int gnn_plan_opts_default(gnn_plan_opts *opts /*host*/);
+
+/*
+ * Canonical CSR by destination from a COO edge list (edge src[k] -> dst[k]).
+ * Rows ascend by destination, each row's sources ascend, duplicate pairs are
+ * removed, and with add_self_loops != 0 every node has the pair (i, i)
+ * exactly once. Device radix sort on 64-bit (dst, src) keys, then
+ * de-duplication and row boundaries; bit-exact and deterministic.
+ *   src, dst      int32 [n_edges_in], device; each in [0, n_nodes)
+ *   indptr        int32 [n_nodes+1], device, written
+ *   indices       int32 [cap], device, written up to min(E, cap)
+ *   n_edges_out   host; receives E (the number of unique edges)
+ * Errors: GNN_ERR_BAD_GRAPH if an endpoint is out of range; GNN_ERR_INVALID_ARG
+ * if E > cap (indptr is then complete, indices truncated). Temporary device
+ * memory (about 20 bytes per input edge) is allocated and freed inside.
+ * Synchronises `stream` once.
+ */
+int gnn_csr_build(const int32_t *src, const int32_t *dst, int64_t n_edges_in, int32_t n_nodes,
+                  int32_t add_self_loops, int32_t *indptr, int32_t *indices, int64_t cap,
+                  int64_t *n_edges_out /*host*/, hipStream_t stream);
+
+/*
+ * Build a plan for one CSR graph: validates indptr/indices (monotone,
+ * indptr[N] = E, indices in range), splits nodes into light/heavy by
+ * in-degree with the heavy chunk-group table, and, as opts ask, the
+ * transposed adjacency with out-degree buckets and the 16x16 tile census.
+ * opts NULL means defaults. Synchronises `stream` once. *plan_out is set only
+ * on success.
+ */
+int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nodes, int64_t n_edges,
+                    const gnn_plan_opts *opts /*host, nullable*/, hipStream_t stream,
+                    gnn_plan_t *plan_out /*host*/);
+
+/* Counts and device pointers of a plan's arrays (read-only views, owned by the plan). */
+typedef struct {
+    int32_t n_nodes;
+    int64_t n_edges;
+    int32_t light_threshold, chunk, waves_per_group;
+    /* in-degree buckets over the CSR */
+    int32_t n_light, n_heavy, n_groups;
+    const int32_t *light_ids;   /* [n_light]   ascending node ids with deg <= T          */
+    const int32_t *heavy_ids;   /* [n_heavy]   ascending node ids with deg > T           */
+    const int32_t *groups;      /* [n_groups][3] (node, e0, e1), e1 - e0 <= C*W          */
+    const int32_t *partial_ofs; /* [n_heavy+1] group range of each heavy node            */
+    /* transposed adjacency and out-degree buckets (want_csc) */
+    int32_t has_csc;
+    const int32_t *cindptr;     /* [N+1] */
+    const int32_t *cindices;    /* [E]   destinations of each source, ascending          */
+    int32_t c_n_light, c_n_heavy, c_n_groups;
+    const int32_t *c_light_ids, *c_heavy_ids, *c_groups, *c_partial_ofs;
+    /* 16x16 tiles (tile_density > 0) */
+    int32_t has_tiles, n_tiles, tile_min_nnz;
+    const int32_t *tile_rc;     /* [n_tiles][2] (row block, col block), ascending       */
+    const uint64_t *tile_mask;  /* [n_tiles][4] bit (dst%16)*16 + (src%16), word = bit/64 */
+    const int32_t *tile_ptr;    /* [ceil(N/16)+1] tiles of each row block               */
+    const int32_t *rindptr;     /* [N+1] residual CSR (edges outside tiles)             */
+    const int32_t *rindices;    /* [n_residual]                                         */
+    int64_t n_residual;
+    /* device memory owned by the plan */
+    int64_t structure_bytes;    /* buckets, transposed adjacency, tiles                 */
+    int64_t workspace_bytes;    /* heavy partials and backward statistics (grows lazily) */
+    int64_t largest_workspace_alloc;
+} gnn_plan_info;
+
+int gnn_plan_export(gnn_plan_t plan, gnn_plan_info *info /*host*/);
+int gnn_plan_destroy(gnn_plan_t plan);
+
+/*
+ * Graph-Transformer attention forward: for each node i and head h,
+ *   s_ij = scale * <Q[i,h,:], K[j,h,:]> over j in row i,
+ *   O[i,h,:] = sum_j softmax_j(s_ij) V[j,h,:],  LSE[i,h] = ln sum_j exp(s_ij).
+ * One streaming pass with an online softmax; no per-edge value reaches
+ * memory. plan NULL runs every node on the light (one wave per node) path;
+ * otherwise the plan's buckets are used and must describe this graph.
+ * scale <= 0 means 1/sqrt(D). LSE may be NULL.
+ */
+int gnn_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
+                 int32_t H, int32_t D, const void *Q, const void *K, const void *V, void *O,
+                 float *LSE /*nullable*/, float scale, gnn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Graph-Transformer attention backward from the cached LSE (the forward's
+ * output for the same inputs): weights are recomputed per edge as
+ * p_ij = exp(s_ij - LSE_i), and with dp_ij = <dO_i, V_j>,
+ * Delta_i = sum_j p_ij dp_ij (which equals <dO_i, O_i> for the exact O):
+ *   dQ_i = scale * sum_j p_ij (dp_ij - Delta_i) K_j        (destination pass, CSR)
+ *   dK_j = scale * sum_i p_ij (dp_ij - Delta_i) Q_i        (source pass, CSC)
+ *   dV_j = sum_i p_ij dO_i
+ * The destination pass forms Delta_i from the recomputed weights in the same
+ * sweep that accumulates dQ_i, so a bf16-rounded O never enters the
+ * gradients; O is therefore not read and may be NULL (it is kept in the
+ * signature so callers can pass the forward's outputs unchanged).
+ * The plan must have been created with want_csc. No atomics: results are
+ * bitwise reproducible for the same inputs and plan. dQ, dK, dV must not
+ * alias inputs.
+ */
+int gnn_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
+                 int32_t H, int32_t D, const void *Q, const void *K, const void *V, const void *O,
+                 const void *dO, const float *LSE, void *dQ, void *dK, void *dV, float scale,
+                 gnn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * GATv2 attention forward (the GATv2 layer named by the pages):
+ *   s_ij = sum_d att[h,d] * LeakyReLU(K[j,h,d] + Q[i,h,d]),
+ *   LeakyReLU(x) = x for x >= 0, negative_slope * x otherwise,
+ * with Q = W_d x (destination projection) and K = W_s x (source projection)
+ * given; O[i,h,:] = sum_j softmax_j(s_ij) V[j,h,:], where V is normally the
+ * same buffer as K (then one row is gathered per edge). att is fp32 [H, D].
+ * No score scaling. LSE may be NULL; plan as for gnn_attn_fwd.
+ */
+int gatv2_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
+                   int32_t H, int32_t D, const void *Q, const void *K, const void *V, const float *att,
+                   float negative_slope, void *O, float *LSE /*nullable*/, gnn_dtype_t dtype,
+                   hipStream_t stream);
+
+/*
+ * Per-kernel timing on a plan (for measurement tools). When enabled, every
+ * attention call on the plan records HIP events around each kernel it
+ * launches, on the call's stream. gnn_plan_timing_read synchronises on the
+ * recorded events, reports for each kernel kind the number of launches and
+ * their summed duration in milliseconds, and clears the log.
+ *   names[k]: static strings owned by the library.
+ */
+int gnn_plan_set_timing(gnn_plan_t plan, int32_t enable);
+int gnn_plan_timing_read(gnn_plan_t plan, int32_t cap, const char **names /*host [cap]*/,
+                         int32_t *launches /*host [cap]*/, double *total_ms /*host [cap]*/,
+                         int32_t *n_out /*host*/);
+
+/* Human-readable text for a status code (includes the last HIP error for GNN_ERR_HIP). */
+const char *gnn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GNN_ATTN_H */

@@ -1,0 +1,338 @@
+"""Fused CSR neighbourhood attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/gnn_attn.h`` (library
+``libgnn_attn.so`` built in-tree by ``python -m io_aware_sparse_amd.build``).
+Every function here only marshals arguments: it checks shapes and dtypes,
+allocates outputs with torch when the caller gives none, passes raw device
+pointers and torch's current HIP stream, and turns a non-zero status into
+:class:`GnnError`. All computation runs in the HIP library; there is no
+fallback path, and calls fail loudly when the library is missing.
+
+Function names match the C ABI: gnn_csr_build, gnn_plan_create,
+gnn_plan_export, gnn_plan_destroy, gnn_attn_fwd, gnn_attn_bwd,
+gatv2_attn_fwd, gnn_plan_set_timing, gnn_plan_timing_read,
+gnn_status_string.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgnn_attn.so")
+
+GNN_F32, GNN_BF16 = 0, 1
+GNN_OK = 0
+STATUS = {0: "GNN_OK", -1: "GNN_ERR_INVALID_ARG", -2: "GNN_ERR_UNSUPPORTED", -3: "GNN_ERR_ALIGNMENT",
+          -4: "GNN_ERR_OOM", -5: "GNN_ERR_HIP", -6: "GNN_ERR_BAD_GRAPH"}
+
+# exported symbols, in the order include/gnn_attn.h declares them
+EXPORTS = ["gnn_plan_opts_default", "gnn_csr_build", "gnn_plan_create", "gnn_plan_export", "gnn_plan_destroy",
+           "gnn_attn_fwd", "gnn_attn_bwd", "gatv2_attn_fwd", "gnn_plan_set_timing", "gnn_plan_timing_read",
+           "gnn_status_string"]
+
+
+class GnnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({gnn_status_string(status)})")
+
+
+class PlanOpts(C.Structure):
+    _fields_ = [("light_threshold", C.c_int32), ("chunk", C.c_int32), ("waves_per_group", C.c_int32),
+                ("tile_density", C.c_float), ("want_csc", C.c_int32)]
+
+
+_P32 = C.POINTER(C.c_int32)
+
+
+class PlanInfo(C.Structure):
+    _fields_ = [("n_nodes", C.c_int32), ("n_edges", C.c_int64),
+                ("light_threshold", C.c_int32), ("chunk", C.c_int32), ("waves_per_group", C.c_int32),
+                ("n_light", C.c_int32), ("n_heavy", C.c_int32), ("n_groups", C.c_int32),
+                ("light_ids", C.c_void_p), ("heavy_ids", C.c_void_p), ("groups", C.c_void_p),
+                ("partial_ofs", C.c_void_p),
+                ("has_csc", C.c_int32), ("cindptr", C.c_void_p), ("cindices", C.c_void_p),
+                ("c_n_light", C.c_int32), ("c_n_heavy", C.c_int32), ("c_n_groups", C.c_int32),
+                ("c_light_ids", C.c_void_p), ("c_heavy_ids", C.c_void_p), ("c_groups", C.c_void_p),
+                ("c_partial_ofs", C.c_void_p),
+                ("has_tiles", C.c_int32), ("n_tiles", C.c_int32), ("tile_min_nnz", C.c_int32),
+                ("tile_rc", C.c_void_p), ("tile_mask", C.c_void_p), ("tile_ptr", C.c_void_p),
+                ("rindptr", C.c_void_p), ("rindices", C.c_void_p), ("n_residual", C.c_int64),
+                ("structure_bytes", C.c_int64), ("workspace_bytes", C.c_int64),
+                ("largest_workspace_alloc", C.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library missing: {LIB_PATH}; build it with "
+                               "`python -m io_aware_sparse_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        V, I32, I64, F = C.c_void_p, C.c_int32, C.c_int64, C.c_float
+        L.gnn_plan_opts_default.argtypes = [C.POINTER(PlanOpts)]
+        L.gnn_csr_build.argtypes = [V, V, I64, I32, I32, V, V, I64, C.POINTER(C.c_int64), V]
+        L.gnn_plan_create.argtypes = [V, V, I32, I64, C.POINTER(PlanOpts), V, C.POINTER(V)]
+        L.gnn_plan_export.argtypes = [V, C.POINTER(PlanInfo)]
+        L.gnn_plan_destroy.argtypes = [V]
+        L.gnn_attn_fwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, V, F, C.c_int, V]
+        L.gnn_attn_bwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, V, V, V, V, V, F, C.c_int, V]
+        L.gatv2_attn_fwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, F, V, V, C.c_int, V]
+        L.gnn_plan_set_timing.argtypes = [V, I32]
+        L.gnn_plan_timing_read.argtypes = [V, I32, C.POINTER(C.c_char_p), C.POINTER(C.c_int32),
+                                           C.POINTER(C.c_double), C.POINTER(C.c_int32)]
+        L.gnn_status_string.argtypes = [C.c_int]
+        L.gnn_status_string.restype = C.c_char_p
+        for name in EXPORTS:
+            if name != "gnn_status_string":
+                getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def gnn_status_string(status: int) -> str:
+    return lib().gnn_status_string(int(status)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != GNN_OK:
+        raise GnnError(rc, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return GNN_F32
+    if t.dtype == torch.bfloat16:
+        return GNN_BF16
+    raise TypeError(f"features must be float32 or bfloat16, got {t.dtype}")
+
+
+def _feat(t, name, shape=None, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dim() != 3 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [N, H, D] tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t
+
+
+def _graph(indptr, indices):
+    torch = _torch()
+    for t, nm in ((indptr, "indptr"), (indices, "indices")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{nm} must be a contiguous int32 device tensor")
+    return int(indptr.numel()) - 1, int(indices.numel())
+
+
+# ---------------------------------------------------------------------------
+
+def gnn_csr_build(src, dst, n_nodes: int, add_self_loops: bool = True, stream=None):
+    """CSR by destination (sorted, de-duplicated, optional self-loops) on the device.
+    Returns (indptr int32 [N+1], indices int32 [E])."""
+    torch = _torch()
+    for t, nm in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{nm} must be a contiguous int32 device tensor")
+    m = int(src.numel())
+    if int(dst.numel()) != m:
+        raise ValueError("src and dst differ in length")
+    cap = m + (n_nodes if add_self_loops else 0)
+    indptr = torch.empty(n_nodes + 1, dtype=torch.int32, device=src.device)
+    indices = torch.empty(max(cap, 1), dtype=torch.int32, device=src.device)
+    e = C.c_int64(0)
+    _check(lib().gnn_csr_build(_ptr(src), _ptr(dst), m, int(n_nodes), int(bool(add_self_loops)), _ptr(indptr),
+                               _ptr(indices), cap, C.byref(e), _stream(stream)), "gnn_csr_build")
+    return indptr, indices[: e.value]
+
+
+class Plan:
+    """Owning handle of a gnn_plan_t; keeps the graph tensors alive."""
+
+    def __init__(self, handle: int, indptr, indices, opts: PlanOpts):
+        self.handle = handle
+        self.indptr = indptr
+        self.indices = indices
+        self.opts = opts
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.gnn_plan_destroy(C.c_void_p(h))
+            self.handle = None
+
+    def destroy(self):
+        if self.handle:
+            lib().gnn_plan_destroy(C.c_void_p(self.handle))
+            self.handle = None
+
+
+def gnn_plan_create(indptr, indices, light_threshold: int = 512, chunk: int = 512, waves_per_group: int = 4,
+                    tile_density: float = 0.0, want_csc: bool = False, stream=None) -> Plan:
+    n, e = _graph(indptr, indices)
+    o = PlanOpts()
+    lib().gnn_plan_opts_default(C.byref(o))
+    o.light_threshold, o.chunk, o.waves_per_group = int(light_threshold), int(chunk), int(waves_per_group)
+    o.tile_density, o.want_csc = float(tile_density), int(bool(want_csc))
+    h = C.c_void_p()
+    _check(lib().gnn_plan_create(_ptr(indptr), _ptr(indices) if e else None, n, e, C.byref(o), _stream(stream),
+                                 C.byref(h)), "gnn_plan_create")
+    return Plan(h.value, indptr, indices, o)
+
+
+def gnn_plan_destroy(plan: Plan):
+    plan.destroy()
+
+
+def _copy_dev(ptr, count, np_dtype):
+    """Copy `count` elements from a device pointer to a new numpy array."""
+    import numpy as np
+    torch = _torch()
+    out = np.empty(int(count), np_dtype)
+    if count == 0 or not ptr:
+        return out
+    torch.cuda.synchronize()
+    hip = C.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int]
+    hip.hipMemcpy.restype = C.c_int
+    rc = hip.hipMemcpy(out.ctypes.data_as(C.c_void_p), C.c_void_p(ptr), out.nbytes, 2)  # device to host
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed ({rc})")
+    return out
+
+
+def gnn_plan_export(plan: Plan, arrays: bool = False) -> dict:
+    """Plan counts (and, with arrays=True, host copies of its device arrays)."""
+    import numpy as np
+    info = PlanInfo()
+    _check(lib().gnn_plan_export(C.c_void_p(plan.handle), C.byref(info)), "gnn_plan_export")
+    d = {k: getattr(info, k) for k, t in PlanInfo._fields_ if t is not C.c_void_p}
+    if arrays:
+        n = info.n_nodes
+        d["light"] = _copy_dev(info.light_ids, info.n_light, np.int32)
+        d["heavy"] = _copy_dev(info.heavy_ids, info.n_heavy, np.int32)
+        d["groups"] = _copy_dev(info.groups, 3 * info.n_groups, np.int32).reshape(-1, 3)
+        d["partial_ofs"] = _copy_dev(info.partial_ofs, info.n_heavy + 1, np.int32)
+        if info.has_csc:
+            d["cindptr"] = _copy_dev(info.cindptr, n + 1, np.int32)
+            d["cindices"] = _copy_dev(info.cindices, info.n_edges, np.int32)
+            d["c_light"] = _copy_dev(info.c_light_ids, info.c_n_light, np.int32)
+            d["c_heavy"] = _copy_dev(info.c_heavy_ids, info.c_n_heavy, np.int32)
+            d["c_groups"] = _copy_dev(info.c_groups, 3 * info.c_n_groups, np.int32).reshape(-1, 3)
+            d["c_partial_ofs"] = _copy_dev(info.c_partial_ofs, info.c_n_heavy + 1, np.int32)
+        if info.has_tiles:
+            d["tile_rc"] = _copy_dev(info.tile_rc, 2 * info.n_tiles, np.int32).reshape(-1, 2)
+            d["tile_mask"] = _copy_dev(info.tile_mask, 4 * info.n_tiles, np.uint64).reshape(-1, 4)
+            d["tile_ptr"] = _copy_dev(info.tile_ptr, (n + 15) // 16 + 1, np.int32)
+            d["rindptr"] = _copy_dev(info.rindptr, n + 1, np.int32)
+            d["rindices"] = _copy_dev(info.rindices, info.n_residual, np.int32)
+    return d
+
+
+def _plan_handle(plan):
+    return None if plan is None else C.c_void_p(plan.handle)
+
+
+def gnn_attn_fwd(plan: Optional[Plan], indptr, indices, Q, K, V, O=None, LSE=None, scale: float = 0.0,
+                 want_lse: bool = True, stream=None):
+    """Graph-Transformer attention forward. Returns (O, LSE or None)."""
+    torch = _torch()
+    n, e = _graph(indptr, indices)
+    _feat(Q, "Q")
+    N, H, D = Q.shape
+    if N != n:
+        raise ValueError("Q rows differ from the graph's node count")
+    _feat(K, "K", Q.shape, Q.dtype)
+    _feat(V, "V", Q.shape, Q.dtype)
+    O = torch.empty_like(Q) if O is None else _feat(O, "O", Q.shape, Q.dtype)
+    if LSE is None and want_lse:
+        LSE = torch.empty((N, H), dtype=torch.float32, device=Q.device)
+    _check(lib().gnn_attn_fwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
+                              _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), float(scale), _dtype_code(Q),
+                              _stream(stream)), "gnn_attn_fwd")
+    return O, LSE
+
+
+def gatv2_attn_fwd(plan: Optional[Plan], indptr, indices, XD, XS, att, V=None, negative_slope: float = 0.2,
+                   O=None, LSE=None, want_lse: bool = True, stream=None):
+    """GATv2 attention forward (V defaults to XS itself). Returns (O, LSE or None)."""
+    torch = _torch()
+    n, e = _graph(indptr, indices)
+    _feat(XD, "XD")
+    N, H, D = XD.shape
+    if N != n:
+        raise ValueError("XD rows differ from the graph's node count")
+    _feat(XS, "XS", XD.shape, XD.dtype)
+    V = XS if V is None else _feat(V, "V", XD.shape, XD.dtype)
+    if not (att.is_cuda and att.dtype == torch.float32 and att.is_contiguous() and tuple(att.shape) == (H, D)):
+        raise TypeError("att must be a contiguous float32 [H, D] device tensor")
+    O = torch.empty_like(XD) if O is None else _feat(O, "O", XD.shape, XD.dtype)
+    if LSE is None and want_lse:
+        LSE = torch.empty((N, H), dtype=torch.float32, device=XD.device)
+    _check(lib().gatv2_attn_fwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
+                                _ptr(XD), _ptr(XS), _ptr(V), _ptr(att), float(negative_slope), _ptr(O), _ptr(LSE),
+                                _dtype_code(XD), _stream(stream)), "gatv2_attn_fwd")
+    return O, LSE
+
+
+def gnn_attn_bwd(plan: Plan, indptr, indices, Q, K, V, O, dO, LSE, dQ=None, dK=None, dV=None, scale: float = 0.0,
+                 stream=None):
+    """Graph-Transformer attention backward from the cached LSE. Returns (dQ, dK, dV)."""
+    torch = _torch()
+    n, e = _graph(indptr, indices)
+    _feat(Q, "Q")
+    N, H, D = Q.shape
+    for t, nm in ((K, "K"), (V, "V"), (dO, "dO")):
+        _feat(t, nm, Q.shape, Q.dtype)
+    if O is not None:
+        _feat(O, "O", Q.shape, Q.dtype)
+    if not (LSE.is_cuda and LSE.dtype == torch.float32 and tuple(LSE.shape) == (N, H) and LSE.is_contiguous()):
+        raise TypeError("LSE must be a contiguous float32 [N, H] device tensor")
+    dQ = torch.empty_like(Q) if dQ is None else _feat(dQ, "dQ", Q.shape, Q.dtype)
+    dK = torch.empty_like(Q) if dK is None else _feat(dK, "dK", Q.shape, Q.dtype)
+    dV = torch.empty_like(Q) if dV is None else _feat(dV, "dV", Q.shape, Q.dtype)
+    _check(lib().gnn_attn_bwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
+                              _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
+                              float(scale), _dtype_code(Q), _stream(stream)), "gnn_attn_bwd")
+    return dQ, dK, dV
+
+
+def gnn_plan_set_timing(plan: Plan, enable: bool = True):
+    _check(lib().gnn_plan_set_timing(C.c_void_p(plan.handle), int(bool(enable))), "gnn_plan_set_timing")
+
+
+def gnn_plan_timing_read(plan: Plan) -> dict:
+    """{kernel name: (launches, total ms)} since the last read; clears the log."""
+    cap = 16
+    names = (C.c_char_p * cap)()
+    launches = (C.c_int32 * cap)()
+    ms = (C.c_double * cap)()
+    n = C.c_int32(0)
+    _check(lib().gnn_plan_timing_read(C.c_void_p(plan.handle), cap, names, launches, ms, C.byref(n)),
+           "gnn_plan_timing_read")
+    return {names[k].decode(): (int(launches[k]), float(ms[k])) for k in range(min(n.value, cap))}

@@ -1,0 +1,104 @@
+// Device-side helpers for gfx950 (CDNA4, 64-lane wavefronts).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gnn {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Cross-lane move through the DPP network (no LDS traffic). CTRL encodings
+// (GFX9 DPP): 0xB1 quad_perm[1,0,3,2], 0x4E quad_perm[2,3,0,1],
+// 0x141 row_half_mirror, 0x140 row_mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float xor_lane(float x, int off) { return __shfl_xor(x, off, kWave); }
+
+// Sum over aligned groups of G lanes (G a power of two <= 64). Every lane of
+// a group receives the same, bitwise identical total (each step adds a
+// commutative pair).
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (G >= 2) x += dpp<0xB1>(x);
+    if constexpr (G >= 4) x += dpp<0x4E>(x);
+    if constexpr (G >= 8) x += dpp<0x141>(x);
+    if constexpr (G >= 16) x += dpp<0x140>(x);
+    if constexpr (G >= 32) x += xor_lane(x, 16);
+    if constexpr (G >= 64) x += xor_lane(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// --------------------------------------------------------------------------
+// 16-byte row vectors: 4 fp32 or 8 bf16 per lane.
+// --------------------------------------------------------------------------
+struct bf16_tag {};
+
+template <class T>
+struct Vec;
+
+template <>
+struct Vec<float> {
+    static constexpr int N = 4;
+    using raw = float4;
+    static constexpr int bytes = 4;
+    __device__ __forceinline__ static void unpack(const raw &r, float (&o)[N]) {
+        o[0] = r.x; o[1] = r.y; o[2] = r.z; o[3] = r.w;
+    }
+    __device__ __forceinline__ static raw pack(const float (&o)[N]) { return make_float4(o[0], o[1], o[2], o[3]); }
+    __device__ __forceinline__ static raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;  // NaN stays NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+template <>
+struct Vec<bf16_tag> {
+    static constexpr int N = 8;
+    using raw = uint4;
+    static constexpr int bytes = 2;
+    __device__ __forceinline__ static void unpack(const raw &r, float (&o)[N]) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            o[2 * k] = __uint_as_float(w[k] << 16);
+            o[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    }
+    __device__ __forceinline__ static raw pack(const float (&o)[N]) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = f32_to_bf16_rne(o[2 * k]) | (f32_to_bf16_rne(o[2 * k + 1]) << 16);
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    __device__ __forceinline__ static raw zero() { return make_uint4(0u, 0u, 0u, 0u); }
+};
+
+template <class T>
+__device__ __forceinline__ typename Vec<T>::raw load_vec(const void *base, int64_t elem_off) {
+    using raw = typename Vec<T>::raw;
+    return *reinterpret_cast<const raw *>(reinterpret_cast<const char *>(base) + elem_off * Vec<T>::bytes);
+}
+
+template <class T>
+__device__ __forceinline__ void store_vec(void *base, int64_t elem_off, const typename Vec<T>::raw &v) {
+    using raw = typename Vec<T>::raw;
+    *reinterpret_cast<raw *>(reinterpret_cast<char *>(base) + elem_off * Vec<T>::bytes) = v;
+}
+
+}  // namespace gnn

@@ -1,0 +1,90 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call
+(no GPU is needed for any of these; no compute is launched)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gnn_attn.h")
+
+
+@pytest.fixture(scope="module")
+def g():
+    import io_aware_sparse_amd as g
+    if not os.path.exists(g.LIB_PATH):
+        from io_aware_sparse_amd import build
+        build.build()
+    g.lib()
+    return g
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function(g):
+    names = declared_functions()
+    assert "gnn_attn_fwd" in names and "gatv2_attn_fwd" in names and "gnn_attn_bwd" in names
+    for n in names:
+        assert hasattr(g.lib(), n), n
+    assert sorted(g.EXPORTS) == names
+
+
+def test_status_strings(g):
+    for code in (0, -1, -2, -3, -4, -5, -6, 99):
+        assert isinstance(g.gnn_status_string(code), str)
+    assert g.gnn_status_string(-3).startswith("feature pointer")
+
+
+def test_host_validation(g):
+    L = g.lib()
+    A = 0x10000        # aligned fake device address: never dereferenced on these paths
+    # attention forward
+    fwd = lambda N=10, E=20, H=2, D=32, q=A, dt=0, ip=A: L.gnn_attn_fwd(None, ip, A, N, E, H, D, q, A, A, A, None,
+                                                                        0.0, dt, None)
+    assert fwd(D=24) == -2 and fwd(D=0) == -2 and fwd(D=256) == -2
+    assert fwd(dt=7) == -2
+    assert fwd(N=-1) == -1 and fwd(E=-1) == -1 and fwd(H=0) == -1 and fwd(E=1 << 31) == -1
+    assert fwd(q=A + 4) == -3
+    assert fwd(ip=None) == -1
+    assert L.gnn_attn_fwd(None, A, A, 10, 20, 2, 32, None, A, A, A, None, 0.0, 0, None) == -1
+    assert L.gnn_attn_fwd(None, A, A, 0, 0, 2, 32, A, A, A, A, None, 0.0, 0, None) == 0   # empty graph: no-op
+    # GATv2 needs att
+    assert L.gatv2_attn_fwd(None, A, A, 10, 20, 2, 32, A, A, A, None, 0.2, A, None, 0, None) == -1
+    # backward needs a plan
+    assert L.gnn_attn_bwd(None, A, A, 10, 20, 2, 32, A, A, A, A, A, A, A, A, A, 0.0, 0, None) == -1
+    # CSR build
+    e = C.c_int64()
+    assert L.gnn_csr_build(A, A, 5, -1, 1, A, A, 10, C.byref(e), None) == -1
+    assert L.gnn_csr_build(None, A, 5, 3, 1, A, A, 10, C.byref(e), None) == -1
+    assert L.gnn_csr_build(A, A, 5, 3, 1, A, A, 10, None, None) == -1
+    assert L.gnn_csr_build(A, A, 1 << 31, 3, 1, A, A, 10, C.byref(e), None) == -1
+    # plans
+    h = C.c_void_p()
+    o = g.PlanOpts()
+    assert L.gnn_plan_opts_default(C.byref(o)) == 0 and o.light_threshold == 512 and o.waves_per_group == 4
+    assert L.gnn_plan_opts_default(None) == -1
+    assert L.gnn_plan_create(None, A, 10, 20, None, None, C.byref(h)) == -1
+    assert L.gnn_plan_create(A, A, 10, 20, None, None, None) == -1
+    for field, bad in (("waves_per_group", 3), ("chunk", 0), ("light_threshold", -1)):
+        L.gnn_plan_opts_default(C.byref(o))
+        setattr(o, field, bad)
+        assert L.gnn_plan_create(A, A, 10, 20, C.byref(o), None, C.byref(h)) == -1, field
+    assert L.gnn_plan_export(None, None) == -1
+    assert L.gnn_plan_destroy(None) == -1
+    assert L.gnn_plan_set_timing(None, 1) == -1
+    n = C.c_int32()
+    assert L.gnn_plan_timing_read(None, 0, None, None, None, C.byref(n)) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import io_aware_sparse_amd as g
+    monkeypatch.setattr(g, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(g, "_lib", None)
+    with pytest.raises(RuntimeError, match="HIP library missing"):
+        g.lib()

@@ -1,0 +1,232 @@
+"""GPU parity of the fused attention kernels against the fp64 oracle.
+
+Graphs are small enough for the oracle to finish in seconds but span many
+workgroups, heavy rows with several chunk groups and ragged last chunks, and
+rows whose degree is not a multiple of the per-step edge count. Plans are
+exercised light-only, heavy-forced and mixed."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from _gpu import TOL, dev_feat, dev_i32, host, rand_feats, say
+
+pytestmark = pytest.mark.gpu
+
+PLANS = {
+    "none": None,
+    "light": dict(light_threshold=10 ** 9, chunk=512, waves_per_group=4),
+    "heavy": dict(light_threshold=0, chunk=5, waves_per_group=4),
+    "heavy_w1": dict(light_threshold=0, chunk=3, waves_per_group=1),
+    "mixed": dict(light_threshold=16, chunk=8, waves_per_group=2),
+    "mixed_w8": dict(light_threshold=40, chunk=16, waves_per_group=8),
+}
+
+
+@pytest.fixture(scope="module")
+def g():
+    import io_aware_sparse_amd as g
+    g.lib()
+    return g
+
+
+def _graph(g, seed, n, self_loops=True):
+    """Chung-Lu power-law graph (hubs up to a few hundred in-edges)."""
+    wl = workloads.make("gt_chunglu25_n169k", n, features=False)
+    src, dst = wl.src, wl.dst
+    if not self_loops:
+        # drop every in-edge of a few nodes to create empty rows
+        rng = np.random.default_rng(seed)
+        empty = rng.choice(n, max(1, n // 50), replace=False)
+        keep = ~np.isin(dst, empty)
+        src, dst = src[keep], dst[keep]
+    rp, rx = oracle.csr_build(src, dst, n, add_self_loops=self_loops)
+    ip, ix = g.gnn_csr_build(dev_i32(src), dev_i32(dst), n, add_self_loops=self_loops)
+    assert np.array_equal(ip.cpu().numpy(), rp) and np.array_equal(ix.cpu().numpy(), rx)
+    return ip, ix, rp, rx
+
+
+def _plan(g, ip, ix, name, want_csc=False):
+    p = PLANS[name]
+    return None if p is None else g.gnn_plan_create(ip, ix, want_csc=want_csc, **p)
+
+
+def _check(name, x, ref, scale, dtype):
+    err = oracle.scaled_error(x, ref, scale)
+    say(f"  {name}: scaled err {err:.3e} (tol {TOL[dtype]:.0e})")
+    assert err <= TOL[dtype], (name, err)
+
+
+CASES = [("f32", 16, 1), ("f32", 32, 4), ("f32", 64, 2), ("f32", 128, 3), ("f32", 16, 8),
+         ("bf16", 16, 2), ("bf16", 32, 4), ("bf16", 64, 8), ("bf16", 128, 1)]
+
+
+@pytest.mark.parametrize("dtype,D,H", CASES)
+@pytest.mark.parametrize("plan", ["none", "light", "heavy", "mixed"])
+def test_gt_fwd_parity(g, dtype, D, H, plan):
+    n = 3000
+    say("gt_fwd", dtype, D, H, plan)
+    ip, ix, rp, rx = _graph(g, 1, n)
+    rng = np.random.default_rng(D * 7 + H)
+    Q, K, V = rand_feats(rng, n, H, D, dtype)
+    pl = _plan(g, ip, ix, plan)
+    O, L = g.gnn_attn_fwd(pl, ip, ix, dev_feat(Q, dtype), dev_feat(K, dtype), dev_feat(V, dtype))
+    ref = oracle.gt_fwd(rp, rx, Q, K, V)
+    _check("O", host(O), ref["O"], ref["SO"], dtype)
+    _check("LSE", host(L), ref["LSE"], ref["SL"], "f32")
+
+
+@pytest.mark.parametrize("plan", ["none", "heavy_w1", "mixed", "mixed_w8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gt_fwd_empty_rows_and_scale(g, plan, dtype):
+    n, H, D = 2500, 2, 32
+    say("gt_fwd empty rows", plan, dtype)
+    ip, ix, rp, rx = _graph(g, 2, n, self_loops=False)
+    assert np.any(np.diff(rp) == 0)
+    rng = np.random.default_rng(3)
+    Q, K, V = rand_feats(rng, n, H, D, dtype)
+    pl = _plan(g, ip, ix, plan)
+    O, L = g.gnn_attn_fwd(pl, ip, ix, dev_feat(Q, dtype), dev_feat(K, dtype), dev_feat(V, dtype), scale=0.3)
+    ref = oracle.gt_fwd(rp, rx, Q, K, V, scale=0.3)
+    _check("O", host(O), ref["O"], ref["SO"], dtype)
+    _check("LSE", host(L), ref["LSE"], ref["SL"], "f32")
+    empty = np.diff(rp) == 0
+    assert np.all(host(O)[empty] == 0) and np.all(np.isneginf(host(L)[empty]))
+
+
+@pytest.mark.parametrize("dtype,D,H", [("f32", 16, 8), ("f32", 32, 2), ("bf16", 16, 8), ("bf16", 64, 4),
+                                       ("f32", 128, 1)])
+@pytest.mark.parametrize("plan", ["none", "heavy", "mixed"])
+@pytest.mark.parametrize("sep_v", [False, True])
+def test_gatv2_fwd_parity(g, dtype, D, H, plan, sep_v):
+    n = 3000
+    say("gatv2_fwd", dtype, D, H, plan, sep_v)
+    ip, ix, rp, rx = _graph(g, 4, n)
+    rng = np.random.default_rng(D + H)
+    XD, XS, V = rand_feats(rng, n, H, D, dtype)
+    att = (rng.standard_normal((H, D)) / np.sqrt(D)).astype(np.float32)
+    import torch
+    pl = _plan(g, ip, ix, plan)
+    xs = dev_feat(XS, dtype)
+    O, L = g.gatv2_attn_fwd(pl, ip, ix, dev_feat(XD, dtype), xs, torch.from_numpy(att).cuda(),
+                            V=dev_feat(V, dtype) if sep_v else None, negative_slope=0.2)
+    ref = oracle.gatv2_fwd(rp, rx, XD, XS, att, V=V if sep_v else None, slope=0.2)
+    _check("O", host(O), ref["O"], ref["SO"], dtype)
+    _check("LSE", host(L), ref["LSE"], ref["SL"], "f32")
+
+
+@pytest.mark.parametrize("dtype,D,H", [("f32", 16, 1), ("f32", 32, 4), ("f32", 64, 3), ("f32", 128, 2),
+                                       ("bf16", 32, 4), ("bf16", 64, 8), ("bf16", 16, 2)])
+@pytest.mark.parametrize("plan", ["light", "heavy", "mixed", "mixed_w8"])
+def test_gt_bwd_parity(g, dtype, D, H, plan):
+    n = 2500
+    say("gt_bwd", dtype, D, H, plan)
+    ip, ix, rp, rx = _graph(g, 5, n, self_loops=(plan != "mixed"))
+    rng = np.random.default_rng(11 * D + H)
+    Q, K, V, dO = rand_feats(rng, n, H, D, dtype, k=4)
+    pl = _plan(g, ip, ix, plan, want_csc=True)
+    q, k, v, go = (dev_feat(x, dtype) for x in (Q, K, V, dO))
+    O, L = g.gnn_attn_fwd(pl, ip, ix, q, k, v)
+    dq, dk, dv = g.gnn_attn_bwd(pl, ip, ix, q, k, v, O, go, L)
+    ref = oracle.gt_bwd(rp, rx, Q, K, V, dO)
+    _check("dQ", host(dq), ref["dQ"], ref["SdQ"], dtype)
+    _check("dK", host(dk), ref["dK"], ref["SdK"], dtype)
+    _check("dV", host(dv), ref["dV"], ref["SdV"], dtype)
+
+
+def test_determinism_bitwise(g):
+    n, H, D, dtype = 4000, 4, 32, "bf16"
+    say("determinism")
+    ip, ix, rp, rx = _graph(g, 6, n)
+    rng = np.random.default_rng(6)
+    q, k, v, go = (dev_feat(x, dtype) for x in rand_feats(rng, n, H, D, dtype, k=4))
+    pl = _plan(g, ip, ix, "mixed", want_csc=True)
+    outs = []
+    for _ in range(2):
+        O, L = g.gnn_attn_fwd(pl, ip, ix, q, k, v)
+        dq, dk, dv = g.gnn_attn_bwd(pl, ip, ix, q, k, v, O, go, L)
+        outs.append([t.clone() for t in (O, L, dq, dk, dv)])
+    import torch
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_special_graphs(g):
+    import torch
+    rng = np.random.default_rng(8)
+    H, D, dtype = 2, 16, "f32"
+    graphs = {}
+    n = 700                                             # star: node 0 hears from everyone
+    graphs["star"] = (np.arange(1, n, dtype=np.int32), np.zeros(n - 1, np.int32), n)
+    n = 64                                              # complete digraph
+    a, b = np.meshgrid(np.arange(n), np.arange(n))
+    graphs["complete"] = (a.ravel().astype(np.int32), b.ravel().astype(np.int32), n)
+    graphs["single"] = (np.zeros(0, np.int32), np.zeros(0, np.int32), 1)
+    graphs["self_only"] = (np.zeros(0, np.int32), np.zeros(0, np.int32), 300)
+    for name, (src, dst, n) in graphs.items():
+        say("special", name)
+        rp, rx = oracle.csr_build(src, dst, n)
+        ip, ix = g.gnn_csr_build(dev_i32(src), dev_i32(dst), n)
+        assert np.array_equal(ip.cpu().numpy(), rp) and np.array_equal(ix.cpu().numpy(), rx)
+        Q, K, V, dO = rand_feats(rng, n, H, D, dtype, k=4)
+        for plan in ("light", "heavy", "mixed"):
+            pl = _plan(g, ip, ix, plan, want_csc=True)
+            q, k, v, go = (dev_feat(x, dtype) for x in (Q, K, V, dO))
+            O, L = g.gnn_attn_fwd(pl, ip, ix, q, k, v)
+            ref = oracle.gt_fwd(rp, rx, Q, K, V)
+            _check(f"{name}/{plan} O", host(O), ref["O"], ref["SO"], dtype)
+            dq, dk, dv = g.gnn_attn_bwd(pl, ip, ix, q, k, v, O, go, L)
+            rb = oracle.gt_bwd(rp, rx, Q, K, V, dO)
+            _check(f"{name}/{plan} dQ", host(dq), rb["dQ"], rb["SdQ"], dtype)
+            _check(f"{name}/{plan} dK", host(dk), rb["dK"], rb["SdK"], dtype)
+            _check(f"{name}/{plan} dV", host(dv), rb["dV"], rb["SdV"], dtype)
+    torch.cuda.synchronize()
+
+
+def test_multigraph_rows(g):
+    """Duplicate entries in a row are each counted (CSR assembled on the host)."""
+    import torch
+    n, H, D, dtype = 500, 2, 32, "f32"
+    rng = np.random.default_rng(9)
+    deg = rng.integers(0, 40, n)
+    rp = np.concatenate([[0], np.cumsum(deg)]).astype(np.int32)
+    rx = np.concatenate([np.sort(rng.integers(0, 20, d)) for d in deg]).astype(np.int32)  # many repeats
+    ip, ix = dev_i32(rp), dev_i32(rx)
+    Q, K, V, dO = rand_feats(rng, n, H, D, dtype, k=4)
+    for plan in ("none", "heavy", "mixed"):
+        say("multigraph", plan)
+        pl = _plan(g, ip, ix, plan, want_csc=plan != "none")
+        q, k, v, go = (dev_feat(x, dtype) for x in (Q, K, V, dO))
+        O, L = g.gnn_attn_fwd(pl, ip, ix, q, k, v)
+        ref = oracle.gt_fwd(rp, rx, Q, K, V)
+        _check("O", host(O), ref["O"], ref["SO"], dtype)
+        if pl is not None:
+            dq, dk, dv = g.gnn_attn_bwd(pl, ip, ix, q, k, v, O, go, L)
+            rb = oracle.gt_bwd(rp, rx, Q, K, V, dO)
+            _check("dK", host(dk), rb["dK"], rb["SdK"], dtype)
+            _check("dV", host(dv), rb["dV"], rb["SdV"], dtype)
+    torch.cuda.synchronize()
+
+
+def test_gpu_identities(g):
+    """Properties that hold for any size, checked on GPU outputs."""
+    import torch
+    n, H, D, dtype = 6000, 4, 32, "f32"
+    say("identities")
+    ip, ix, rp, rx = _graph(g, 10, n)
+    rng = np.random.default_rng(10)
+    Q, K, V, dO = rand_feats(rng, n, H, D, dtype, k=4)
+    pl = _plan(g, ip, ix, "mixed", want_csc=True)
+    q, k, v, go = (dev_feat(x, dtype) for x in (Q, K, V, dO))
+    # V constant -> O constant
+    O1, _ = g.gnn_attn_fwd(pl, ip, ix, q, k, torch.full_like(v, 0.75))
+    assert torch.max(torch.abs(O1 - 0.75)).item() < 1e-5
+    O, L = g.gnn_attn_fwd(pl, ip, ix, q, k, v)
+    dq, dk, dv = g.gnn_attn_bwd(pl, ip, ix, q, k, v, O, go, L)
+    # shift invariance: sum of dK over sources vanishes; weights sum to one:
+    # sum of dV over sources equals the sum of dO over destinations
+    sdk = dk.double().sum(0).abs()
+    sdv = (dv.double().sum(0) - go.double().sum(0)).abs()
+    assert torch.all(sdk <= 1e-4 * dk.double().abs().sum(0) + 1e-6)
+    assert torch.all(sdv <= 1e-4 * dv.double().abs().sum(0) + 1e-6)

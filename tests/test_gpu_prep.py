@@ -1,0 +1,90 @@
+"""GPU preprocessor parity: CSR build, degree bucketing and the transposed
+adjacency must equal the oracle's integer definitions bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from _gpu import dev_i32, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import io_aware_sparse_amd as g
+    g.lib()
+    return g
+
+
+def _csr_case(g, src, dst, n, self_loops):
+    say("csr_build", n, src.size, self_loops)
+    ip, ix = g.gnn_csr_build(dev_i32(src), dev_i32(dst), n, add_self_loops=self_loops)
+    rp, rx = oracle.csr_build(src, dst, n, add_self_loops=self_loops)
+    assert np.array_equal(ip.cpu().numpy(), rp)
+    assert np.array_equal(ix.cpu().numpy(), rx)
+    return ip, ix, rp, rx
+
+
+@pytest.mark.parametrize("seed,n,m", [(0, 1, 0), (1, 1, 5), (2, 2, 7), (3, 37, 300), (4, 1000, 20000),
+                                      (5, 5000, 4097), (6, 70000, 300000)])
+@pytest.mark.parametrize("self_loops", [True, False])
+def test_csr_build_random(g, seed, n, m, self_loops):
+    rng = np.random.default_rng(seed)
+    src = rng.integers(0, n, m).astype(np.int32)
+    dst = rng.integers(0, n, m).astype(np.int32)
+    if m > 10:
+        dup = rng.integers(0, m, m // 5)          # explicit duplicates and self-pairs
+        src[dup[: dup.size // 2]] = dst[dup[: dup.size // 2]]
+        src = np.concatenate([src, src[dup]])
+        dst = np.concatenate([dst, dst[dup]])
+    _csr_case(g, src, dst, n, self_loops)
+
+
+@pytest.mark.parametrize("name,n", [("gt_uniform_n2708", None), ("gt_chunglu25_n169k", 20000),
+                                    ("gatv2_zipf21_n100k", 20000), ("gt_comm16_n1m_deg100", 4096)])
+def test_csr_build_workloads(g, name, n):
+    wl = workloads.make(name, n, features=False)
+    _csr_case(g, wl.src, wl.dst, wl.n_nodes, True)
+
+
+def test_csr_build_rejects_bad_endpoint(g):
+    src = np.array([0, 1, 7], np.int32)
+    dst = np.array([1, 2, 0], np.int32)
+    with pytest.raises(g.GnnError) as e:
+        g.gnn_csr_build(dev_i32(src), dev_i32(dst), 5)
+    assert e.value.status == -6
+
+
+@pytest.mark.parametrize("T,C,W", [(0, 1, 1), (0, 5, 4), (3, 2, 2), (16, 8, 2), (64, 64, 8), (512, 512, 4),
+                                   (10 ** 9, 512, 4)])
+def test_buckets_and_csc(g, T, C, W):
+    wl = workloads.make("gatv2_zipf21_n100k", 12000, features=False)
+    n = wl.n_nodes
+    ip, ix, rp, rx = _csr_case(g, wl.src, wl.dst, n, True)
+    say("plan", T, C, W)
+    plan = g.gnn_plan_create(ip, ix, light_threshold=T, chunk=C, waves_per_group=W, want_csc=True)
+    d = g.gnn_plan_export(plan, arrays=True)
+    ref = oracle.bucketing(rp, T, C, W)
+    for k in ("light", "heavy", "groups", "partial_ofs"):
+        assert np.array_equal(d[k], ref[k]), k
+    cip, cix = oracle.csc(rp, rx, n)
+    assert np.array_equal(d["cindptr"], cip) and np.array_equal(d["cindices"], cix)
+    cref = oracle.bucketing(cip, T, C, W)
+    for k in ("light", "heavy", "groups", "partial_ofs"):
+        assert np.array_equal(d["c_" + k], cref[k]), "c_" + k
+    assert d["n_light"] + d["n_heavy"] == n
+
+
+def test_plan_rejects_inconsistent_graph(g):
+    import torch
+    ip = dev_i32(np.array([0, 2, 3], np.int32))
+    ix = dev_i32(np.array([0, 1, 1, 0], np.int32))       # indptr[N] = 3 != E = 4
+    with pytest.raises(g.GnnError) as e:
+        g.gnn_plan_create(ip, ix)
+    assert e.value.status == -6
+    ix = dev_i32(np.array([0, 5, 1], np.int32))          # index out of range
+    with pytest.raises(g.GnnError) as e:
+        g.gnn_plan_create(ip, ix)
+    assert e.value.status == -6
+    torch.cuda.synchronize()
