@@ -74,6 +74,9 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"HIP library missing: {LIB_PATH}; build it with "
                                "`python -m io_aware_sparse_amd.build`")
+        # torch carries its own HIP runtime; load it first so that the library
+        # binds to the same runtime instance (one HIP runtime per process)
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         V, I32, I64, F = C.c_void_p, C.c_int32, C.c_int64, C.c_float
         L.gnn_plan_opts_default.argtypes = [C.POINTER(PlanOpts)]

@@ -36,7 +36,9 @@ int dev_alloc(DevBuf &b, size_t bytes) {
     hipError_t e = hipMalloc(&p, bytes);
     if (e != hipSuccess) {
         (void)hipGetLastError();
-        set_hip_error(e, "hipMalloc");
+        char what[64];
+        snprintf(what, sizeof(what), "hipMalloc(%zu bytes)", bytes);
+        set_hip_error(e, what);
         return GNN_ERR_OOM;
     }
     b.p = p;
@@ -500,7 +502,7 @@ const char *gnn_status_string(int status) {
         case GNN_ERR_INVALID_ARG: return "invalid argument";
         case GNN_ERR_UNSUPPORTED: return "unsupported configuration";
         case GNN_ERR_ALIGNMENT: return "feature pointer not 16-byte aligned";
-        case GNN_ERR_OOM: return "device allocation failed";
+        case GNN_ERR_OOM: return g_hip_msg[0] ? g_hip_msg : "device allocation failed";
         case GNN_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP runtime error";
         case GNN_ERR_BAD_GRAPH: return "graph arrays inconsistent or out of range";
         default: return "unknown status";

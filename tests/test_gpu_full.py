@@ -1,0 +1,117 @@
+"""Full-size parity at the benchmark's launch configuration (default plan:
+T = 512, C = 512, W = 4) on every workload.
+
+The CSR, buckets and transposed adjacency are compared bit for bit over the
+whole graph. Outputs are compared on sampled rows the oracle computes one by
+one: every heavy row (heavy sources for dK/dV) plus seeded uniform samples
+of light rows; the small workloads are compared in full. Properties that
+hold at any size are checked on the full GPU outputs."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from _gpu import TOL, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+FULL = ["gt_uniform_n2708", "gt_chunglu25_n169k", "gatv2_zipf21_n100k", "gt_chunglu22_n2450k",
+        "gt_comm16_n1m_deg100", "gt_comm16_n1m_deg27"]
+N_SAMPLE = 20000
+
+
+@pytest.fixture(scope="module")
+def g():
+    import io_aware_sparse_amd as g
+    g.lib()
+    return g
+
+
+def _dev(wl, nm):
+    import torch
+    if wl.dtype == "bf16":
+        return torch.from_numpy(wl.bits[nm].view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(wl.feats[nm]).cuda()
+
+
+def _host(t):
+    import torch
+    return t.float().cpu().numpy().astype(np.float64) if t.dtype == torch.bfloat16 else t.cpu().numpy().astype(np.float64)
+
+
+def _sample(rng, n, heavy, k):
+    if n <= k + heavy.size:
+        return np.arange(n)
+    return np.unique(np.concatenate([heavy.astype(np.int64), rng.choice(n, k, replace=False)]))
+
+
+def _check(name, x, ref, scale, dtype):
+    err = oracle.scaled_error(x, ref, scale)
+    say(f"  {name}: scaled err {err:.3e} over {np.asarray(ref).shape[0]} rows (tol {TOL[dtype]:.0e})")
+    assert err <= TOL[dtype], (name, err)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size(g, name):
+    import torch
+    say("full-size", name)
+    wl = workloads.make(name)
+    n, H, D = wl.n_nodes, wl.heads, wl.dim
+    ip, ix = g.gnn_csr_build(torch.from_numpy(wl.src).cuda(), torch.from_numpy(wl.dst).cuda(), n)
+    rp, rx = oracle.csr_build(wl.src, wl.dst, n)
+    assert np.array_equal(ip.cpu().numpy(), rp), "indptr"
+    assert np.array_equal(ix.cpu().numpy(), rx), "indices"
+    say("  CSR bit-exact, E =", rx.size)
+    plan = g.gnn_plan_create(ip, ix, want_csc=wl.backward)
+    d = g.gnn_plan_export(plan, arrays=True)
+    ref_b = oracle.bucketing(rp, 512, 512, 4)
+    for k in ("light", "heavy", "groups", "partial_ofs"):
+        assert np.array_equal(d[k], ref_b[k]), k
+    if wl.backward:
+        cip, cix = oracle.csc(rp, rx, n)
+        assert np.array_equal(d["cindptr"], cip) and np.array_equal(d["cindices"], cix), "csc"
+        ref_c = oracle.bucketing(cip, 512, 512, 4)
+        for k in ("light", "heavy", "groups", "partial_ofs"):
+            assert np.array_equal(d["c_" + k], ref_c[k]), "c_" + k
+    say(f"  buckets bit-exact: light {d['n_light']} heavy {d['n_heavy']} groups {d['n_groups']}")
+    rng = np.random.default_rng(77)
+    rows = _sample(rng, n, ref_b["heavy"], N_SAMPLE)
+    if wl.kind == "gatv2":
+        xd, xs = _dev(wl, "XD"), _dev(wl, "XS")
+        att = torch.from_numpy(wl.att).cuda()
+        O, L = g.gatv2_attn_fwd(plan, ip, ix, xd, xs, att, negative_slope=0.2)
+        torch.cuda.synchronize()
+        ref = oracle.gatv2_fwd(rp, rx, wl.feats["XD"], wl.feats["XS"], wl.att, slope=0.2, rows=rows)
+        _check("O", _host(O)[rows], ref["O"], ref["SO"], wl.dtype)
+        _check("LSE", _host(L)[rows], ref["LSE"], ref["SL"], "f32")
+        return
+    q, k, v = _dev(wl, "Q"), _dev(wl, "K"), _dev(wl, "V")
+    O, L = g.gnn_attn_fwd(plan, ip, ix, q, k, v)
+    torch.cuda.synchronize()
+    Q = np.asarray(wl.feats["Q"], np.float64)
+    K = np.asarray(wl.feats["K"], np.float64)
+    V = np.asarray(wl.feats["V"], np.float64)
+    ref = oracle.gt_fwd(rp, rx, Q, K, V, rows=rows)
+    _check("O", _host(O)[rows], ref["O"], ref["SO"], wl.dtype)
+    _check("LSE", _host(L)[rows], ref["LSE"], ref["SL"], "f32")
+    # weights sum to one at any size
+    Oc, _ = g.gnn_attn_fwd(plan, ip, ix, q, k, torch.full_like(v, 0.5), want_lse=False)
+    assert torch.max(torch.abs(Oc.float() - 0.5)).item() <= (1e-5 if wl.dtype == "f32" else 4e-3)
+    del Oc
+    if not wl.backward:
+        return
+    go = _dev(wl, "dO")
+    dq, dk, dv = g.gnn_attn_bwd(plan, ip, ix, q, k, v, O, go, L)
+    torch.cuda.synchronize()
+    srcs = _sample(rng, n, d["c_heavy"], N_SAMPLE // 4)
+    dO = np.asarray(wl.feats["dO"], np.float64)
+    rb = oracle.gt_bwd(rp, rx, Q, K, V, dO, rows=rows, srcs=srcs, csc_arrays=(cip, cix))
+    _check("dQ", _host(dq)[rows], rb["dQ"], rb["SdQ"], wl.dtype)
+    _check("dK", _host(dk)[srcs], rb["dK"], rb["SdK"], wl.dtype)
+    _check("dV", _host(dv)[srcs], rb["dV"], rb["SdV"], wl.dtype)
+    # gradient identities on the full GPU outputs
+    sdk = dk.double().sum(0).abs()
+    sdv = (dv.double().sum(0) - go.double().sum(0)).abs()
+    say(f"  |sum dK| max {sdk.max().item():.3e}, |sum dV - sum dO| max {sdv.max().item():.3e}")
+    assert torch.all(sdk <= 2e-2 * dk.double().abs().sum(0) + 1e-3)
+    assert torch.all(sdv <= 2e-2 * dv.double().abs().sum(0) + 1e-3)

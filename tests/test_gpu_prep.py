@@ -88,3 +88,17 @@ def test_plan_rejects_inconsistent_graph(g):
         g.gnn_plan_create(ip, ix)
     assert e.value.status == -6
     torch.cuda.synchronize()
+
+
+def test_library_loaded_before_torch_in_fresh_process():
+    """Loading the library before anything else imported torch must still
+    leave one HIP runtime in the process (regression: allocations failed)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import io_aware_sparse_amd as g; g.lib(); import torch; "
+            "s = torch.arange(10, dtype=torch.int32).cuda(); d = torch.roll(s, 1).contiguous(); "
+            "ip, ix = g.gnn_csr_build(s, d, 10); assert ip.cpu().tolist()[-1] == 20; print('ok')")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
