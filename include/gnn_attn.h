@@ -115,7 +115,13 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
                     const gnn_plan_opts *opts /*host, nullable*/, hipStream_t stream,
                     gnn_plan_t *plan_out /*host*/);
 
-/* Counts and device pointers of a plan's arrays (read-only views, owned by the plan). */
+/* Counts and device pointers of a plan's arrays (read-only views, owned by the plan).
+ * Tiles follow the 16x16 block-sparse tiles of the attention layers (technical
+ * summary, Methodology): a (row block, column block) pair of aligned 16-node
+ * blocks becomes a tile when it holds >= tile_min_nnz distinct positions and
+ * neither block contains a node of degree > T (in-degree for rows, out-degree
+ * for sources); the first copy of each position in a tile is covered by the
+ * tile's mask and every other edge stays in the residual CSR. */
 typedef struct {
     int32_t n_nodes;
     int64_t n_edges;
@@ -140,6 +146,15 @@ typedef struct {
     const int32_t *rindptr;     /* [N+1] residual CSR (edges outside tiles)             */
     const int32_t *rindices;    /* [n_residual]                                         */
     int64_t n_residual;
+    int32_t n_trb, n_light_nt, n_tcb, n_c_light_nt;
+    const int32_t *trb;         /* [n_trb] row blocks holding tiles, ascending           */
+    const int32_t *light_nt;    /* [n_light_nt] light nodes outside tiled row blocks     */
+    const int32_t *ctile;       /* [n_tiles] tile ids ordered by (col block, row block)  */
+    const int32_t *ctile_ptr;   /* [ceil(N/16)+1] range of each column block in ctile   */
+    const int32_t *tcb;         /* [n_tcb] column blocks holding tiles (want_csc)        */
+    const int32_t *rcindptr;    /* [N+1] transposed residual (want_csc)                  */
+    const int32_t *rcindices;   /* [n_residual]                                          */
+    const int32_t *c_light_nt;  /* [n_c_light_nt] light sources outside tiled column blocks */
     /* device memory owned by the plan */
     int64_t structure_bytes;    /* buckets, transposed adjacency, tiles                 */
     int64_t workspace_bytes;    /* heavy partials and backward statistics (grows lazily) */

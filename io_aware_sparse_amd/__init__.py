@@ -60,6 +60,10 @@ class PlanInfo(C.Structure):
                 ("has_tiles", C.c_int32), ("n_tiles", C.c_int32), ("tile_min_nnz", C.c_int32),
                 ("tile_rc", C.c_void_p), ("tile_mask", C.c_void_p), ("tile_ptr", C.c_void_p),
                 ("rindptr", C.c_void_p), ("rindices", C.c_void_p), ("n_residual", C.c_int64),
+                ("n_trb", C.c_int32), ("n_light_nt", C.c_int32), ("n_tcb", C.c_int32), ("n_c_light_nt", C.c_int32),
+                ("trb", C.c_void_p), ("light_nt", C.c_void_p), ("ctile", C.c_void_p), ("ctile_ptr", C.c_void_p),
+                ("tcb", C.c_void_p), ("rcindptr", C.c_void_p), ("rcindices", C.c_void_p),
+                ("c_light_nt", C.c_void_p),
                 ("structure_bytes", C.c_int64), ("workspace_bytes", C.c_int64),
                 ("largest_workspace_alloc", C.c_int64)]
 
@@ -254,6 +258,15 @@ def gnn_plan_export(plan: Plan, arrays: bool = False) -> dict:
             d["tile_ptr"] = _copy_dev(info.tile_ptr, (n + 15) // 16 + 1, np.int32)
             d["rindptr"] = _copy_dev(info.rindptr, n + 1, np.int32)
             d["rindices"] = _copy_dev(info.rindices, info.n_residual, np.int32)
+            d["trb"] = _copy_dev(info.trb, info.n_trb, np.int32)
+            d["light_nt"] = _copy_dev(info.light_nt, info.n_light_nt, np.int32)
+            d["ctile"] = _copy_dev(info.ctile, info.n_tiles, np.int32)
+            d["ctile_ptr"] = _copy_dev(info.ctile_ptr, (n + 15) // 16 + 1, np.int32)
+            if info.has_csc:
+                d["tcb"] = _copy_dev(info.tcb, info.n_tcb, np.int32)
+                d["rcindptr"] = _copy_dev(info.rcindptr, n + 1, np.int32)
+                d["rcindices"] = _copy_dev(info.rcindices, info.n_residual, np.int32)
+                d["c_light_nt"] = _copy_dev(info.c_light_nt, info.n_c_light_nt, np.int32)
     return d
 
 

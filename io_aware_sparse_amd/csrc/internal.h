@@ -89,11 +89,15 @@ struct gnn_plan_s {
     bool has_csc = false;
     gnn::DevBuf cindptr, cindices;
     gnn::Buckets bwd;          // out-degree buckets over the transposed adjacency
-    // tiles
+    // 16x16 tiles: tile list by (row block, col block), residual CSR, the
+    // light rows outside tiled row blocks; for the backward also the tiles
+    // ordered by column block, the transposed residual and the light sources
+    // outside tiled column blocks
     bool has_tiles = false;
-    int32_t n_tiles = 0, tile_min_nnz = 0;
+    int32_t n_tiles = 0, tile_min_nnz = 0, n_trb = 0, n_light_nt = 0, n_tcb = 0, n_c_light_nt = 0;
     int64_t n_residual = 0;
-    gnn::DevBuf tile_rc, tile_mask, tile_ptr, rindptr, rindices;
+    gnn::DevBuf tile_rc, tile_mask, tile_ptr, trb, rindptr, rindices, light_nt;
+    gnn::DevBuf ctile, ctile_ptr, tcb, rcindptr, rcindices, c_light_nt;
     // workspace (heavy partials, backward statistics), grows on demand
     gnn::DevBuf ws;
     int64_t largest_ws = 0;
@@ -105,11 +109,27 @@ namespace gnn {
 // plan workspace of at least `bytes` (kept, grown on demand)
 int plan_workspace(gnn_plan_s *p, size_t bytes, hipStream_t s, void **out);
 
-// device-wide exclusive scan of int32 (in may equal out); returns the total in *total_dev (int32 device scalar)
-int scan_exclusive(const int32_t *in, int32_t *out, int64_t n, int32_t *total_dev, hipStream_t s);
-// LSD radix sort of 64-bit keys on bits [0, bits); result in keys (tmp: same size scratch)
-int radix_sort_u64(uint64_t *keys, uint64_t *tmp, int64_t n, int bits, hipStream_t s);
+int64_t cdiv(int64_t a, int64_t b);
+dim3 grid1d(int64_t n, int t = 256);
+int bits_for(int64_t n);
+// int32 scratch elements needed by scan_rec / radix_sort on n elements
+int64_t scan_scratch(int64_t n);
+int64_t sort_scratch(int64_t n);
+// device-wide exclusive scan of int32 (in may equal out); *total_dev receives the sum
+int scan_rec(const int32_t *in, int32_t *out, int64_t n, int32_t *total_dev, int32_t *scratch, hipStream_t s);
+// stable LSD radix sort of 64-bit keys on bits [0, bits) (tmp: same-size scratch);
+// an optional int32 payload moves with its key
+int radix_sort(uint64_t *keys, uint64_t *tmp, int64_t n, int bits, int32_t *scratch, hipStream_t s,
+               int32_t *vals = nullptr, int32_t *vtmp = nullptr);
+// sorted (row << nb | col) keys -> rowptr [n_rows+1] / col [<= cap]; dedupe drops repeated keys
+int emit_structure(uint64_t *keys, int64_t n, int nb, int dedupe, int32_t n_rows, int32_t *rowptr, int32_t *col,
+                   int64_t cap, int32_t *flags, int32_t *pos, int32_t *total_dev, int32_t *scratch, hipStream_t s);
+// transpose a CSR (indptr/indices over n rows) into cindptr/cindices
+int build_transpose(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, DevBuf &cindptr,
+                    DevBuf &cindices, hipStream_t s);
 // bucket a CSR-like structure
 int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_t W, Buckets &b,
                   hipStream_t s);
+// 16x16 tile census of the plan's graph (fills the plan's tile arrays)
+int build_tiles(gnn_plan_s *p, int32_t min_nnz, hipStream_t s);
 }  // namespace gnn

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -172,10 +173,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const int32_t *in, 
 
 __global__ void k_set_i32(int32_t *p, int32_t v) { *p = v; }
 
-static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // int32 elements of scratch that scan_exclusive(n) needs
-static int64_t scan_scratch(int64_t n) {
+int64_t scan_scratch(int64_t n) {
     int64_t tot = 0;
     while (n > kScanTile) {
         n = cdiv(n, kScanTile);
@@ -184,8 +185,8 @@ static int64_t scan_scratch(int64_t n) {
     return tot + 1;
 }
 
-static int scan_rec(const int32_t *in, int32_t *out, int64_t n, int32_t *total_dev, int32_t *scratch,
-                    hipStream_t s) {
+int scan_rec(const int32_t *in, int32_t *out, int64_t n, int32_t *total_dev, int32_t *scratch,
+             hipStream_t s) {
     if (n <= 0) {
         if (total_dev) hipLaunchKernelGGL(k_set_i32, dim3(1), dim3(1), 0, s, total_dev, 0);
         return GNN_OK;
@@ -228,7 +229,8 @@ __global__ __launch_bounds__(kSortThreads) void k_rs_hist(const uint64_t *keys, 
 // Stable scatter: element order inside a tile is (sub-tile, thread), and the
 // ranking below preserves it, so equal digits keep their input order.
 __global__ __launch_bounds__(kSortThreads) void k_rs_scatter(const uint64_t *in, uint64_t *out, int64_t n,
-                                                              int shift, const int32_t *ofs, int nblocks) {
+                                                              int shift, const int32_t *ofs, int nblocks,
+                                                              const int32_t *vin, int32_t *vout) {
     constexpr int NW = kSortThreads / kWave;
     __shared__ int base[256];
     __shared__ int wcnt[NW][256];
@@ -262,19 +264,26 @@ __global__ __launch_bounds__(kSortThreads) void k_rs_scatter(const uint64_t *in,
             run += c;
         }
         __syncthreads();
-        if (valid) out[base[d] + wcnt[w][d] + rank] = key;
+        if (valid) {
+            const int64_t dst = base[d] + wcnt[w][d] + rank;
+            out[dst] = key;
+            if (vin) vout[dst] = vin[i];
+        }
         __syncthreads();
         base[t] += run;
         __syncthreads();
     }
 }
 
-static int64_t sort_scratch(int64_t n) {
+int64_t sort_scratch(int64_t n) {
     const int64_t nb = std::max<int64_t>(1, cdiv(n, kSortTile));
     return 256 * nb + scan_scratch(256 * nb) + 1;
 }
 
-static int radix_sort(uint64_t *keys, uint64_t *tmp, int64_t n, int bits, int32_t *scratch, hipStream_t s) {
+// Stable LSD radix sort of keys on bits [0, bits); optional int32 payload
+// (vals, with vtmp as its scratch twin) moves with its key.
+int radix_sort(uint64_t *keys, uint64_t *tmp, int64_t n, int bits, int32_t *scratch, hipStream_t s,
+               int32_t *vals, int32_t *vtmp) {
     if (n <= 1 || bits <= 0) return GNN_OK;
     const int64_t nb = cdiv(n, kSortTile);
     if (nb > 0x7FFFFFFF / 256) return GNN_ERR_INVALID_ARG;
@@ -282,22 +291,27 @@ static int radix_sort(uint64_t *keys, uint64_t *tmp, int64_t n, int bits, int32_
     int32_t *tot = scratch + 256 * nb;
     int32_t *sc = tot + 1;
     uint64_t *a = keys, *b = tmp;
+    int32_t *va = vals, *vb = vtmp;
     const int passes = (bits + 7) / 8;
     for (int p = 0; p < passes; ++p) {
         hipLaunchKernelGGL(k_rs_hist, dim3((unsigned)nb), dim3(kSortThreads), 0, s, a, n, 8 * p, hist, (int)nb);
         GNN_TRY(scan_rec(hist, hist, 256 * nb, tot, sc, s));
         hipLaunchKernelGGL(k_rs_scatter, dim3((unsigned)nb), dim3(kSortThreads), 0, s, a, b, n, 8 * p,
-                           (const int32_t *)hist, (int)nb);
+                           (const int32_t *)hist, (int)nb, (const int32_t *)va, vb);
         std::swap(a, b);
+        std::swap(va, vb);
     }
-    if (a != keys) GNN_HIP(hipMemcpyAsync(keys, a, (size_t)n * 8, hipMemcpyDeviceToDevice, s));
+    if (a != keys) {
+        GNN_HIP(hipMemcpyAsync(keys, a, (size_t)n * 8, hipMemcpyDeviceToDevice, s));
+        if (vals) GNN_HIP(hipMemcpyAsync(vals, va, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+    }
     GNN_HIP(hipGetLastError());
     return GNN_OK;
 }
 
 // ---------------------------------------------------------------- CSR / CSC
 
-static int bits_for(int64_t n) {
+int bits_for(int64_t n) {
     int b = 1;
     while (b < 31 && (1ll << b) < n) ++b;
     return b;
@@ -348,10 +362,10 @@ __global__ void k_fill_i32(int32_t *p, int64_t n, int32_t v) {
     if (i < n) p[i] = v;
 }
 
-static dim3 grid1d(int64_t n, int t = 256) { return dim3((unsigned)std::max<int64_t>(1, cdiv(n, t))); }
+dim3 grid1d(int64_t n, int t) { return dim3((unsigned)std::max<int64_t>(1, cdiv(n, t))); }
 
 // keys must hold the sorted (row << nb | col) keys; writes rowptr [n_rows+1], col [<= cap]
-static int emit_structure(uint64_t *keys, int64_t n, int nb, int dedupe, int32_t n_rows, int32_t *rowptr,
+int emit_structure(uint64_t *keys, int64_t n, int nb, int dedupe, int32_t n_rows, int32_t *rowptr,
                           int32_t *col, int64_t cap, int32_t *flags, int32_t *pos, int32_t *total_dev,
                           int32_t *scratch, hipStream_t s) {
     if (n == 0) {
@@ -464,6 +478,34 @@ __global__ void k_validate(const int32_t *indptr, const int32_t *indices, int32_
     }
 }
 
+int build_transpose(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t m, DevBuf &cindptr,
+                    DevBuf &cindices, hipStream_t s) {
+    const int nb = bits_for(std::max<int64_t>(2, n));
+    const int64_t ss = std::max(sort_scratch(m), scan_scratch(m)) + 2;
+    DevBuf tmp;
+    int rc = dev_alloc(tmp, (size_t)(24 * std::max<int64_t>(m, 1) + 4 * ss + 64));
+    if (rc == GNN_OK) rc = dev_alloc(cindptr, (size_t)(n + 1) * 4);
+    if (rc == GNN_OK) rc = dev_alloc(cindices, (size_t)std::max<int64_t>(m, 1) * 4);
+    if (rc == GNN_OK) {
+        uint64_t *keys = as<uint64_t>(tmp), *kt = keys + std::max<int64_t>(m, 1);
+        int32_t *flags = reinterpret_cast<int32_t *>(kt + std::max<int64_t>(m, 1));
+        int32_t *pos = flags + std::max<int64_t>(m, 1), *total = pos + std::max<int64_t>(m, 1), *scr = total + 1;
+        if (n > 0)
+            hipLaunchKernelGGL(k_transpose_keys, dim3((unsigned)cdiv(n, 4)), dim3(256), 0, s, indptr, indices, n, nb,
+                               keys);
+        rc = radix_sort(keys, kt, m, 2 * nb, scr, s);
+        if (rc == GNN_OK)
+            rc = emit_structure(keys, m, nb, 0, n, as<int32_t>(cindptr), as<int32_t>(cindices), m, flags, pos, total,
+                                scr, s);
+        if (rc == GNN_OK && hipStreamSynchronize(s) != hipSuccess) {
+            set_hip_error(hipGetLastError(), "transpose");
+            rc = GNN_ERR_HIP;
+        }
+    }
+    dev_free(tmp);
+    return rc;
+}
+
 }  // namespace gnn
 
 using namespace gnn;
@@ -472,7 +514,8 @@ int64_t gnn_plan_s::structure_bytes() const {
     int64_t t = 0;
     for (const DevBuf *b : {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &cindptr, &cindices,
                             &bwd.light, &bwd.heavy, &bwd.groups, &bwd.partial_ofs, &tile_rc, &tile_mask,
-                            &tile_ptr, &rindptr, &rindices})
+                            &tile_ptr, &trb, &rindptr, &rindices, &light_nt, &ctile, &ctile_ptr, &tcb,
+                            &rcindptr, &rcindices, &c_light_nt})
         t += (int64_t)b->bytes;
     return t;
 }
@@ -606,36 +649,17 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
     if (rc == GNN_OK)
         rc = build_buckets(indptr, n_nodes, o.light_threshold, o.chunk, o.waves_per_group, p->fwd, stream);
     if (rc == GNN_OK && o.want_csc) {
-        const int nb = bits_for(std::max<int64_t>(2, n_nodes));
-        const int64_t m = n_edges;
-        const int64_t ss = std::max(sort_scratch(m), scan_scratch(m)) + 2;
-        rc = dev_alloc(tmp, (size_t)(24 * std::max<int64_t>(m, 1) + 4 * ss + 64));
-        if (rc == GNN_OK) rc = dev_alloc(p->cindptr, (size_t)(n_nodes + 1) * 4);
-        if (rc == GNN_OK) rc = dev_alloc(p->cindices, (size_t)std::max<int64_t>(m, 1) * 4);
-        if (rc == GNN_OK) {
-            uint64_t *keys = as<uint64_t>(tmp), *kt = keys + std::max<int64_t>(m, 1);
-            int32_t *flags = reinterpret_cast<int32_t *>(kt + std::max<int64_t>(m, 1));
-            int32_t *pos = flags + std::max<int64_t>(m, 1), *total = pos + std::max<int64_t>(m, 1), *scr = total + 1;
-            if (n_nodes > 0)
-                hipLaunchKernelGGL(k_transpose_keys, dim3((unsigned)cdiv(n_nodes, 4)), dim3(256), 0, stream, indptr,
-                                   indices, n_nodes, nb, keys);
-            rc = radix_sort(keys, kt, m, 2 * nb, scr, stream);
-            if (rc == GNN_OK)
-                rc = emit_structure(keys, m, nb, 0, n_nodes, as<int32_t>(p->cindptr), as<int32_t>(p->cindices), m,
-                                    flags, pos, total, scr, stream);
-            if (rc == GNN_OK && hipStreamSynchronize(stream) != hipSuccess) {
-                set_hip_error(hipGetLastError(), "transpose");
-                rc = GNN_ERR_HIP;
-            }
-        }
-        dev_free(tmp);
+        rc = build_transpose(indptr, indices, n_nodes, n_edges, p->cindptr, p->cindices, stream);
         if (rc == GNN_OK) {
             p->has_csc = true;
             rc = build_buckets(as<int32_t>(p->cindptr), n_nodes, o.light_threshold, o.chunk, o.waves_per_group,
                                p->bwd, stream);
         }
     }
-    if (rc == GNN_OK && o.tile_density > 0.0f) rc = GNN_ERR_UNSUPPORTED;   // tile census: see tiles.hip
+    if (rc == GNN_OK && o.tile_density > 0.0f) {
+        const int32_t min_nnz = std::max(1, (int32_t)std::ceil((double)o.tile_density * 256.0 - 1e-9));
+        rc = build_tiles(p, min_nnz, stream);
+    }
     if (rc != GNN_OK) {
         gnn_plan_destroy(p);
         return rc;
@@ -678,6 +702,18 @@ int gnn_plan_export(gnn_plan_t p, gnn_plan_info *info) {
     info->rindptr = as<int32_t>(p->rindptr);
     info->rindices = as<int32_t>(p->rindices);
     info->n_residual = p->n_residual;
+    info->n_trb = p->n_trb;
+    info->trb = as<int32_t>(p->trb);
+    info->n_light_nt = p->n_light_nt;
+    info->light_nt = as<int32_t>(p->light_nt);
+    info->ctile = as<int32_t>(p->ctile);
+    info->ctile_ptr = as<int32_t>(p->ctile_ptr);
+    info->n_tcb = p->n_tcb;
+    info->tcb = as<int32_t>(p->tcb);
+    info->rcindptr = as<int32_t>(p->rcindptr);
+    info->rcindices = as<int32_t>(p->rcindices);
+    info->n_c_light_nt = p->n_c_light_nt;
+    info->c_light_nt = as<int32_t>(p->c_light_nt);
     info->structure_bytes = p->structure_bytes();
     info->workspace_bytes = (int64_t)p->ws.bytes;
     info->largest_workspace_alloc = p->largest_ws;
@@ -688,7 +724,8 @@ int gnn_plan_destroy(gnn_plan_t p) {
     if (!p) return GNN_ERR_INVALID_ARG;
     for (DevBuf *b : {&p->fwd.light, &p->fwd.heavy, &p->fwd.groups, &p->fwd.partial_ofs, &p->cindptr, &p->cindices,
                       &p->bwd.light, &p->bwd.heavy, &p->bwd.groups, &p->bwd.partial_ofs, &p->tile_rc, &p->tile_mask,
-                      &p->tile_ptr, &p->rindptr, &p->rindices, &p->ws})
+                      &p->tile_ptr, &p->trb, &p->rindptr, &p->rindices, &p->light_nt, &p->ctile, &p->ctile_ptr,
+                      &p->tcb, &p->rcindptr, &p->rcindices, &p->c_light_nt, &p->ws})
         dev_free(*b);
     delete p;
     return GNN_OK;

@@ -152,43 +152,74 @@ def csc(indptr, indices, n_nodes: int):
     return cindptr.astype(np.int32), cindices
 
 
-def tile_census(indptr, indices, n_nodes: int, min_nnz: int):
-    """16x16 dense-tile census.
+def tile_census(indptr, indices, n_nodes: int, min_nnz: int, threshold: int):
+    """16x16 dense-tile census (the pages' block-sparse 16x16 tiles for
+    locally dense neighbourhoods).
 
-    Node ids are grouped into aligned blocks of 16. Every (destination block,
-    source block) pair holding at least min_nnz edges becomes a tile with a
-    256-bit presence mask: bit (dst % 16) * 16 + (src % 16), stored as four
-    uint64 words, word w holding bits 64w..64w+63 (bit b of the word is
-    position 64w + b). Tiles are listed by (row block, col block) ascending.
-    Every edge not inside a tile goes to the residual CSR, in CSR order.
+    Node ids are grouped into aligned blocks of 16. A block pair (destination
+    row block b, source column block c) is eligible when no node of row block
+    b has in-degree > threshold and no node of column block c has out-degree
+    > threshold (heavy rows and sources keep the chunked CSR path). An
+    eligible pair holding at least min_nnz distinct (dst, src) positions
+    becomes a tile with a 256-bit presence mask: bit (dst % 16) * 16 +
+    (src % 16), stored as four uint64 words (word w holds bits 64w..64w+63).
+    Tiles are listed by (b, c) ascending. The first occurrence (CSR order) of
+    each position inside a tile is represented by the tile; every other edge
+    (including repeated copies) stays in the residual CSR, in CSR order.
 
-    Returns dict: tile_rc int32 [n_tiles, 2], tile_mask uint64 [n_tiles, 4],
-    tile_ptr int32 [n_rowblk+1] (tiles of each row block), rindptr int32 [N+1],
-    rindices int32 [E_res]."""
+    Returns dict with
+      tile_rc [T,2] int32, tile_mask [T,4] uint64, tile_ptr [NB+1] int32,
+      trb: row blocks with tiles, rindptr/rindices: residual CSR,
+      light_nt: nodes of in-degree <= threshold in row blocks without tiles,
+      ctile [T] int32: tile ids ordered by (c, b), ctile_ptr [NB+1] int32,
+      tcb: column blocks with tiles, rcindptr/rcindices: transposed residual,
+      c_light_nt: nodes of out-degree <= threshold in column blocks without tiles."""
     n = int(n_nodes)
+    nb = (n + 15) // 16
     ip = np.asarray(indptr, np.int64)
     src = np.asarray(indices, np.int64)
-    dst = np.repeat(np.arange(n, dtype=np.int64), np.diff(ip))
-    nb = (n + 15) // 16
-    pair = (dst // 16) * nb + (src // 16)
-    upair, cnt = np.unique(pair, return_counts=True)
-    tiles = upair[cnt >= min_nnz]
-    in_tile = np.isin(pair, tiles)
+    deg = np.diff(ip)
+    dst = np.repeat(np.arange(n, dtype=np.int64), deg)
+    odeg = np.bincount(src, minlength=n)
+    blk = np.arange(n) // 16
+    rb_ok = np.bincount(blk, weights=(deg > threshold), minlength=nb) == 0
+    cb_ok = np.bincount(blk, weights=(odeg > threshold), minlength=nb) == 0
+    pair = (dst // 16) * nb + src // 16
+    elig = rb_ok[dst // 16] & cb_ok[src // 16]
+    first = np.zeros(src.size, bool)
+    if src.size:
+        first[np.unique(dst * n + src, return_index=True)[1]] = True
+    cand = first & elig
+    up, uc = np.unique(pair[cand], return_counts=True)
+    tiles = up[uc >= min_nnz]
+    in_tile = cand & np.isin(pair, tiles)
     mask = np.zeros((tiles.size, 4), np.uint64)
     if tiles.size:
         t = np.searchsorted(tiles, pair[in_tile])
         bit = (dst[in_tile] % 16) * 16 + (src[in_tile] % 16)
-        word = bit // 64
         val = np.left_shift(np.uint64(1), (bit % 64).astype(np.uint64))
-        np.bitwise_or.at(mask, (t, word), val)
-    rc = np.stack([tiles // nb, tiles % nb], axis=1) if tiles.size else np.zeros((0, 2), np.int64)
+        np.bitwise_or.at(mask, (t, bit // 64), val)
+    trow, tcol = tiles // nb, tiles % nb
     tile_ptr = np.zeros(nb + 1, np.int64)
-    np.cumsum(np.bincount(rc[:, 0], minlength=nb), out=tile_ptr[1:])
+    np.cumsum(np.bincount(trow, minlength=nb), out=tile_ptr[1:])
     keep = ~in_tile
     rindptr = np.zeros(n + 1, np.int64)
     np.cumsum(np.bincount(dst[keep], minlength=n), out=rindptr[1:])
-    return dict(tile_rc=rc.astype(np.int32), tile_mask=mask, tile_ptr=tile_ptr.astype(np.int32),
-                rindptr=rindptr.astype(np.int32), rindices=src[keep].astype(np.int32))
+    rindices = src[keep]
+    rb_has = np.diff(tile_ptr) > 0
+    light_nt = np.nonzero((deg <= threshold) & ~rb_has[blk])[0]
+    ctile = np.lexsort((trow, tcol)) if tiles.size else np.zeros(0, np.int64)
+    ctile_ptr = np.zeros(nb + 1, np.int64)
+    np.cumsum(np.bincount(tcol, minlength=nb), out=ctile_ptr[1:])
+    cb_has = np.diff(ctile_ptr) > 0
+    rcindptr, rcindices = csc(rindptr, rindices, n)
+    c_light_nt = np.nonzero((odeg <= threshold) & ~cb_has[blk])[0]
+    i32 = lambda a: np.asarray(a).astype(np.int32)
+    return dict(tile_rc=i32(np.stack([trow, tcol], axis=1).reshape(-1, 2)), tile_mask=mask,
+                tile_ptr=i32(tile_ptr), trb=i32(np.nonzero(rb_has)[0]), rindptr=i32(rindptr),
+                rindices=i32(rindices), light_nt=i32(light_nt), ctile=i32(ctile), ctile_ptr=i32(ctile_ptr),
+                tcb=i32(np.nonzero(cb_has)[0]), rcindptr=rcindptr, rcindices=rcindices,
+                c_light_nt=i32(c_light_nt))
 
 
 # ---------------------------------------------------------------------------

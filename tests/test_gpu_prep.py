@@ -102,3 +102,40 @@ def test_library_loaded_before_torch_in_fresh_process():
             "ip, ix = g.gnn_csr_build(s, d, 10); assert ip.cpu().tolist()[-1] == 20; print('ok')")
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
+def _tile_graphs():
+    rng = np.random.default_rng(300)
+    out = []
+    for name in ("gt_comm16_n1m_deg100", "gt_comm16_n1m_deg27"):
+        wl = workloads.make(name, 4096, features=False)
+        out.append((name, wl.src, wl.dst, wl.n_nodes))
+    n = 1000                                   # dense blocks of varying fill + hubs + ragged last block
+    a = rng.random((n, n)) < 0.01
+    for b0 in range(0, n - 15, 16):
+        if rng.random() < 0.6:
+            a[b0:b0 + 16, b0:b0 + 16] |= rng.random((16, 16)) < rng.uniform(0.5, 1.0)
+    a[:, 7] = True                             # a source of out-degree n
+    a[333, :] = True                           # a row of in-degree n
+    dst, src = np.nonzero(a)
+    out.append(("blocks+hubs", src.astype(np.int32), dst.astype(np.int32), n))
+    return out
+
+
+@pytest.mark.parametrize("case", range(3))
+@pytest.mark.parametrize("tau,T", [(0.75, 512), (0.5, 40), (1.0, 10 ** 6), (0.1, 512)])
+def test_tile_census(g, case, tau, T):
+    name, src, dst, n = _tile_graphs()[case]
+    ip, ix, rp, rx = _csr_case(g, src, dst, n, True)
+    say("tiles", name, tau, T)
+    plan = g.gnn_plan_create(ip, ix, light_threshold=T, chunk=64, waves_per_group=4, tile_density=tau, want_csc=True)
+    d = g.gnn_plan_export(plan, arrays=True)
+    import math
+    ref = oracle.tile_census(rp, rx, n, max(1, math.ceil(tau * 256 - 1e-9)), T)
+    assert d["n_tiles"] == ref["tile_rc"].shape[0]
+    for k in ("tile_rc", "tile_mask", "tile_ptr", "trb", "rindptr", "rindices", "light_nt", "ctile", "tcb",
+              "rcindptr", "rcindices", "c_light_nt"):
+        assert np.array_equal(d[k], np.asarray(ref[k]).reshape(d[k].shape)), k
+    n_pop = int(sum(bin(int(w)).count("1") for w in d["tile_mask"].ravel()))
+    assert n_pop + d["n_residual"] == rx.size
+    say(f"  tiles {d['n_tiles']} residual {d['n_residual']} of {rx.size}")

@@ -128,26 +128,47 @@ def test_csc_multigraph_keeps_multiplicity():
     assert cip.tolist() == [0, 1, 4] and cix.tolist() == [0, 0, 0, 1]
 
 
-def _brute_tiles(indptr, indices, n, min_nnz):
-    cnt = {}
+def _brute_tiles(indptr, indices, n, min_nnz, T):
+    nb = (n + 15) // 16
+    deg = [indptr[i + 1] - indptr[i] for i in range(n)]
+    odeg = [0] * n
+    for j in indices:
+        odeg[int(j)] += 1
+    rb_ok = [all(deg[i] <= T for i in range(16 * b, min(n, 16 * b + 16))) for b in range(nb)]
+    cb_ok = [all(odeg[j] <= T for j in range(16 * c, min(n, 16 * c + 16))) for c in range(nb)]
+    seen = set()
+    cand = {}                                   # pair -> list of CSR edge ids (first occurrences)
     for i in range(n):
-        for j in indices[indptr[i]:indptr[i + 1]]:
-            cnt.setdefault((i // 16, int(j) // 16), []).append((i, int(j)))
-    tiles = sorted(k for k, v in cnt.items() if len(v) >= min_nnz)
+        for e in range(indptr[i], indptr[i + 1]):
+            j = int(indices[e])
+            if (i, j) in seen:
+                continue
+            seen.add((i, j))
+            if rb_ok[i // 16] and cb_ok[j // 16]:
+                cand.setdefault((i // 16, j // 16), []).append(e)
+    tiles = sorted(k for k, v in cand.items() if len(v) >= min_nnz)
+    in_tile = set()
     masks = []
     for t in tiles:
         bits = 0
-        for (i, j) in cnt[t]:
-            bits |= 1 << ((i % 16) * 16 + (j % 16))
+        for e in cand[t]:
+            i = int(np.searchsorted(indptr, e, side="right") - 1)
+            bits |= 1 << ((i % 16) * 16 + int(indices[e]) % 16)
+            in_tile.add(e)
         masks.append([(bits >> (64 * w)) & ((1 << 64) - 1) for w in range(4)])
-    tset = set(tiles)
-    rows = [[int(j) for j in indices[indptr[i]:indptr[i + 1]] if (i // 16, int(j) // 16) not in tset]
-            for i in range(n)]
-    return tiles, masks, rows
+    rows = [[int(indices[e]) for e in range(indptr[i], indptr[i + 1]) if e not in in_tile] for i in range(n)]
+    rb_t = [sum(1 for t in tiles if t[0] == b) for b in range(nb)]
+    cb_t = [sum(1 for t in tiles if t[1] == c) for c in range(nb)]
+    ctile = sorted(range(len(tiles)), key=lambda k: (tiles[k][1], tiles[k][0]))
+    light_nt = [i for i in range(n) if deg[i] <= T and rb_t[i // 16] == 0]
+    c_light_nt = [j for j in range(n) if odeg[j] <= T and cb_t[j // 16] == 0]
+    return dict(tiles=tiles, masks=masks, rows=rows, rb_t=rb_t, cb_t=cb_t, ctile=ctile, light_nt=light_nt,
+                c_light_nt=c_light_nt)
 
 
-@pytest.mark.parametrize("seed,n,min_nnz", [(0, 48, 192), (1, 70, 100), (2, 33, 1), (3, 16, 256)])
-def test_tile_census_matches_brute_force(seed, n, min_nnz):
+@pytest.mark.parametrize("seed,n,min_nnz,T", [(0, 48, 192, 10 ** 6), (1, 70, 100, 10 ** 6), (2, 33, 1, 10 ** 6),
+                                              (3, 16, 256, 10 ** 6), (4, 64, 150, 18), (5, 80, 120, 25)])
+def test_tile_census_matches_brute_force(seed, n, min_nnz, T):
     rng = np.random.default_rng(200 + seed)
     a = rng.random((n, n)) < 0.08
     for b0 in range(0, n - 15, 16):                 # some dense blocks, some partial ones
@@ -155,15 +176,36 @@ def test_tile_census_matches_brute_force(seed, n, min_nnz):
             a[b0:b0 + 16, b0:b0 + 16] |= rng.random((16, 16)) < 0.9
     dst, src = np.nonzero(a)
     ip, ix = oracle.csr_build(src, dst, n)
-    t = oracle.tile_census(ip, ix, n, min_nnz)
-    tiles, masks, rows = _brute_tiles(ip, ix, n, min_nnz)
-    assert [tuple(x) for x in t["tile_rc"].tolist()] == tiles
-    assert t["tile_mask"].tolist() == masks
-    rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    t = oracle.tile_census(ip, ix, n, min_nnz, T)
+    b = _brute_tiles(ip, ix, n, min_nnz, T)
+    assert [tuple(x) for x in t["tile_rc"].tolist()] == b["tiles"]
+    assert t["tile_mask"].tolist() == b["masks"]
+    rp = np.concatenate([[0], np.cumsum([len(r) for r in b["rows"]])])
     assert t["rindptr"].tolist() == rp.tolist()
-    assert t["rindices"].tolist() == sum(rows, [])
+    assert t["rindices"].tolist() == sum(b["rows"], [])
+    assert t["tile_ptr"].tolist() == np.concatenate([[0], np.cumsum(b["rb_t"])]).tolist()
+    assert t["ctile_ptr"].tolist() == np.concatenate([[0], np.cumsum(b["cb_t"])]).tolist()
+    assert t["ctile"].tolist() == b["ctile"]
+    assert t["light_nt"].tolist() == b["light_nt"] and t["c_light_nt"].tolist() == b["c_light_nt"]
+    assert t["trb"].tolist() == [k for k, v in enumerate(b["rb_t"]) if v]
+    assert t["tcb"].tolist() == [k for k, v in enumerate(b["cb_t"]) if v]
+    cip, cix = oracle.csc(t["rindptr"], t["rindices"], n)
+    assert np.array_equal(t["rcindptr"], cip) and np.array_equal(t["rcindices"], cix)
     # invariants: popcounts + residual account for every edge once
     pop = sum(bin(int(w)).count("1") for w in t["tile_mask"].ravel())
     assert pop + t["rindices"].size == ix.size
-    nb = (n + 15) // 16
-    assert t["tile_ptr"].size == nb + 1 and t["tile_ptr"][-1] == len(tiles)
+    if T < 10 ** 6:
+        deg = np.diff(ip)
+        for rb, _ in t["tile_rc"]:
+            assert np.all(deg[16 * rb:16 * rb + 16] <= T)
+
+
+def test_tile_census_multigraph_copies_stay_residual():
+    n = 16
+    rows = [np.concatenate([np.arange(16), [3, 3]]) if i == 2 else np.arange(16) for i in range(n)]
+    ip = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    ix = np.concatenate(rows).astype(np.int32)
+    t = oracle.tile_census(ip, ix, n, 256, 10 ** 6)
+    assert t["tile_rc"].tolist() == [[0, 0]]
+    assert all(int(w) == (1 << 64) - 1 for w in t["tile_mask"][0])
+    assert t["rindices"].tolist() == [3, 3] and np.diff(t["rindptr"]).tolist()[2] == 2
