@@ -38,7 +38,8 @@ sys.path.insert(0, ROOT)
 METRIC = "GEdges/s and achieved HBM GB/s (% of peak) for fused CSR attention fwd/bwd"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "gatv2_zipf21_n100k"
-KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_sparse_amd", "csrc", f) for f in ("attn.hip", "device.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_sparse_amd", "csrc", f)
+                  for f in ("attn.hip", "attn_core.h", "attn_tile.hip", "device.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 

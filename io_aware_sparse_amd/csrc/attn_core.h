@@ -1,0 +1,422 @@
+// Device building blocks shared by the CSR attention kernels and the 16x16
+// tile kernels: lane geometry, online-softmax state, the per-node edge
+// streams of the forward and of both backward passes, and launch helpers.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "device.h"
+#include "internal.h"
+
+namespace gnn {
+
+constexpr float kNegInf = -INFINITY;
+
+enum Mode { M_GT = 0, M_GAT_ALIAS = 1, M_GAT_SEPV = 2 };
+
+struct Geom {
+    int32_t N, H, D;
+    int32_t HW;       // heads per wave
+    int32_t NHG;      // head groups per node
+    int32_t lr_shift; // log2(LR)
+    int32_t G;        // edge groups per wave
+};
+
+struct FwdParams {
+    Geom g;
+    const int32_t *indptr, *indices;
+    const void *Q, *K, *V;
+    void *O;
+    float *LSE;
+    const float *att;
+    float slope, mul;   // mul: score multiplier into log2 units
+    const int32_t *light;
+    int32_t n_light;
+    const int32_t *groups;
+    int32_t n_groups, C;
+    const int32_t *heavy, *partial_ofs;
+    int32_t n_heavy;
+    float *ws_acc, *ws_ml;
+    int32_t W;
+};
+
+// per-lane position inside the wave's (node, head group) slice
+struct LanePos {
+    int lane, g, r, hh, dv, h;
+    bool act;
+    int64_t col;   // element offset inside the node's H*D row
+};
+
+template <int LH, int NV>
+__device__ __forceinline__ LanePos lane_pos(const Geom &G, int hg) {
+    LanePos p;
+    p.lane = lane_id();
+    const int LR = 1 << G.lr_shift;
+    p.g = p.lane >> G.lr_shift;
+    p.r = p.lane & (LR - 1);
+    p.hh = p.r / LH;
+    p.dv = p.r % LH;
+    p.h = hg * G.HW + p.hh;
+    p.act = (p.hh < G.HW) && (p.h < G.H);
+    p.col = (int64_t)p.h * G.D + p.dv * NV;
+    return p;
+}
+
+template <int NV>
+struct SoftState {
+    float m, l, acc[NV];
+};
+
+template <int NV>
+__device__ __forceinline__ void merge_state(SoftState<NV> &a, float m2, float l2, const float (&a2)[NV]) {
+    const float mn = fmaxf(a.m, m2);
+    const float ms = (mn == kNegInf) ? 0.f : mn;
+    const float c1 = fast_exp2(a.m - ms), c2 = fast_exp2(m2 - ms);
+    a.l = a.l * c1 + l2 * c2;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) a.acc[k] = a.acc[k] * c1 + a2[k] * c2;
+    a.m = mn;
+}
+
+template <int NV>
+__device__ __forceinline__ void merge_groups(SoftState<NV> &st, int lr_shift) {
+    for (int off = 1 << lr_shift; off < kWave; off <<= 1) {
+        const float m2 = xor_lane(st.m, off), l2 = xor_lane(st.l, off);
+        float a2[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) a2[k] = xor_lane(st.acc[k], off);
+        merge_state(st, m2, l2, a2);
+    }
+}
+
+// Stream edges [e0, e1) of `node` for this lane's head group; returns the
+// wave-merged online-softmax state (valid in every lane). With reset false
+// the caller's state is continued (only edge group 0 may carry a non-empty
+// state, the other groups must start empty).
+template <class T, int LH, int MODE, int U>
+__device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp, int node, int e0, int e1,
+                                           SoftState<Vec<T>::N> &st, bool reset = true) {
+    using VT = Vec<T>;
+    constexpr int NV = VT::N;
+    const Geom &G = P.g;
+    const int64_t rowlen = (int64_t)G.H * G.D;
+    float q[NV];
+    float a[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) q[k] = a[k] = 0.f;
+    if (lp.act) {
+        VT::unpack(load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col), q);
+        if (MODE != M_GT) {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) a[k] = P.att[lp.col + k] * kLog2e;
+        }
+    }
+    if (reset) {
+        st.m = kNegInf;
+        st.l = 0.f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) st.acc[k] = 0.f;
+    }
+
+    const int S = min(kWave, G.G * U);   // edges per step
+    const int UE = S / G.G;               // steps per group actually used
+    int jn = (lp.lane < S && e0 + lp.lane < e1) ? P.indices[e0 + lp.lane] : -1;
+    for (int base = e0; base < e1; base += S) {
+        const int jc = jn;
+        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? P.indices[base + S + lp.lane] : -1;
+        int j[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) j[u] = (u < UE) ? __shfl(jc, u * G.G + lp.g, kWave) : -1;
+        typename VT::raw kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            kr[u] = (lp.act && j[u] >= 0) ? load_vec<T>(P.K, (int64_t)j[u] * rowlen + lp.col) : VT::zero();
+            if (MODE != M_GAT_ALIAS)
+                vr[u] = (lp.act && j[u] >= 0) ? load_vec<T>(P.V, (int64_t)j[u] * rowlen + lp.col) : VT::zero();
+        }
+        float s[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float kf[NV];
+            VT::unpack(kr[u], kf);
+            float t = 0.f;
+            if (MODE == M_GT) {
+#pragma unroll
+                for (int k = 0; k < NV; ++k) t = fmaf(q[k], kf[k], t);
+            } else {
+#pragma unroll
+                for (int k = 0; k < NV; ++k) {
+                    const float z = kf[k] + q[k];
+                    t = fmaf(a[k], z >= 0.f ? z : P.slope * z, t);
+                }
+            }
+            t = group_sum<LH>(t);
+            s[u] = (j[u] >= 0) ? t * P.mul : kNegInf;
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u]);
+        const float mn = fmaxf(st.m, mx);
+        const float ms = (mn == kNegInf) ? 0.f : mn;
+        const float c = fast_exp2(st.m - ms);
+        st.l *= c;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) st.acc[k] *= c;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float p = fast_exp2(s[u] - ms);
+            st.l += p;
+            float vf[NV];
+            VT::unpack(MODE == M_GAT_ALIAS ? kr[u] : vr[u], vf);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) st.acc[k] = fmaf(p, vf[k], st.acc[k]);
+        }
+        st.m = mn;
+    }
+    merge_groups(st, G.lr_shift);
+}
+
+template <class T, int NV>
+__device__ __forceinline__ void write_out(const FwdParams &P, const LanePos &lp, int node, const SoftState<NV> &st) {
+    using VT = Vec<T>;
+    if (lp.g != 0 || !lp.act) return;
+    const int64_t rowlen = (int64_t)P.g.H * P.g.D;
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    float o[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) o[k] = st.acc[k] * inv;
+    store_vec<T>(P.O, (int64_t)node * rowlen + lp.col, VT::pack(o));
+    if (P.LSE && lp.dv == 0)
+        P.LSE[(int64_t)node * P.g.H + lp.h] = st.l > 0.f ? (st.m + fast_log2(st.l)) * kLn2 : kNegInf;
+}
+
+// Main forward kernel: blocks [0, n_groups*NHG) are heavy chunk groups,
+// the rest hold W light (node, head group) items, one per wave.
+
+struct BwdParams {
+    Geom g;
+    const int32_t *indptr, *indices;     // CSR (destination pass)
+    const int32_t *cindptr, *cindices;   // transposed adjacency (source pass)
+    const void *Q, *K, *V, *O, *dO;
+    const float *LSE;
+    void *dQ, *dK, *dV;
+    float mul, scale;
+    // destination-pass buckets
+    const int32_t *a_light, *a_groups, *a_heavy, *a_ofs;
+    int32_t a_n_light, a_n_groups, a_n_heavy;
+    // source-pass buckets
+    const int32_t *b_light, *b_groups, *b_heavy, *b_ofs;
+    int32_t b_n_light, b_n_groups, b_n_heavy;
+    int32_t C, W;
+    float2 *stat;    // [N][H] (LSE * log2 e, Delta)
+    float *ws_a;     // [a_n_groups][2*H*D + H]
+    float *ws_b;     // [b_n_groups][2][H*D]
+};
+
+template <int NV>
+__device__ __forceinline__ void sum_groups(float (&x)[NV], int lr_shift) {
+    for (int off = 1 << lr_shift; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) x[k] += xor_lane(x[k], off);
+    }
+}
+
+template <class T, int NV>
+__device__ __forceinline__ void store_scaled(void *base, int64_t off, const float (&x)[NV], float sc) {
+    float o[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) o[k] = x[k] * sc;
+    store_vec<T>(base, off, Vec<T>::pack(o));
+}
+
+// Destination side over edges [e0, e1) of `node`. With p = exp(s - LSE) and
+// dp = <dO_i, V_j> it accumulates A = sum p*dp*K_j, B = sum p*K_j and
+// Delta = sum p*dp, so that dQ_i = scale * (A - Delta * B) in one pass.
+// Delta is thus formed from the recomputed weights (its definition), not
+// from <dO_i, O_i> with a rounded O. Returns this lane's lse2 = LSE*log2 e.
+template <class T, int LH, int U>
+__device__ __forceinline__ void bwd_dst_stream(const BwdParams &P, const LanePos &lp, int node, int e0, int e1,
+                                               float (&A)[Vec<T>::N], float (&B)[Vec<T>::N], float &dsum,
+                                               float &lse2, bool reset = true) {
+    using VT = Vec<T>;
+    constexpr int NV = VT::N;
+    const Geom &G = P.g;
+    const int64_t rowlen = (int64_t)G.H * G.D;
+    float q[NV], dof[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) q[k] = dof[k] = 0.f;
+    if (reset) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) A[k] = B[k] = 0.f;
+        dsum = 0.f;
+    }
+    lse2 = kNegInf;
+    if (lp.act) {
+        VT::unpack(load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col), q);
+        VT::unpack(load_vec<T>(P.dO, (int64_t)node * rowlen + lp.col), dof);
+        lse2 = P.LSE[(int64_t)node * G.H + lp.h] * kLog2e;
+    }
+    const int S = min(kWave, G.G * U);
+    const int UE = S / G.G;
+    int jn = (lp.lane < S && e0 + lp.lane < e1) ? P.indices[e0 + lp.lane] : -1;
+    for (int base = e0; base < e1; base += S) {
+        const int jc = jn;
+        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? P.indices[base + S + lp.lane] : -1;
+        int j[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) j[u] = (u < UE) ? __shfl(jc, u * G.G + lp.g, kWave) : -1;
+        typename VT::raw kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = lp.act && j[u] >= 0;
+            kr[u] = ok ? load_vec<T>(P.K, (int64_t)j[u] * rowlen + lp.col) : VT::zero();
+            vr[u] = ok ? load_vec<T>(P.V, (int64_t)j[u] * rowlen + lp.col) : VT::zero();
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float kf[NV], vf[NV];
+            VT::unpack(kr[u], kf);
+            VT::unpack(vr[u], vf);
+            float ts = 0.f, tp = 0.f;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                ts = fmaf(q[k], kf[k], ts);
+                tp = fmaf(dof[k], vf[k], tp);
+            }
+            ts = group_sum<LH>(ts);
+            tp = group_sum<LH>(tp);
+            const float p = (j[u] >= 0) ? fast_exp2(ts * P.mul - lse2) : 0.f;
+            const float pd = p * tp;
+            dsum += pd;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                A[k] = fmaf(pd, kf[k], A[k]);
+                B[k] = fmaf(p, kf[k], B[k]);
+            }
+        }
+    }
+    sum_groups(A, G.lr_shift);
+    sum_groups(B, G.lr_shift);
+    for (int off = 1 << G.lr_shift; off < kWave; off <<= 1) dsum += xor_lane(dsum, off);
+}
+
+// Source side: dK_j, dV_j partials over transposed edges [e0, e1).
+template <class T, int LH, int U>
+__device__ __forceinline__ void bwd_src_stream(const BwdParams &P, const LanePos &lp, int node, int e0, int e1,
+                                               float (&dk)[Vec<T>::N], float (&dv)[Vec<T>::N],
+                                               bool reset = true) {
+    using VT = Vec<T>;
+    constexpr int NV = VT::N;
+    const Geom &G = P.g;
+    const int64_t rowlen = (int64_t)G.H * G.D;
+    float kf[NV], vf[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) kf[k] = vf[k] = 0.f;
+    if (reset) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) dk[k] = dv[k] = 0.f;
+    }
+    if (lp.act) {
+        VT::unpack(load_vec<T>(P.K, (int64_t)node * rowlen + lp.col), kf);
+        VT::unpack(load_vec<T>(P.V, (int64_t)node * rowlen + lp.col), vf);
+    }
+    const int S = min(kWave, G.G * U);
+    const int UE = S / G.G;
+    int jn = (lp.lane < S && e0 + lp.lane < e1) ? P.cindices[e0 + lp.lane] : -1;
+    for (int base = e0; base < e1; base += S) {
+        const int jc = jn;
+        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? P.cindices[base + S + lp.lane] : -1;
+        int i[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) i[u] = (u < UE) ? __shfl(jc, u * G.G + lp.g, kWave) : -1;
+        typename VT::raw qr[U], gr[U];
+        float2 stt[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = lp.act && i[u] >= 0;
+            qr[u] = ok ? load_vec<T>(P.Q, (int64_t)i[u] * rowlen + lp.col) : VT::zero();
+            gr[u] = ok ? load_vec<T>(P.dO, (int64_t)i[u] * rowlen + lp.col) : VT::zero();
+            stt[u] = ok ? P.stat[(int64_t)i[u] * G.H + lp.h] : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float qf[NV], gf[NV];
+            VT::unpack(qr[u], qf);
+            VT::unpack(gr[u], gf);
+            float ts = 0.f, tp = 0.f;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                ts = fmaf(qf[k], kf[k], ts);
+                tp = fmaf(gf[k], vf[k], tp);
+            }
+            ts = group_sum<LH>(ts);
+            tp = group_sum<LH>(tp);
+            const float p = (i[u] >= 0) ? fast_exp2(ts * P.mul - stt[u].x) : 0.f;
+            const float ds = p * (tp - stt[u].y);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                dv[k] = fmaf(p, gf[k], dv[k]);
+                dk[k] = fmaf(ds, qf[k], dk[k]);
+            }
+        }
+    }
+    sum_groups(dk, G.lr_shift);
+    sum_groups(dv, G.lr_shift);
+}
+
+// LDS sum of W waves' partial vectors (ascending wave order), result in wave 0.
+template <int NV, int NA>
+__device__ __forceinline__ bool lds_sum_waves(float *lds, int w, int W, int lane, int LR, float (&x)[NA][NV]) {
+    float *mine = lds + ((size_t)w * LR + lane) * (NV * NA);
+    if (lane < LR) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int k = 0; k < NV; ++k) mine[a * NV + k] = x[a][k];
+    }
+    __syncthreads();
+    if (w != 0 || lane >= LR) return false;
+    for (int v = 1; v < W; ++v) {
+        const float *o = lds + ((size_t)v * LR + lane) * (NV * NA);
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int k = 0; k < NV; ++k) x[a][k] += o[a * NV + k];
+    }
+    return true;
+}
+
+template <class T, int NV>
+__device__ __forceinline__ void store_dq(const BwdParams &P, const LanePos &lp, int node, const float (&A)[NV],
+                                         const float (&B)[NV], float dsum, float lse2) {
+    float dq[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) dq[k] = fmaf(-dsum, B[k], A[k]);
+    store_scaled<T, NV>(P.dQ, (int64_t)node * P.g.H * P.g.D + lp.col, dq, P.scale);
+    if (lp.dv == 0) P.stat[(int64_t)node * P.g.H + lp.h] = make_float2(lse2, dsum);
+}
+
+
+// kernel launch with optional per-kernel event timing on the plan
+template <class K, class... Args>
+static int launch(gnn_plan_t plan, int kind, K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                  const Args &...args) {
+    if (grid.x == 0) return GNN_OK;
+    TimingRec rec;
+    const bool timed = plan && plan->timer.enabled;
+    if (timed) GNN_TRY(plan->timer.begin(kind, s, rec));
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    GNN_HIP(hipGetLastError());
+    if (timed) GNN_TRY(plan->timer.end(rec, s));
+    return GNN_OK;
+}
+
+// 16x16 tile kernels (attn_tile.hip): true when the tile path serves this
+// dtype / head size; the launchers run the tiled row (or column) blocks
+bool tile_supported(gnn_dtype_t dt, int D);
+int launch_tile_fwd(gnn_plan_t plan, const FwdParams &P, int D, hipStream_t s);
+int launch_tile_bwd_dst(gnn_plan_t plan, const BwdParams &P, int D, hipStream_t s);
+int launch_tile_bwd_src(gnn_plan_t plan, const BwdParams &P, int D, hipStream_t s);
+
+}  // namespace gnn

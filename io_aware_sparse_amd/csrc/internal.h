@@ -63,7 +63,8 @@ enum KernelKind {
     K_BWD_SRC_MAIN,
     K_BWD_SRC_MERGE,
     K_TILE_FWD,
-    K_TILE_BWD,
+    K_TILE_BWD_DST,
+    K_TILE_BWD_SRC,
     K_NUM_KINDS
 };
 extern const char *kKernelNames[K_NUM_KINDS];
