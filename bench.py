@@ -57,28 +57,77 @@ def kernel_source_hash() -> str:
 
 # --------------------------------------------------------------- byte model
 
-def kernel_bytes(kind, N, E, H, D, s, n_light, n_heavy, c_n_light, c_n_heavy, v_alias=True):
+def step_counts(info, indptr, indices, tiled):
+    """Per-kernel unit counts for the byte model."""
+    import numpy as np
+    ip = indptr.astype(np.int64)
+    n = ip.size - 1
+    deg = np.diff(ip)
+    c = {"N": n, "E": int(ip[-1])}
+    light = info["light_nt"] if tiled else info["light"]
+    heavy = info["heavy"]
+    c["main_rows"] = int(light.size + heavy.size)
+    c["main_light"] = int(light.size)
+    c["main_heavy"] = int(heavy.size)
+    c["main_edges"] = int(deg[light].sum() + deg[heavy].sum())
+    if info.get("has_csc"):
+        odeg = np.diff(info["cindptr"].astype(np.int64))
+        cl = info["c_light_nt"] if tiled else info["c_light"]
+        ch = info["c_heavy"]
+        c["src_rows"] = int(cl.size + ch.size)
+        c["src_light"] = int(cl.size)
+        c["src_heavy"] = int(ch.size)
+        c["src_edges"] = int(odeg[cl].sum() + odeg[ch].sum())
+    if tiled:
+        c["tiles"] = int(info["n_tiles"])
+        rows = (16 * info["trb"][:, None].astype(np.int64) + np.arange(16)).ravel()
+        rows = rows[rows < n]
+        rdeg = np.diff(info["rindptr"].astype(np.int64))
+        c["tile_rows"] = int(rows.size)
+        c["tile_res_edges"] = int(rdeg[rows].sum())
+        if info.get("has_csc"):
+            srcs = (16 * info["tcb"][:, None].astype(np.int64) + np.arange(16)).ravel()
+            srcs = srcs[srcs < n]
+            rcdeg = np.diff(info["rcindptr"].astype(np.int64))
+            c["tile_srcs"] = int(srcs.size)
+            c["tile_res_src_edges"] = int(rcdeg[srcs].sum())
+    return c
+
+
+def kernel_bytes(kind, c, H, D, s, v_alias=True):
     """Algorithmic HBM bytes one launch of kernel `kind` must move.
 
-    R = H*D*s is one node's feature row. Counted: CSR structure once, one
-    gathered row per edge per gathered table, per-node rows read or written
-    once, per-node statistics. Not counted: heavy partials (workspace) and
-    any re-read a cache would serve."""
+    R = H*D*s is one node's feature row. Counted: the CSR structure the
+    kernel walks, one gathered row per edge per gathered table (a 16x16 tile
+    counts its 16 source rows per table once: 32R per tile for two tables),
+    per-node rows read or written once, per-node statistics and tile
+    metadata (40 B per tile). Not counted: heavy partials (workspace) and any
+    re-read a cache would serve."""
     R = H * D * s
+    rows, E, nl, nh = c.get("main_rows", 0), c.get("main_edges", 0), c.get("main_light", 0), c.get("main_heavy", 0)
     if kind in ("gt_fwd_main", "gatv2_fwd_main"):
-        rows = R * E * (1 if (kind == "gatv2_fwd_main" and v_alias) else 2)
+        g = R * E * (1 if (kind == "gatv2_fwd_main" and v_alias) else 2)
         extra = 4 * H * D if kind == "gatv2_fwd_main" else 0
-        return 4 * (N + 1) + 4 * E + rows + R * N + (R + 4 * H) * n_light + extra
+        return 4 * (rows + 1) + 4 * E + g + R * rows + (R + 4 * H) * nl + extra
     if kind in ("gt_fwd_merge", "gatv2_fwd_merge"):
-        return (R + 4 * H) * n_heavy
+        return (R + 4 * H) * nh
     if kind == "gt_bwd_dst_main":     # reads Q, dO, LSE; gathers K, V; writes dQ and (lse, Delta)
-        return 4 * (N + 1) + 4 * E + 2 * R * E + (2 * R + 4 * H) * N + (R + 8 * H) * n_light
+        return 4 * (rows + 1) + 4 * E + 2 * R * E + (2 * R + 4 * H) * rows + (R + 8 * H) * nl
     if kind == "gt_bwd_dst_merge":
-        return (R + 8 * H) * n_heavy
+        return (R + 8 * H) * nh
+    sr, se, sl, sh = c.get("src_rows", 0), c.get("src_edges", 0), c.get("src_light", 0), c.get("src_heavy", 0)
     if kind == "gt_bwd_src_main":     # reads K, V; gathers Q, dO and (lse, Delta); writes dK, dV
-        return 4 * (N + 1) + 4 * E + (2 * R + 8 * H) * E + 2 * R * N + 2 * R * c_n_light
+        return 4 * (sr + 1) + 4 * se + (2 * R + 8 * H) * se + 2 * R * sr + 2 * R * sl
     if kind == "gt_bwd_src_merge":
-        return 2 * R * c_n_heavy
+        return 2 * R * sh
+    t, tr, te = c.get("tiles", 0), c.get("tile_rows", 0), c.get("tile_res_edges", 0)
+    if kind == "gt_tile_fwd":         # tiles: K, V blocks; rows: Q in, O and LSE out; residual gathers
+        return 40 * t + 32 * R * t + 4 * (tr + 1) + (4 + 2 * R) * te + R * tr + (R + 4 * H) * tr
+    if kind == "gt_tile_bwd_dst":     # tiles: K, V blocks; rows: Q, dO, LSE in, dQ, stats out
+        return 40 * t + 32 * R * t + 4 * (tr + 1) + (4 + 2 * R) * te + (2 * R + 4 * H) * tr + (R + 8 * H) * tr
+    ts, tse = c.get("tile_srcs", 0), c.get("tile_res_src_edges", 0)
+    if kind == "gt_tile_bwd_src":     # tiles: Q, dO blocks + 16 row stats; sources: K, V in, dK, dV out
+        return 40 * t + (32 * R + 16 * 8 * H) * t + 4 * (ts + 1) + (4 + 2 * R + 8 * H) * tse + 4 * R * ts
     return 0
 
 
@@ -325,7 +374,8 @@ def bench(args) -> int:
         return 2
     g.lib()
     torch.cuda.set_device(0)
-    opts = dict(light_threshold=args.light_threshold, chunk=args.chunk, waves_per_group=args.waves)
+    opts = dict(light_threshold=args.light_threshold, chunk=args.chunk, waves_per_group=args.waves,
+                tile_density=args.tile_density)
     log(f"[bench] workload {args.workload}: generating and building the graph")
     wl, indptr, indices, plan, T, E, prep = setup(args.workload, opts)
     info = g.gnn_plan_export(plan)
@@ -366,19 +416,19 @@ def bench(args) -> int:
     value = E / (ms_step * 1e-3) / 1e9
 
     v_alias = True
-    counts = dict(n_light=info["n_light"], n_heavy=info["n_heavy"], c_n_light=info["c_n_light"],
-                  c_n_heavy=info["c_n_heavy"])
+    tiled = bool(info["has_tiles"]) and wl.dtype == "bf16" and D in (32, 64, 128) and wl.kind == "gt"
+    counts = step_counts(g.gnn_plan_export(plan, arrays=True), indptr.cpu().numpy(), indices.cpu().numpy(), tiled)
     kernels = {}
     for name, (launches, tot_ms) in kt.items():
         avg_ms = tot_ms / max(1, launches)
-        b = kernel_bytes(name, N, E, H, D, s, v_alias=v_alias, **counts)
+        b = kernel_bytes(name, counts, H, D, s, v_alias=v_alias)
         kernels[name] = dict(launches=launches, avg_us=round(1e3 * avg_ms, 3), alg_bytes=b,
                              GBps=round(b / (avg_ms * 1e-3) / 1e9, 1) if avg_ms > 0 else None)
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dk = kernels[dom]
     achieved = dk["GBps"]
     traffic = read_traffic(dom, args.workload)
-    step_bytes = sum(kernel_bytes(k, N, E, H, D, s, v_alias=v_alias, **counts) for k in kernels)
+    step_bytes = sum(kernel_bytes(k, counts, H, D, s, v_alias=v_alias) for k in kernels)
     rec = {
         "metric": METRIC,
         "value": round(value, 4),
@@ -399,6 +449,7 @@ def bench(args) -> int:
             "n_nodes": N, "n_edges": E, "heads": H, "dim": D,
             "storage": wl.dtype, "math": "f32",
             "light_threshold": args.light_threshold, "chunk": args.chunk, "waves_per_group": args.waves,
+            "tile_density": args.tile_density, "tiles": int(info["n_tiles"]),
             "cache": "flushed 512 MiB between steps" if args.flush else "warm (back-to-back steps)",
             "parallelism": "single GPU",
         },
@@ -452,6 +503,8 @@ def main():
     ap.add_argument("--light-threshold", type=int, default=512)
     ap.add_argument("--chunk", type=int, default=512)
     ap.add_argument("--waves", type=int, default=4)
+    ap.add_argument("--tile-density", type=float, default=0.0,
+                    help="16x16 tile threshold tau (0 disables the tile path)")
     ap.add_argument("--flush", action="store_true", help="flush caches with a 512 MiB write between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
