@@ -59,7 +59,10 @@ def _load():
         lib.orc_gatv2_fwd.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, i64, P, P, P, P, P]
         lib.orc_gt_bwd_rows.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, i64, P, P, P, P, P, P]
         lib.orc_gt_bwd_srcs.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, P, P, P, P, i64, P, P, P, P, P]
-        for f in (lib.orc_gt_fwd, lib.orc_gatv2_fwd, lib.orc_gt_bwd_rows, lib.orc_gt_bwd_srcs):
+        lib.orc_gatv2_bwd_rows.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, P, i64, P, P, P, P, P, P, P, P]
+        lib.orc_gatv2_bwd_srcs.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, P, P, P, P, P, i64, P, P, P, P, P]
+        for f in (lib.orc_gt_fwd, lib.orc_gatv2_fwd, lib.orc_gt_bwd_rows, lib.orc_gt_bwd_srcs, lib.orc_gatv2_bwd_rows,
+                  lib.orc_gatv2_bwd_srcs):
             f.restype = C.c_int
         lib.orc_num_threads.restype = C.c_int
         _lib = lib
@@ -331,6 +334,69 @@ def gt_bwd(indptr, indices, Q, K, V, dO, scale: Optional[float] = None, rows=Non
         raise RuntimeError("oracle source pass: missing destination statistics")
     out.update(dK=dK, dV=dV, SdK=SdK, SdV=SdV)
     return out
+
+
+def gatv2_bwd(indptr, indices, XD, XS, att, dO, V=None, slope: float = 0.2, rows=None, srcs=None,
+              csc_arrays=None, want_src: bool = True, want_da: bool = True):
+    """GATv2 backward in fp64, from the definition.
+
+    Returns dict with dXD, Delta, SdXD for `rows` (None = all); dXS (score
+    path plus, when V is XS, the value path), dV (value path, only when V is
+    separate) and their scales for `srcs`; and, with want_da, d_att [H, D]
+    summed over every edge of the graph (with its scale)."""
+    XD, XS, dO, a = _f64(XD), _f64(XS), _f64(dO), _f64(att)
+    alias = V is None
+    Vv = XS if alias else _f64(V)
+    N, H, D = XD.shape
+    ip, ix = _graph(indptr, indices)
+    lib = _load()
+
+    def rows_pass(r, nr):
+        out = [np.empty((nr, H, D)), np.empty((nr, H)), np.empty((nr, H)), np.empty((nr, H)),
+               np.empty((nr, H, D)), np.empty((nr, H, D)), np.empty((nr, H, D))]
+        rc = lib.orc_gatv2_bwd_rows(N, _p(ip), _p(ix), H, D, _p(XD), _p(XS), _p(Vv), _p(a), float(slope), _p(dO),
+                                    nr, _p(r), *[_p(o) for o in out])
+        if rc:
+            raise MemoryError("oracle row buffer")
+        return out
+
+    r, nr = _rows(rows, N)
+    dXD, Dl, M, Z, DA, SdXD, SDA = rows_pass(r, nr)
+    res = dict(dXD=dXD, Delta=Dl, SdXD=SdXD)
+    if want_da:
+        if r is None:
+            DAall, SDAall = DA, SDA
+        else:
+            _, _, _, _, DAall, _, SDAall = rows_pass(None, N)
+        res["d_att"] = DAall.sum(axis=0)
+        res["Sd_att"] = SDAall.sum(axis=0)
+    if not want_src:
+        return res
+    cip, cix = csc(ip, ix, N) if csc_arrays is None else csc_arrays
+    cip = np.ascontiguousarray(cip, np.int64)
+    cix = np.ascontiguousarray(cix, np.int32)
+    s, ns = _rows(srcs, N)
+    if s is None:
+        need = np.arange(N, dtype=np.int64)
+    else:
+        parts = [cix[cip[j]:cip[j + 1]] for j in s]
+        need = np.unique(np.concatenate(parts).astype(np.int64)) if parts else np.zeros(0, np.int64)
+    if r is None and s is None:
+        M2, Z2, D2 = M, Z, Dl
+    else:
+        _, D2, M2, Z2, _, _, _ = rows_pass(need, need.size)
+    slot = np.full(N, -1, np.int64)
+    slot[need] = np.arange(need.size)
+    dXS = np.empty((ns, H, D)); dV = np.empty((ns, H, D)); SdXS = np.empty((ns, H, D)); SdV = np.empty((ns, H, D))
+    rc = lib.orc_gatv2_bwd_srcs(N, _p(cip), _p(cix), H, D, _p(XD), _p(XS), _p(Vv), _p(a), float(slope), _p(dO),
+                                _p(slot), _p(M2), _p(Z2), _p(D2), ns, _p(s), _p(dXS), _p(dV), _p(SdXS), _p(SdV))
+    if rc:
+        raise RuntimeError("oracle source pass: missing destination statistics")
+    if alias:
+        res.update(dXS=dXS + dV, SdXS=SdXS + SdV)
+    else:
+        res.update(dXS=dXS, SdXS=SdXS, dV=dV, SdV=SdV)
+    return res
 
 
 def scaled_error(x, ref, scale) -> float:

@@ -333,3 +333,139 @@ int orc_gt_bwd_srcs(int64_t N, const int64_t *cindptr, const int32_t *cindices, 
     }
     return err;
 }
+
+/*
+ * GATv2 backward, written from the definition. Per head h, with
+ * z_ijd = xs_jd + xd_id, phi = LeakyReLU(slope), phi'(z) = 1 (z >= 0) or slope,
+ * s_ij = sum_d a_d phi(z_ijd), alpha_ij = softmax_j s_ij, O_i = sum_j alpha_ij v_j:
+ *   dalpha_ij = <dO_i, v_j>,  Delta_i = sum_j alpha_ij dalpha_ij,
+ *   ds_ij = alpha_ij (dalpha_ij - Delta_i),  dz_ijd = ds_ij a_d phi'(z_ijd)
+ *   dXD_i = sum_j dz_ij,   dXS_j = sum_i dz_ij,   dV_j = sum_i alpha_ij dO_i,
+ *   da_d  = sum_ij ds_ij phi(z_ijd).
+ * Destination side (per listed row): dXD, Delta, the row statistics M, Z, the
+ * row's da contribution DA [nr,H,D], and scales SdXD, SDA.
+ */
+int orc_gatv2_bwd_rows(int64_t N, const int64_t *indptr, const int32_t *indices, int H, int D,
+                       const double *XD, const double *XS, const double *V, const double *att, double slope,
+                       const double *dO, int64_t nr, const int64_t *rows, double *dXD, double *Delta, double *M,
+                       double *Z, double *DA, double *SdXD, double *SDA) {
+    if (!rows) nr = N;
+    int err = 0;
+#pragma omp parallel
+    {
+        rowbuf b = {0, 0};
+        rowbuf da = {0, 0};
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t r = 0; r < nr; ++r) {
+            int64_t i = row_of(rows, r);
+            int64_t e0 = indptr[i], deg = indptr[i + 1] - e0;
+            if (rowbuf_need(&b, deg) || rowbuf_need(&da, deg)) {
+#pragma omp atomic write
+                err = -1;
+                continue;
+            }
+            for (int h = 0; h < H; ++h) {
+                double *gx = dXD + IDX3(r, h, 0, H, D), *ga = DA + IDX3(r, h, 0, H, D);
+                double *sx = SdXD ? SdXD + IDX3(r, h, 0, H, D) : NULL, *sa = SDA ? SDA + IDX3(r, h, 0, H, D) : NULL;
+                for (int d = 0; d < D; ++d) {
+                    gx[d] = ga[d] = 0.0;
+                    if (sx) sx[d] = 0.0;
+                    if (sa) sa[d] = 0.0;
+                }
+                if (deg == 0) {
+                    Delta[r * H + h] = 0.0;
+                    M[r * H + h] = -INFINITY;
+                    Z[r * H + h] = 0.0;
+                    continue;
+                }
+                double m = -INFINITY;
+                for (int64_t e = 0; e < deg; ++e) {
+                    b.s[e] = gatv2_logit(XD, XS, att, i, indices[e0 + e], h, H, D, slope);
+                    if (b.s[e] > m) m = b.s[e];
+                }
+                double z = 0.0;
+                for (int64_t e = 0; e < deg; ++e) z += exp(b.s[e] - m);
+                double delta = 0.0;
+                for (int64_t e = 0; e < deg; ++e) {
+                    int64_t j = indices[e0 + e];
+                    b.s[e] = exp(b.s[e] - m) / z;
+                    double t = 0.0;
+                    for (int d = 0; d < D; ++d) t += dO[IDX3(i, h, d, H, D)] * V[IDX3(j, h, d, H, D)];
+                    da.s[e] = t;
+                    delta += b.s[e] * t;
+                }
+                for (int64_t e = 0; e < deg; ++e) {
+                    int64_t j = indices[e0 + e];
+                    double ds = b.s[e] * (da.s[e] - delta);
+                    double cs = b.s[e] * (fabs(da.s[e]) + fabs(delta));
+                    for (int d = 0; d < D; ++d) {
+                        double zz = XS[IDX3(j, h, d, H, D)] + XD[IDX3(i, h, d, H, D)];
+                        double ph = (zz >= 0.0) ? zz : slope * zz;
+                        double dph = (zz >= 0.0) ? 1.0 : slope;
+                        double ad = att[(int64_t)h * D + d];
+                        gx[d] += ds * ad * dph;
+                        ga[d] += ds * ph;
+                        if (sx) sx[d] += cs * fabs(ad * dph);
+                        if (sa) sa[d] += cs * fabs(ph);
+                    }
+                }
+                Delta[r * H + h] = delta;
+                M[r * H + h] = m;
+                Z[r * H + h] = z;
+            }
+        }
+        free(b.s);
+        free(da.s);
+    }
+    return err;
+}
+
+/*
+ * GATv2 backward, source side over the transposed adjacency: dXS_j (the
+ * score path only) and dV_j, with scales. Row statistics from
+ * orc_gatv2_bwd_rows through slot[] as in orc_gt_bwd_srcs.
+ */
+int orc_gatv2_bwd_srcs(int64_t N, const int64_t *cindptr, const int32_t *cindices, int H, int D,
+                       const double *XD, const double *XS, const double *V, const double *att, double slope,
+                       const double *dO, const int64_t *slot, const double *M, const double *Z, const double *Delta,
+                       int64_t ns, const int64_t *srcs, double *dXS, double *dV, double *SdXS, double *SdV) {
+    if (!srcs) ns = N;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t r = 0; r < ns; ++r) {
+        int64_t j = row_of(srcs, r);
+        for (int h = 0; h < H; ++h) {
+            double *gs = dXS + IDX3(r, h, 0, H, D), *gv = dV + IDX3(r, h, 0, H, D);
+            double *ss = SdXS ? SdXS + IDX3(r, h, 0, H, D) : NULL, *sv = SdV ? SdV + IDX3(r, h, 0, H, D) : NULL;
+            for (int d = 0; d < D; ++d) {
+                gs[d] = gv[d] = 0.0;
+                if (ss) ss[d] = 0.0;
+                if (sv) sv[d] = 0.0;
+            }
+            for (int64_t e = cindptr[j]; e < cindptr[j + 1]; ++e) {
+                int64_t i = cindices[e];
+                int64_t si = slot[i];
+                if (si < 0) {
+#pragma omp atomic write
+                    err = -2;
+                    continue;
+                }
+                double a = exp(gatv2_logit(XD, XS, att, i, j, h, H, D, slope) - M[si * H + h]) / Z[si * H + h];
+                double t = 0.0;
+                for (int d = 0; d < D; ++d) t += dO[IDX3(i, h, d, H, D)] * V[IDX3(j, h, d, H, D)];
+                double dlt = Delta[si * H + h];
+                double ds = a * (t - dlt), cs = a * (fabs(t) + fabs(dlt));
+                for (int d = 0; d < D; ++d) {
+                    double zz = XS[IDX3(j, h, d, H, D)] + XD[IDX3(i, h, d, H, D)];
+                    double dph = (zz >= 0.0) ? 1.0 : slope;
+                    double ad = att[(int64_t)h * D + d], g = dO[IDX3(i, h, d, H, D)];
+                    gs[d] += ds * ad * dph;
+                    gv[d] += a * g;
+                    if (ss) ss[d] += cs * fabs(ad * dph);
+                    if (sv) sv[d] += a * fabs(g);
+                }
+            }
+        }
+    }
+    return err;
+}

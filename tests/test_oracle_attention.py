@@ -355,3 +355,91 @@ def test_partial_merge_equals_two_pass_softmax():
             m, l, acc = mm, l * c1 + l2 * c2, acc * c1 + a2 * c2
         assert np.max(np.abs(acc / l - ref["O"][0, 0])) < 1e-13
         assert abs(m + np.log(l) - ref["LSE"][0, 0]) < 1e-13
+
+
+# -------------------------------------------------------- GATv2 backward pins
+
+def torch_gatv2(A, XD, XS, att, slope, V, dO):
+    t = lambda x: torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    xd, xs, a = t(XD), t(XS), t(att)
+    v = xs if V is None else t(V)
+    z = xs[None, :, :, :] + xd[:, None, :, :]                       # [i, j, h, d]
+    s = (torch.nn.functional.leaky_relu(z, slope) * a[None, None]).sum(-1)   # [i, j, h]
+    s = s.masked_fill(~torch.tensor(A)[:, :, None], float("-inf"))
+    alpha = torch.softmax(s, dim=1)
+    O = torch.einsum("ijh,jhd->ihd", alpha, v)
+    O.backward(torch.tensor(dO))
+    return xd.grad.numpy(), xs.grad.numpy(), a.grad.numpy(), (None if V is None else v.grad.numpy())
+
+
+@pytest.mark.parametrize("sep_v", [False, True])
+@pytest.mark.parametrize("seed,n,h,d,slope", [(0, 9, 1, 4, 0.2), (1, 11, 2, 3, 0.05)])
+def test_gatv2_bwd_finite_differences(seed, n, h, d, slope, sep_v):
+    rng, ip, ix = _graph(seed, n, p=0.4)
+    XD, XS, V, dO = _feats(rng, n, h, d, 4)
+    att = rng.standard_normal((h, d))
+    Vx = V if sep_v else None
+    g = oracle.gatv2_bwd(ip, ix, XD, XS, att, dO, V=Vx, slope=slope)
+    eps = 1e-6
+
+    def f(xd, xs, a, v):
+        return float(np.sum(dO * oracle.gatv2_fwd(ip, ix, xd, xs, a, V=v, slope=slope)["O"]))
+
+    args = {"XD": XD, "XS": XS, "att": att, "V": Vx}
+    targets = [("XD", "dXD"), ("XS", "dXS"), ("att", "d_att")] + ([("V", "dV")] if sep_v else [])
+    for name, key in targets:
+        X = args[name]
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            vals = []
+            for sgn in (1, -1):
+                Xp = X.copy()
+                Xp[idx] += sgn * eps
+                a2 = dict(args)
+                a2[name] = Xp
+                vals.append(f(a2["XD"], a2["XS"], a2["att"], a2["V"]))
+            num[idx] = (vals[0] - vals[1]) / (2 * eps)
+        err = np.max(np.abs(num - g[key])) / max(1.0, np.max(np.abs(g[key])))
+        assert err < 1e-7, (name, err)
+
+
+@pytest.mark.parametrize("sep_v", [False, True])
+def test_gatv2_bwd_torch_autograd(sep_v):
+    rng, ip, ix = _graph(50, 30)
+    n, h, d = 30, 2, 8
+    XD, XS, V, dO = _feats(rng, n, h, d, 4)
+    att = rng.standard_normal((h, d)) / np.sqrt(d)
+    g = oracle.gatv2_bwd(ip, ix, XD, XS, att, dO, V=V if sep_v else None, slope=0.2)
+    txd, txs, ta, tv = torch_gatv2(dense_adjacency(ip, ix, n), XD, XS, att, 0.2, V if sep_v else None, dO)
+    assert np.max(np.abs(g["dXD"] - txd)) < 1e-12
+    assert np.max(np.abs(g["dXS"] - txs)) < 1e-12
+    assert np.max(np.abs(g["d_att"] - ta)) < 1e-11
+    if sep_v:
+        assert np.max(np.abs(g["dV"] - tv)) < 1e-12
+
+
+def test_gatv2_bwd_closed_forms_and_subsets():
+    rng, ip, ix = _graph(51, 40)
+    n, h, d = 40, 2, 8
+    XD, XS, V, dO = _feats(rng, n, h, d, 4)
+    att = rng.standard_normal((h, d))
+    # slope 1: scores separate into <a, xs_j> + <a, xd_i>, weights do not depend on xd -> dXD = 0
+    g = oracle.gatv2_bwd(ip, ix, XD, XS, att, dO, V=V, slope=1.0)
+    assert np.max(np.abs(g["dXD"])) < 1e-12
+    # a = 0: uniform weights -> no score gradient; dV_j = sum over destinations of dO_i / deg_i
+    g = oracle.gatv2_bwd(ip, ix, XD, XS, np.zeros_like(att), dO, V=V, slope=0.2)
+    assert np.max(np.abs(g["dXD"])) < 1e-15 and np.max(np.abs(g["dXS"])) < 1e-15
+    deg = np.diff(ip)
+    ref = np.zeros_like(V)
+    for i in range(n):
+        for j in ix[ip[i]:ip[i + 1]]:
+            ref[j] += dO[i] / deg[i]
+    assert np.max(np.abs(g["dV"] - ref)) < 1e-13
+    # subsets reproduce the full result
+    full = oracle.gatv2_bwd(ip, ix, XD, XS, att, dO, slope=0.2)
+    rows = np.array([3, 0, 39])
+    sub = oracle.gatv2_bwd(ip, ix, XD, XS, att, dO, slope=0.2, rows=rows, srcs=rows)
+    for k in ("dXD", "Delta"):
+        assert np.array_equal(sub[k], full[k][rows]), k
+    assert np.array_equal(sub["dXS"], full["dXS"][rows])
+    assert np.array_equal(sub["d_att"], full["d_att"])
