@@ -39,7 +39,7 @@ METRIC = "GEdges/s and achieved HBM GB/s (% of peak) for fused CSR attention fwd
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "gatv2_zipf21_n100k"
 KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_sparse_amd", "csrc", f)
-                  for f in ("attn.hip", "attn_core.h", "attn_tile.hip", "device.h")]
+                  for f in ("attn.hip", "attn_core.h", "attn_tile.hip", "attn_gat.hip", "device.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -120,6 +120,18 @@ def kernel_bytes(kind, c, H, D, s, v_alias=True):
         return 4 * (sr + 1) + 4 * se + (2 * R + 8 * H) * se + 2 * R * sr + 2 * R * sl
     if kind == "gt_bwd_src_merge":
         return 2 * R * sh
+    if kind == "gatv2_bwd_dst_main":  # reads XD, dO, LSE, att; gathers XS (+V); writes dXD, stats, d_att rows
+        return (4 * (rows + 1) + 4 * E + R * E * (1 if v_alias else 2) + (2 * R + 4 * H) * rows + 4 * H * D
+                + (R + 8 * H + 4 * H * D) * nl)
+    if kind == "gatv2_bwd_dst_merge":
+        return (R + 8 * H + 4 * H * D) * nh
+    if kind == "gatv2_bwd_src_main":  # reads XS (+V); gathers XD, dO and stats; writes dXS (+dV)
+        nv = 1 if v_alias else 2
+        return 4 * (sr + 1) + 4 * se + (2 * R + 8 * H) * se + nv * R * sr + nv * R * sl + 4 * H * D
+    if kind == "gatv2_bwd_src_merge":
+        return (1 if v_alias else 2) * R * sh
+    if kind == "gatv2_bwd_datt":      # per-node d_att rows read once
+        return 4 * H * D * c.get("N", 0)
     t, tr, te = c.get("tiles", 0), c.get("tile_rows", 0), c.get("tile_res_edges", 0)
     if kind == "gt_tile_fwd":         # tiles: K, V blocks; rows: Q in, O and LSE out; residual gathers
         return 40 * t + 32 * R * t + 4 * (tr + 1) + (4 + 2 * R) * te + R * tr + (R + 4 * H) * tr
@@ -247,7 +259,7 @@ def summarize(args) -> int:
 
 # ----------------------------------------------------------------- workload
 
-def setup(name, plan_opts):
+def setup(name, plan_opts, backward=None):
     import numpy as np
     import torch
 
@@ -255,7 +267,7 @@ def setup(name, plan_opts):
     import workloads
 
     t0 = time.time()
-    wl = workloads.make(name)
+    wl = workloads.make(name, backward=backward)
     t_gen = time.time() - t0
     n, H, D = wl.n_nodes, wl.heads, wl.dim
     dev = torch.device("cuda:0")
@@ -286,22 +298,32 @@ def setup(name, plan_opts):
     else:
         tensors["XD"], tensors["XS"] = feat("XD"), feat("XS")
         tensors["att"] = torch.from_numpy(wl.att).to(dev)
+        if wl.backward:
+            tensors["dO"] = feat("dO")
     E = int(indices.numel())
     tensors["O"] = torch.empty_like(tensors["Q"] if wl.kind == "gt" else tensors["XD"])
     tensors["LSE"] = torch.empty((n, H), dtype=torch.float32, device=dev)
     if wl.backward:
+        ref = tensors["Q"] if wl.kind == "gt" else tensors["XD"]
         for nm in ("dQ", "dK", "dV"):
-            tensors[nm] = torch.empty_like(tensors["Q"])
+            tensors[nm] = torch.empty_like(ref)
+        tensors["d_att"] = torch.empty((H, D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     prep = dict(generate_s=round(t_gen, 3), csr_build_ms=round(1e3 * t_csr, 3), plan_create_ms=round(1e3 * t_plan, 3))
     return wl, indptr, indices, plan, tensors, E, prep
 
 
 def make_step(g, wl, indptr, indices, plan, T):
-    if wl.kind == "gatv2":
+    if wl.kind == "gatv2" and not wl.backward:
         def step():
             g.gatv2_attn_fwd(plan, indptr, indices, T["XD"], T["XS"], T["att"], negative_slope=0.2, O=T["O"],
                              LSE=T["LSE"])
+    elif wl.kind == "gatv2":
+        def step():
+            g.gatv2_attn_fwd(plan, indptr, indices, T["XD"], T["XS"], T["att"], negative_slope=0.2, O=T["O"],
+                             LSE=T["LSE"])
+            g.gatv2_attn_bwd(plan, indptr, indices, T["XD"], T["XS"], T["att"], T["dO"], T["LSE"],
+                             negative_slope=0.2, dXD=T["dQ"], dXS=T["dK"], d_att=T["d_att"])
     elif not wl.backward:
         def step():
             g.gnn_attn_fwd(plan, indptr, indices, T["Q"], T["K"], T["V"], O=T["O"], LSE=T["LSE"])
@@ -331,6 +353,7 @@ def cpu_baseline(wl, rp, rx, target_s):
         dO = np.asarray(wl.feats["dO"], np.float64) if wl.backward else None
     else:
         XD, XS = (np.asarray(wl.feats[k], np.float64) for k in ("XD", "XS"))
+        dO = np.asarray(wl.feats["dO"], np.float64) if wl.backward else None
     csc = oracle.csc(rp, rx, n) if wl.backward else None
 
     def run(edges):
@@ -339,6 +362,9 @@ def cpu_baseline(wl, rp, rx, target_s):
         t0 = time.perf_counter()
         if wl.kind == "gatv2":
             oracle.gatv2_fwd(rp, rx, XD, XS, wl.att, slope=0.2, rows=rows)
+            if wl.backward:
+                oracle.gatv2_bwd(rp, rx, XD, XS, wl.att, dO, slope=0.2, rows=rows, srcs=rows, csc_arrays=csc,
+                                 want_da=False)
         else:
             oracle.gt_fwd(rp, rx, Q, K, V, rows=rows)
             if wl.backward:
@@ -377,7 +403,7 @@ def bench(args) -> int:
     opts = dict(light_threshold=args.light_threshold, chunk=args.chunk, waves_per_group=args.waves,
                 tile_density=args.tile_density)
     log(f"[bench] workload {args.workload}: generating and building the graph")
-    wl, indptr, indices, plan, T, E, prep = setup(args.workload, opts)
+    wl, indptr, indices, plan, T, E, prep = setup(args.workload, opts, True if args.backward else None)
     info = g.gnn_plan_export(plan)
     N, H, D = wl.n_nodes, wl.heads, wl.dim
     s = 4 if wl.dtype == "f32" else 2
@@ -444,8 +470,8 @@ def bench(args) -> int:
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "pass": "GATv2 forward" if wl.kind == "gatv2" else
-                    ("GT forward + LSE-recompute backward" if wl.backward else "GT forward"),
+            "pass": ("GATv2" if wl.kind == "gatv2" else "GT") + (" forward + LSE-recompute backward"
+                                                                  if wl.backward else " forward"),
             "n_nodes": N, "n_edges": E, "heads": H, "dim": D,
             "storage": wl.dtype, "math": "f32",
             "light_threshold": args.light_threshold, "chunk": args.chunk, "waves_per_group": args.waves,
@@ -506,6 +532,8 @@ def main():
     ap.add_argument("--tile-density", type=float, default=0.0,
                     help="16x16 tile threshold tau (0 disables the tile path)")
     ap.add_argument("--flush", action="store_true", help="flush caches with a 512 MiB write between steps")
+    ap.add_argument("--backward", action="store_true",
+                    help="add the LSE-recompute backward to the step (seeded upstream gradient)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true")

@@ -213,6 +213,26 @@ int gatv2_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indice
                    hipStream_t stream);
 
 /*
+ * GATv2 attention backward from the cached LSE (the forward's LSE for the same
+ * inputs; weights recomputed per edge as p_ij = exp(s_ij - LSE_i), as for the
+ * Graph Transformer). With z = K[j] + Q[i], phi = LeakyReLU(negative_slope),
+ * dp_ij = <dO_i, V_j>, Delta_i = sum_j p_ij dp_ij, ds_ij = p_ij (dp_ij - Delta_i):
+ *   dQ_i   = sum_j ds_ij att * phi'(z_ij)           (destination projection XD)
+ *   dK_j   = sum_i ds_ij att * phi'(z_ij)           (source projection XS)
+ *            + sum_i p_ij dO_i  when V is the same buffer as K
+ *   dV_j   = sum_i p_ij dO_i    when V is a separate buffer (dV may be NULL otherwise)
+ *   d_att  = sum over all edges of ds_ij phi(z_ij)  (fp32 [H, D], overwritten)
+ * phi'(z) = 1 for z >= 0 and negative_slope otherwise (the forward's branch).
+ * The plan must have been created with want_csc. No atomics: d_att is a
+ * fixed-order sum and every output is bitwise reproducible. The plan
+ * workspace grows by N*H*D fp32 for the per-node d_att rows.
+ */
+int gatv2_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
+                   int32_t H, int32_t D, const void *Q, const void *K, const void *V, const float *att,
+                   float negative_slope, const void *dO, const float *LSE, void *dQ, void *dK,
+                   void *dV /*nullable when V == K*/, float *d_att, gnn_dtype_t dtype, hipStream_t stream);
+
+/*
  * Per-kernel timing on a plan (for measurement tools). When enabled, every
  * attention call on the plan records HIP events around each kernel it
  * launches, on the call's stream. gnn_plan_timing_read synchronises on the

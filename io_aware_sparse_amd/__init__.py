@@ -10,7 +10,7 @@ fallback path, and calls fail loudly when the library is missing.
 
 Function names match the C ABI: gnn_csr_build, gnn_plan_create,
 gnn_plan_export, gnn_plan_destroy, gnn_attn_fwd, gnn_attn_bwd,
-gatv2_attn_fwd, gnn_plan_set_timing, gnn_plan_timing_read,
+gatv2_attn_fwd, gatv2_attn_bwd, gnn_plan_set_timing, gnn_plan_timing_read,
 gnn_status_string.
 """
 from __future__ import annotations
@@ -29,8 +29,8 @@ STATUS = {0: "GNN_OK", -1: "GNN_ERR_INVALID_ARG", -2: "GNN_ERR_UNSUPPORTED", -3:
 
 # exported symbols, in the order include/gnn_attn.h declares them
 EXPORTS = ["gnn_plan_opts_default", "gnn_csr_build", "gnn_plan_create", "gnn_plan_export", "gnn_plan_destroy",
-           "gnn_attn_fwd", "gnn_attn_bwd", "gatv2_attn_fwd", "gnn_plan_set_timing", "gnn_plan_timing_read",
-           "gnn_status_string"]
+           "gnn_attn_fwd", "gnn_attn_bwd", "gatv2_attn_fwd", "gatv2_attn_bwd", "gnn_plan_set_timing",
+           "gnn_plan_timing_read", "gnn_status_string"]
 
 
 class GnnError(RuntimeError):
@@ -91,6 +91,7 @@ def lib():
         L.gnn_attn_fwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, V, F, C.c_int, V]
         L.gnn_attn_bwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, V, V, V, V, V, F, C.c_int, V]
         L.gatv2_attn_fwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, F, V, V, C.c_int, V]
+        L.gatv2_attn_bwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, F, V, V, V, V, V, V, C.c_int, V]
         L.gnn_plan_set_timing.argtypes = [V, I32]
         L.gnn_plan_timing_read.argtypes = [V, I32, C.POINTER(C.c_char_p), C.POINTER(C.c_int32),
                                            C.POINTER(C.c_double), C.POINTER(C.c_int32)]
@@ -336,6 +337,36 @@ def gnn_attn_bwd(plan: Plan, indptr, indices, Q, K, V, O, dO, LSE, dQ=None, dK=N
                               _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
                               float(scale), _dtype_code(Q), _stream(stream)), "gnn_attn_bwd")
     return dQ, dK, dV
+
+
+def gatv2_attn_bwd(plan: Plan, indptr, indices, XD, XS, att, dO, LSE, V=None, negative_slope: float = 0.2,
+                   dXD=None, dXS=None, dV=None, d_att=None, stream=None):
+    """GATv2 attention backward from the cached LSE. Returns (dXD, dXS, dV or
+    None, d_att); with V None (V is XS) dXS includes the value gradient."""
+    torch = _torch()
+    n, e = _graph(indptr, indices)
+    _feat(XD, "XD")
+    N, H, D = XD.shape
+    _feat(XS, "XS", XD.shape, XD.dtype)
+    _feat(dO, "dO", XD.shape, XD.dtype)
+    sep = V is not None and V.data_ptr() != XS.data_ptr()
+    Vt = _feat(V, "V", XD.shape, XD.dtype) if sep else XS
+    if not (att.is_cuda and att.dtype == torch.float32 and att.is_contiguous() and tuple(att.shape) == (H, D)):
+        raise TypeError("att must be a contiguous float32 [H, D] device tensor")
+    if not (LSE.is_cuda and LSE.dtype == torch.float32 and tuple(LSE.shape) == (N, H) and LSE.is_contiguous()):
+        raise TypeError("LSE must be a contiguous float32 [N, H] device tensor")
+    dXD = torch.empty_like(XD) if dXD is None else _feat(dXD, "dXD", XD.shape, XD.dtype)
+    dXS = torch.empty_like(XD) if dXS is None else _feat(dXS, "dXS", XD.shape, XD.dtype)
+    if sep:
+        dV = torch.empty_like(XD) if dV is None else _feat(dV, "dV", XD.shape, XD.dtype)
+    else:
+        dV = None
+    d_att = torch.empty((H, D), dtype=torch.float32, device=XD.device) if d_att is None else d_att
+    _check(lib().gatv2_attn_bwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
+                                _ptr(XD), _ptr(XS), _ptr(Vt), _ptr(att), float(negative_slope), _ptr(dO), _ptr(LSE),
+                                _ptr(dXD), _ptr(dXS), _ptr(dV), _ptr(d_att), _dtype_code(XD), _stream(stream)),
+           "gatv2_attn_bwd")
+    return dXD, dXS, dV, d_att
 
 
 def gnn_plan_set_timing(plan: Plan, enable: bool = True):

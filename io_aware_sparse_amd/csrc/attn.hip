@@ -262,46 +262,6 @@ __global__ __launch_bounds__(256) void k_bwd_src_merge(BwdParams P) {
 // host side
 // ======================================================================
 
-static int ilog2(int x) {
-    int s = 0;
-    while ((1 << s) < x) ++s;
-    return s;
-}
-
-// lanes per head for (dtype, D); 0 if unsupported
-static int lanes_per_head(gnn_dtype_t dt, int D) {
-    if (!(D == 16 || D == 32 || D == 64 || D == 128)) return 0;
-    if (dt == GNN_F32) return D / 4;
-    if (dt == GNN_BF16) return D / 8;
-    return 0;
-}
-
-static Geom make_geom(int N, int H, int D, int LH) {
-    Geom g;
-    g.N = N;
-    g.H = H;
-    g.D = D;
-    g.HW = std::min(H, kWave / LH);
-    g.NHG = (H + g.HW - 1) / g.HW;
-    g.lr_shift = ilog2(g.HW * LH);
-    g.G = kWave >> g.lr_shift;
-    return g;
-}
-
-static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-
-static int check_common(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
-                        int32_t H, int32_t D, gnn_dtype_t dtype) {
-    if (N < 0 || E < 0 || E >= (1ll << 31) || H < 1 || !indptr) return GNN_ERR_INVALID_ARG;
-    if (E > 0 && !indices) return GNN_ERR_INVALID_ARG;
-    if (dtype != GNN_F32 && dtype != GNN_BF16) return GNN_ERR_UNSUPPORTED;
-    if (!lanes_per_head(dtype, D)) return GNN_ERR_UNSUPPORTED;
-    if ((int64_t)N * H * D >= (1ll << 40)) return GNN_ERR_INVALID_ARG;
-    if (plan && (plan->n_nodes != N || plan->n_edges != E || plan->indptr != indptr || plan->indices != indices))
-        return GNN_ERR_INVALID_ARG;
-    return GNN_OK;
-}
-
 template <class T, int LH, int MODE>
 static int run_fwd(gnn_plan_t plan, FwdParams &P, hipStream_t s) {
     constexpr int U = 4;
@@ -466,39 +426,7 @@ int gnn_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices,
     if (N == 0) return GNN_OK;
     const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
     BwdParams P{};
-    const int LH = lanes_per_head(dtype, D);
-    P.g = make_geom(N, H, D, LH);
-    P.indptr = indptr;
-    P.indices = indices;
-    P.cindptr = as<int32_t>(plan->cindptr);
-    P.cindices = as<int32_t>(plan->cindices);
-    P.Q = Q;
-    P.K = K;
-    P.V = V;
-    P.O = O;
-    P.dO = dO;
-    P.LSE = LSE;
-    P.dQ = dQ;
-    P.dK = dK;
-    P.dV = dV;
-    P.mul = sc * kLog2e;
-    P.scale = sc;
-    P.a_light = as<int32_t>(plan->fwd.light);
-    P.a_groups = as<int32_t>(plan->fwd.groups);
-    P.a_heavy = as<int32_t>(plan->fwd.heavy);
-    P.a_ofs = as<int32_t>(plan->fwd.partial_ofs);
-    P.a_n_light = plan->fwd.n_light;
-    P.a_n_groups = plan->fwd.n_groups;
-    P.a_n_heavy = plan->fwd.n_heavy;
-    P.b_light = as<int32_t>(plan->bwd.light);
-    P.b_groups = as<int32_t>(plan->bwd.groups);
-    P.b_heavy = as<int32_t>(plan->bwd.heavy);
-    P.b_ofs = as<int32_t>(plan->bwd.partial_ofs);
-    P.b_n_light = plan->bwd.n_light;
-    P.b_n_groups = plan->bwd.n_groups;
-    P.b_n_heavy = plan->bwd.n_heavy;
-    P.C = plan->opts.chunk;
-    P.W = plan->opts.waves_per_group;
+    fill_bwd_params(plan, P, indptr, indices, N, H, D, Q, K, V, dO, LSE, dQ, dK, dV, sc, dtype);
     const size_t rowlen = (size_t)H * D;
     const size_t n_stat = (size_t)N * H * 2;
     const size_t n_a = (size_t)P.a_n_groups * (2 * rowlen + H), n_b = (size_t)P.b_n_groups * 2 * rowlen;

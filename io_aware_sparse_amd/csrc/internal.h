@@ -65,6 +65,11 @@ enum KernelKind {
     K_TILE_FWD,
     K_TILE_BWD_DST,
     K_TILE_BWD_SRC,
+    K_GAT_BWD_DST_MAIN,
+    K_GAT_BWD_DST_MERGE,
+    K_GAT_BWD_SRC_MAIN,
+    K_GAT_BWD_SRC_MERGE,
+    K_GAT_DATT,
     K_NUM_KINDS
 };
 extern const char *kKernelNames[K_NUM_KINDS];

@@ -58,6 +58,7 @@ def test_host_validation(g):
     assert L.gatv2_attn_fwd(None, A, A, 10, 20, 2, 32, A, A, A, None, 0.2, A, None, 0, None) == -1
     # backward needs a plan
     assert L.gnn_attn_bwd(None, A, A, 10, 20, 2, 32, A, A, A, A, A, A, A, A, A, 0.0, 0, None) == -1
+    assert L.gatv2_attn_bwd(None, A, A, 10, 20, 2, 32, A, A, A, A, 0.2, A, A, A, A, None, A, 0, None) == -1
     # CSR build
     e = C.c_int64()
     assert L.gnn_csr_build(A, A, 5, -1, 1, A, A, 10, C.byref(e), None) == -1

@@ -230,3 +230,43 @@ def test_gpu_identities(g):
     sdv = (dv.double().sum(0) - go.double().sum(0)).abs()
     assert torch.all(sdk <= 1e-4 * dk.double().abs().sum(0) + 1e-6)
     assert torch.all(sdv <= 1e-4 * dv.double().abs().sum(0) + 1e-6)
+
+
+@pytest.mark.parametrize("dtype,D,H", [("f32", 16, 8), ("f32", 32, 2), ("f32", 128, 1), ("bf16", 16, 8),
+                                       ("bf16", 64, 4), ("bf16", 32, 3)])
+@pytest.mark.parametrize("plan", ["light", "heavy", "mixed", "mixed_w8"])
+@pytest.mark.parametrize("sep_v", [False, True])
+def test_gatv2_bwd_parity(g, dtype, D, H, plan, sep_v):
+    import torch
+    n = 2500
+    say("gatv2_bwd", dtype, D, H, plan, sep_v)
+    ip, ix, rp, rx = _graph(g, 12, n, self_loops=(plan != "mixed"))
+    rng = np.random.default_rng(7 * D + H)
+    XD, XS, V, dO = rand_feats(rng, n, H, D, dtype, k=4)
+    att = (rng.standard_normal((H, D)) / np.sqrt(D)).astype(np.float32)
+    pl = _plan(g, ip, ix, plan, want_csc=True)
+    xd, xs, v, go = (dev_feat(x, dtype) for x in (XD, XS, V, dO))
+    a = torch.from_numpy(att).cuda()
+    O, L = g.gatv2_attn_fwd(pl, ip, ix, xd, xs, a, V=v if sep_v else None)
+    gxd, gxs, gv, gda = g.gatv2_attn_bwd(pl, ip, ix, xd, xs, a, go, L, V=v if sep_v else None)
+    ref = oracle.gatv2_bwd(rp, rx, XD, XS, att, dO, V=V if sep_v else None, slope=0.2)
+    _check("dXD", host(gxd), ref["dXD"], ref["SdXD"], dtype)
+    _check("dXS", host(gxs), ref["dXS"], ref["SdXS"], dtype)
+    if sep_v:
+        _check("dV", host(gv), ref["dV"], ref["SdV"], dtype)
+    _check("d_att", gda.cpu().numpy(), ref["d_att"], ref["Sd_att"], dtype)
+
+
+def test_gatv2_bwd_deterministic(g):
+    import torch
+    n, H, D, dtype = 3000, 8, 16, "f32"
+    ip, ix, rp, rx = _graph(g, 13, n)
+    rng = np.random.default_rng(13)
+    xd, xs, go = (dev_feat(x, dtype) for x in rand_feats(rng, n, H, D, dtype, k=3))
+    a = torch.from_numpy((rng.standard_normal((H, D)) / 4).astype(np.float32)).cuda()
+    pl = _plan(g, ip, ix, "mixed", want_csc=True)
+    O, L = g.gatv2_attn_fwd(pl, ip, ix, xd, xs, a)
+    r1 = [t.clone() for t in g.gatv2_attn_bwd(pl, ip, ix, xd, xs, a, go, L) if t is not None]
+    r2 = [t.clone() for t in g.gatv2_attn_bwd(pl, ip, ix, xd, xs, a, go, L) if t is not None]
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)

@@ -103,7 +103,7 @@ def test_full_size(g, name):
     go = _dev(wl, "dO")
     dq, dk, dv = g.gnn_attn_bwd(plan, ip, ix, q, k, v, O, go, L)
     torch.cuda.synchronize()
-    srcs = _sample(rng, n, d["c_heavy"], N_SAMPLE // 4)
+    srcs = _sample(rng, n, ref_c["heavy"], N_SAMPLE // 4)
     dO = np.asarray(wl.feats["dO"], np.float64)
     rb = oracle.gt_bwd(rp, rx, Q, K, V, dO, rows=rows, srcs=srcs, csc_arrays=(cip, cix))
     _check("dQ", _host(dq)[rows], rb["dQ"], rb["SdQ"], wl.dtype)
@@ -115,3 +115,31 @@ def test_full_size(g, name):
     say(f"  |sum dK| max {sdk.max().item():.3e}, |sum dV - sum dO| max {sdv.max().item():.3e}")
     assert torch.all(sdk <= 2e-2 * dk.double().abs().sum(0) + 1e-3)
     assert torch.all(sdv <= 2e-2 * dv.double().abs().sum(0) + 1e-3)
+
+
+def test_full_size_gatv2_backward(g):
+    """GATv2 forward + backward on the Zipf(2.1) graph (N = 100,000,
+    E = 5.1M, H = 8, D = 16, fp32) with a seeded upstream gradient."""
+    import torch
+    name = "gatv2_zipf21_n100k"
+    say("full-size backward", name)
+    wl = workloads.make(name, backward=True)
+    n = wl.n_nodes
+    ip, ix = g.gnn_csr_build(torch.from_numpy(wl.src).cuda(), torch.from_numpy(wl.dst).cuda(), n)
+    rp, rx = oracle.csr_build(wl.src, wl.dst, n)
+    assert np.array_equal(ip.cpu().numpy(), rp) and np.array_equal(ix.cpu().numpy(), rx)
+    plan = g.gnn_plan_create(ip, ix, want_csc=True)
+    cip, cix = oracle.csc(rp, rx, n)
+    xd, xs, go = _dev(wl, "XD"), _dev(wl, "XS"), _dev(wl, "dO")
+    att = torch.from_numpy(wl.att).cuda()
+    O, L = g.gatv2_attn_fwd(plan, ip, ix, xd, xs, att)
+    gxd, gxs, _, gda = g.gatv2_attn_bwd(plan, ip, ix, xd, xs, att, go, L)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(78)
+    rows = _sample(rng, n, oracle.bucketing(rp, 512, 512, 4)["heavy"], N_SAMPLE)
+    srcs = _sample(rng, n, oracle.bucketing(cip, 512, 512, 4)["heavy"], N_SAMPLE // 4)
+    ref = oracle.gatv2_bwd(rp, rx, wl.feats["XD"], wl.feats["XS"], wl.att, wl.feats["dO"], slope=0.2, rows=rows,
+                           srcs=srcs, csc_arrays=(cip, cix))
+    _check("dXD", _host(gxd)[rows], ref["dXD"], ref["SdXD"], "f32")
+    _check("dXS", _host(gxs)[srcs], ref["dXS"], ref["SdXS"], "f32")
+    _check("d_att", gda.cpu().numpy(), ref["d_att"], ref["Sd_att"], "f32")

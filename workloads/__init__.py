@@ -359,10 +359,14 @@ def _graph(name, n, ss):
     return src.astype(np.int32), dst.astype(np.int32), meta
 
 
-def make(name: str, n_nodes: Optional[int] = None, features: bool = True) -> Workload:
+def make(name: str, n_nodes: Optional[int] = None, features: bool = True,
+         backward: Optional[bool] = None) -> Workload:
     """Build workload `name` (see module doc). `n_nodes` scales the graph down
-    with the same recipe (edge budgets, hub caps and w_max scale with n)."""
-    spec = SPECS[name]
+    with the same recipe (edge budgets, hub caps and w_max scale with n).
+    `backward` overrides whether an upstream gradient dO is drawn."""
+    spec = dict(SPECS[name])
+    if backward is not None:
+        spec["backward"] = bool(backward)
     n = int(n_nodes or spec["n"])
     root = np.random.SeedSequence([spec["seed"], n])
     g_ss, f_ss = root.spawn(2)
@@ -380,13 +384,14 @@ def add_features(wl: Workload, f_ss: Optional[np.random.SeedSequence] = None) ->
         f_ss = np.random.SeedSequence([wl.seed, wl.n_nodes]).spawn(2)[1]
     shape = (wl.n_nodes, wl.heads, wl.dim)
     names = ["Q", "K", "V"] if wl.kind == "gt" else ["XD", "XS"]
+    kids = f_ss.spawn(len(names) + 2)
     if wl.backward:
         names.append("dO")
-    kids = f_ss.spawn(len(names) + 1)
-    for nm, k in zip(names, kids):
+    # the gradient stream is the last child so adding it leaves the others unchanged
+    for nm, k in zip(names, list(kids[:len(names) - wl.backward]) + ([kids[-1]] if wl.backward else [])):
         if wl.dtype == "bf16":
             wl.bits[nm], wl.feats[nm] = normal_f32(k, shape, bf16=True)
         else:
             wl.feats[nm] = normal_f32(k, shape)
     if wl.kind == "gatv2":
-        wl.att = normal_f32(kids[-1], (wl.heads, wl.dim), std=1.0 / np.sqrt(wl.dim))
+        wl.att = normal_f32(kids[-2], (wl.heads, wl.dim), std=1.0 / np.sqrt(wl.dim))
