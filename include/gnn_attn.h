@@ -79,6 +79,8 @@ typedef struct {
                                 <= 0 disables the tile path; default 0                         */
     int32_t want_csc;        /* build the transposed adjacency and its out-degree buckets,
                                 needed by gnn_attn_bwd; default 0                               */
+    int32_t sched_order;     /* launch order of light nodes: 1 = descending degree (longest
+                                first, default), 0 = ascending id; outputs do not depend on it  */
 } gnn_plan_opts;
 
 /* Fill *opts with the defaults above. Returns GNN_ERR_INVALID_ARG if opts is NULL. */
@@ -156,6 +158,8 @@ typedef struct {
     const int32_t *rcindices;   /* [n_residual]                                          */
     const int32_t *c_light_nt;  /* [n_c_light_nt] light sources outside tiled column blocks */
     /* device memory owned by the plan */
+    const int32_t *light_sched;   /* [n_light]   launch order of the light nodes          */
+    const int32_t *c_light_sched; /* [c_n_light] launch order of the light sources        */
     int64_t structure_bytes;    /* buckets, transposed adjacency, tiles                 */
     int64_t workspace_bytes;    /* heavy partials and backward statistics (grows lazily) */
     int64_t largest_workspace_alloc;

@@ -41,7 +41,7 @@ class GnnError(RuntimeError):
 
 class PlanOpts(C.Structure):
     _fields_ = [("light_threshold", C.c_int32), ("chunk", C.c_int32), ("waves_per_group", C.c_int32),
-                ("tile_density", C.c_float), ("want_csc", C.c_int32)]
+                ("tile_density", C.c_float), ("want_csc", C.c_int32), ("sched_order", C.c_int32)]
 
 
 _P32 = C.POINTER(C.c_int32)
@@ -63,7 +63,7 @@ class PlanInfo(C.Structure):
                 ("n_trb", C.c_int32), ("n_light_nt", C.c_int32), ("n_tcb", C.c_int32), ("n_c_light_nt", C.c_int32),
                 ("trb", C.c_void_p), ("light_nt", C.c_void_p), ("ctile", C.c_void_p), ("ctile_ptr", C.c_void_p),
                 ("tcb", C.c_void_p), ("rcindptr", C.c_void_p), ("rcindices", C.c_void_p),
-                ("c_light_nt", C.c_void_p),
+                ("c_light_nt", C.c_void_p), ("light_sched", C.c_void_p), ("c_light_sched", C.c_void_p),
                 ("structure_bytes", C.c_int64), ("workspace_bytes", C.c_int64),
                 ("largest_workspace_alloc", C.c_int64)]
 
@@ -201,12 +201,12 @@ class Plan:
 
 
 def gnn_plan_create(indptr, indices, light_threshold: int = 512, chunk: int = 512, waves_per_group: int = 4,
-                    tile_density: float = 0.0, want_csc: bool = False, stream=None) -> Plan:
+                    tile_density: float = 0.0, want_csc: bool = False, sched_order: int = 1, stream=None) -> Plan:
     n, e = _graph(indptr, indices)
     o = PlanOpts()
     lib().gnn_plan_opts_default(C.byref(o))
     o.light_threshold, o.chunk, o.waves_per_group = int(light_threshold), int(chunk), int(waves_per_group)
-    o.tile_density, o.want_csc = float(tile_density), int(bool(want_csc))
+    o.tile_density, o.want_csc, o.sched_order = float(tile_density), int(bool(want_csc)), int(sched_order)
     h = C.c_void_p()
     _check(lib().gnn_plan_create(_ptr(indptr), _ptr(indices) if e else None, n, e, C.byref(o), _stream(stream),
                                  C.byref(h)), "gnn_plan_create")
@@ -246,6 +246,7 @@ def gnn_plan_export(plan: Plan, arrays: bool = False) -> dict:
         d["heavy"] = _copy_dev(info.heavy_ids, info.n_heavy, np.int32)
         d["groups"] = _copy_dev(info.groups, 3 * info.n_groups, np.int32).reshape(-1, 3)
         d["partial_ofs"] = _copy_dev(info.partial_ofs, info.n_heavy + 1, np.int32)
+        d["light_sched"] = _copy_dev(info.light_sched, info.n_light, np.int32)
         if info.has_csc:
             d["cindptr"] = _copy_dev(info.cindptr, n + 1, np.int32)
             d["cindices"] = _copy_dev(info.cindices, info.n_edges, np.int32)
@@ -253,6 +254,7 @@ def gnn_plan_export(plan: Plan, arrays: bool = False) -> dict:
             d["c_heavy"] = _copy_dev(info.c_heavy_ids, info.c_n_heavy, np.int32)
             d["c_groups"] = _copy_dev(info.c_groups, 3 * info.c_n_groups, np.int32).reshape(-1, 3)
             d["c_partial_ofs"] = _copy_dev(info.c_partial_ofs, info.c_n_heavy + 1, np.int32)
+            d["c_light_sched"] = _copy_dev(info.c_light_sched, info.c_n_light, np.int32)
         if info.has_tiles:
             d["tile_rc"] = _copy_dev(info.tile_rc, 2 * info.n_tiles, np.int32).reshape(-1, 2)
             d["tile_mask"] = _copy_dev(info.tile_mask, 4 * info.n_tiles, np.uint64).reshape(-1, 4)

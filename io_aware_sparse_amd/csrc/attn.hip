@@ -83,16 +83,19 @@ __global__ __launch_bounds__(512) void k_fwd_main(FwdParams P) {
     write_out<T, NV>(P, lp, node, st);
 }
 
-// Second pass: one wave per (heavy node, head group) merges the node's
-// partials in a fixed order (group-strided, then a fixed xor tree).
+// Second pass: one 4-wave workgroup per (heavy node, head group) merges the
+// node's partials in a fixed order: wave w takes partials p0 + w*G + g
+// (stride 4G), merges them in sequence, the wave's groups merge by a fixed
+// xor tree, and wave 0 merges the four wave states in ascending order.
+constexpr int kMergeWaves = 4;
+
 template <class T, int LH>
 __global__ __launch_bounds__(256) void k_fwd_merge(FwdParams P) {
     using VT = Vec<T>;
     constexpr int NV = VT::N;
+    __shared__ float red[kMergeWaves][kWave][NV + 2];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t item = (int64_t)blockIdx.x * (blockDim.x / kWave) + w;
-    if (item >= (int64_t)P.n_heavy * P.g.NHG) return;
-    const int k = (int)(item / P.g.NHG), hg = (int)(item % P.g.NHG);
+    const int k = (int)(blockIdx.x / P.g.NHG), hg = (int)(blockIdx.x % P.g.NHG);
     const int node = P.heavy[k];
     const int p0 = P.partial_ofs[k], p1 = P.partial_ofs[k + 1];
     const LanePos lp = lane_pos<LH, NV>(P.g, hg);
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void k_fwd_merge(FwdParams P) {
 #pragma unroll
     for (int q = 0; q < NV; ++q) st.acc[q] = 0.f;
     if (lp.act) {
-        for (int p = p0 + lp.g; p < p1; p += P.g.G) {
+        for (int p = p0 + w * P.g.G + lp.g; p < p1; p += kMergeWaves * P.g.G) {
             float a2[NV];
 #pragma unroll
             for (int q = 0; q < NV; ++q) a2[q] = P.ws_acc[(int64_t)p * rowlen + lp.col + q];
@@ -111,6 +114,18 @@ __global__ __launch_bounds__(256) void k_fwd_merge(FwdParams P) {
         }
     }
     merge_groups(st, P.g.lr_shift);
+    red[w][lp.lane][0] = st.m;
+    red[w][lp.lane][1] = st.l;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) red[w][lp.lane][2 + q] = st.acc[q];
+    __syncthreads();
+    if (w != 0) return;
+    for (int v = 1; v < kMergeWaves; ++v) {
+        float a2[NV];
+#pragma unroll
+        for (int q = 0; q < NV; ++q) a2[q] = red[v][lp.lane][2 + q];
+        merge_state(st, red[v][lp.lane][0], red[v][lp.lane][1], a2);
+    }
     write_out<T, NV>(P, lp, node, st);
 }
 
@@ -274,8 +289,8 @@ static int run_fwd(gnn_plan_t plan, FwdParams &P, hipStream_t s) {
     const size_t lds = P.n_groups ? (size_t)P.W * (1 << P.g.lr_shift) * (NV + 2) * sizeof(float) : 0;
     GNN_TRY(launch(plan, kind_main, k_fwd_main<T, LH, MODE, U>, dim3((unsigned)blocks), dim3(64 * P.W), lds, s, P));
     if (P.n_heavy) {
-        const int64_t mb = ((int64_t)P.n_heavy * P.g.NHG + 3) / 4;
-        GNN_TRY(launch(plan, kind_merge, k_fwd_merge<T, LH>, dim3((unsigned)mb), dim3(256), 0, s, P));
+        const int64_t mb = (int64_t)P.n_heavy * P.g.NHG;
+        GNN_TRY(launch(plan, kind_merge, k_fwd_merge<T, LH>, dim3((unsigned)mb), dim3(64 * kMergeWaves), 0, s, P));
     }
     return GNN_OK;
 }
@@ -323,7 +338,7 @@ static int fwd_common(gnn_plan_t plan, const int32_t *indptr, const int32_t *ind
     P.slope = slope;
     P.mul = mul;
     if (plan) {
-        P.light = as<int32_t>(plan->fwd.light);
+        P.light = as<int32_t>(plan->fwd.sched);
         P.n_light = plan->fwd.n_light;
         P.groups = as<int32_t>(plan->fwd.groups);
         P.n_groups = plan->fwd.n_groups;

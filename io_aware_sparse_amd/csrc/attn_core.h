@@ -462,14 +462,14 @@ static inline void fill_bwd_params(gnn_plan_t plan, BwdParams &P, const int32_t 
     P.dV = dV;
     P.mul = sc * kLog2e;
     P.scale = sc;
-    P.a_light = as<int32_t>(plan->fwd.light);
+    P.a_light = as<int32_t>(plan->fwd.sched);
     P.a_groups = as<int32_t>(plan->fwd.groups);
     P.a_heavy = as<int32_t>(plan->fwd.heavy);
     P.a_ofs = as<int32_t>(plan->fwd.partial_ofs);
     P.a_n_light = plan->fwd.n_light;
     P.a_n_groups = plan->fwd.n_groups;
     P.a_n_heavy = plan->fwd.n_heavy;
-    P.b_light = as<int32_t>(plan->bwd.light);
+    P.b_light = as<int32_t>(plan->bwd.sched);
     P.b_groups = as<int32_t>(plan->bwd.groups);
     P.b_heavy = as<int32_t>(plan->bwd.heavy);
     P.b_ofs = as<int32_t>(plan->bwd.partial_ofs);

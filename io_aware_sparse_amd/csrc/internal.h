@@ -45,6 +45,10 @@ T *as(const DevBuf &b) { return reinterpret_cast<T *>(b.p); }
 struct Buckets {
     int32_t n_light = 0, n_heavy = 0, n_groups = 0;
     DevBuf light, heavy, groups, partial_ofs;
+    // launch order of the light list (descending degree, ties by ascending id,
+    // when the plan asks for it, else a copy of the light list); the results
+    // of every kernel are independent of the order
+    DevBuf sched;
 };
 
 // Per-kernel timing log.
@@ -134,8 +138,8 @@ int emit_structure(uint64_t *keys, int64_t n, int nb, int dedupe, int32_t n_rows
 int build_transpose(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, DevBuf &cindptr,
                     DevBuf &cindices, hipStream_t s);
 // bucket a CSR-like structure
-int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_t W, Buckets &b,
-                  hipStream_t s);
+int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_t W, int32_t sched_order,
+                  Buckets &b, hipStream_t s);
 // 16x16 tile census of the plan's graph (fills the plan's tile arrays)
 int build_tiles(gnn_plan_s *p, int32_t min_nnz, hipStream_t s);
 }  // namespace gnn

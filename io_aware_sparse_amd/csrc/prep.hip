@@ -426,8 +426,51 @@ __global__ void k_bucket_emit(const int32_t *indptr, int32_t n, int32_t T, int64
     }
 }
 
-int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_t W, Buckets &b,
-                  hipStream_t s) {
+__global__ void k_sched_keys(const int32_t *indptr, const int32_t *light, int32_t n_light, int64_t cap,
+                             uint64_t *keys) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n_light) return;
+    const int32_t v = light[k];
+    const int64_t deg = (int64_t)indptr[v + 1] - indptr[v];
+    keys[k] = ((uint64_t)(cap - deg) << 32) | (uint32_t)v;
+}
+
+__global__ void k_low32_i32(const uint64_t *keys, int64_t n, int32_t *out) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k < n) out[k] = (int32_t)(keys[k] & 0xFFFFFFFFull);
+}
+
+// light launch order: descending degree, ties by ascending id
+static int build_sched(const int32_t *indptr, int32_t T, int64_t max_deg, int32_t sched_order, Buckets &b,
+                       hipStream_t s) {
+    GNN_TRY(dev_alloc(b.sched, (size_t)std::max(1, b.n_light) * 4));
+    if (b.n_light == 0) return GNN_OK;
+    if (!sched_order) {
+        GNN_HIP(hipMemcpyAsync(b.sched.p, b.light.p, (size_t)b.n_light * 4, hipMemcpyDeviceToDevice, s));
+        return GNN_OK;
+    }
+    const int64_t cap = std::min<int64_t>(T, max_deg);
+    const int64_t m = b.n_light;
+    const int64_t ss = sort_scratch(m) + 2;
+    DevBuf tmp;
+    GNN_TRY(dev_alloc(tmp, (size_t)(16 * m + 4 * ss + 64)));
+    uint64_t *keys = as<uint64_t>(tmp), *kt = keys + m;
+    int32_t *scr = reinterpret_cast<int32_t *>(kt + m);
+    hipLaunchKernelGGL(k_sched_keys, grid1d(m), dim3(256), 0, s, indptr, as<int32_t>(b.light), b.n_light, cap, keys);
+    int rc = radix_sort(keys, kt, m, 32 + bits_for(cap + 2), scr, s);
+    if (rc == GNN_OK) {
+        hipLaunchKernelGGL(k_low32_i32, grid1d(m), dim3(256), 0, s, keys, m, as<int32_t>(b.sched));
+        if (hipStreamSynchronize(s) != hipSuccess) {
+            set_hip_error(hipGetLastError(), "light schedule");
+            rc = GNN_ERR_HIP;
+        }
+    }
+    dev_free(tmp);
+    return rc;
+}
+
+int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_t W, int32_t sched_order,
+                  Buckets &b, hipStream_t s) {
     const int64_t span = (int64_t)C * W;
     DevBuf tmp;
     const int64_t sc = scan_scratch(n);
@@ -463,6 +506,17 @@ int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_
     if (hipStreamSynchronize(s) != hipSuccess || hipGetLastError() != hipSuccess) {
         set_hip_error(hipErrorUnknown, "bucket emit");
         rc = GNN_ERR_HIP;
+        goto done;
+    }
+    {
+        int32_t ends[2] = {0, 0};
+        if (n > 0 && (hipMemcpy(&ends[0], indptr, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+                      hipMemcpy(&ends[1], indptr + n, 4, hipMemcpyDeviceToHost) != hipSuccess)) {
+            set_hip_error(hipGetLastError(), "bucket schedule");
+            rc = GNN_ERR_HIP;
+            goto done;
+        }
+        rc = build_sched(indptr, T, (int64_t)ends[1] - ends[0], sched_order, b, s);
     }
 done:
     dev_free(tmp);
@@ -513,8 +567,8 @@ using namespace gnn;
 
 int64_t gnn_plan_s::structure_bytes() const {
     int64_t t = 0;
-    for (const DevBuf *b : {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &cindptr, &cindices,
-                            &bwd.light, &bwd.heavy, &bwd.groups, &bwd.partial_ofs, &tile_rc, &tile_mask,
+    for (const DevBuf *b : {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &fwd.sched, &cindptr, &cindices,
+                            &bwd.light, &bwd.heavy, &bwd.groups, &bwd.partial_ofs, &bwd.sched, &tile_rc, &tile_mask,
                             &tile_ptr, &trb, &rindptr, &rindices, &light_nt, &ctile, &ctile_ptr, &tcb,
                             &rcindptr, &rcindices, &c_light_nt})
         t += (int64_t)b->bytes;
@@ -560,6 +614,7 @@ int gnn_plan_opts_default(gnn_plan_opts *o) {
     o->waves_per_group = 4;
     o->tile_density = 0.0f;
     o->want_csc = 0;
+    o->sched_order = 1;
     return GNN_OK;
 }
 
@@ -618,7 +673,7 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
     if (o.light_threshold < 0 || o.chunk < 1 ||
         !(o.waves_per_group == 1 || o.waves_per_group == 2 || o.waves_per_group == 4 || o.waves_per_group == 8))
         return GNN_ERR_INVALID_ARG;
-    if (o.tile_density > 1.0f) return GNN_ERR_INVALID_ARG;
+    if (o.tile_density > 1.0f || o.sched_order < 0 || o.sched_order > 1) return GNN_ERR_INVALID_ARG;
     if ((int64_t)o.chunk * o.waves_per_group >= (1ll << 30)) return GNN_ERR_INVALID_ARG;
 
     gnn_plan_s *p = new (std::nothrow) gnn_plan_s();
@@ -648,13 +703,14 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
         dev_free(tmp);
     }
     if (rc == GNN_OK)
-        rc = build_buckets(indptr, n_nodes, o.light_threshold, o.chunk, o.waves_per_group, p->fwd, stream);
+        rc = build_buckets(indptr, n_nodes, o.light_threshold, o.chunk, o.waves_per_group, o.sched_order, p->fwd,
+                           stream);
     if (rc == GNN_OK && o.want_csc) {
         rc = build_transpose(indptr, indices, n_nodes, n_edges, p->cindptr, p->cindices, stream);
         if (rc == GNN_OK) {
             p->has_csc = true;
             rc = build_buckets(as<int32_t>(p->cindptr), n_nodes, o.light_threshold, o.chunk, o.waves_per_group,
-                               p->bwd, stream);
+                               o.sched_order, p->bwd, stream);
         }
     }
     if (rc == GNN_OK && o.tile_density > 0.0f) {
@@ -684,6 +740,8 @@ int gnn_plan_export(gnn_plan_t p, gnn_plan_info *info) {
     info->heavy_ids = as<int32_t>(p->fwd.heavy);
     info->groups = as<int32_t>(p->fwd.groups);
     info->partial_ofs = as<int32_t>(p->fwd.partial_ofs);
+    info->light_sched = as<int32_t>(p->fwd.sched);
+    info->c_light_sched = as<int32_t>(p->bwd.sched);
     info->has_csc = p->has_csc;
     info->cindptr = as<int32_t>(p->cindptr);
     info->cindices = as<int32_t>(p->cindices);
@@ -723,8 +781,8 @@ int gnn_plan_export(gnn_plan_t p, gnn_plan_info *info) {
 
 int gnn_plan_destroy(gnn_plan_t p) {
     if (!p) return GNN_ERR_INVALID_ARG;
-    for (DevBuf *b : {&p->fwd.light, &p->fwd.heavy, &p->fwd.groups, &p->fwd.partial_ofs, &p->cindptr, &p->cindices,
-                      &p->bwd.light, &p->bwd.heavy, &p->bwd.groups, &p->bwd.partial_ofs, &p->tile_rc, &p->tile_mask,
+    for (DevBuf *b : {&p->fwd.light, &p->fwd.heavy, &p->fwd.groups, &p->fwd.partial_ofs, &p->fwd.sched, &p->cindptr,
+                      &p->cindices, &p->bwd.light, &p->bwd.heavy, &p->bwd.groups, &p->bwd.partial_ofs, &p->bwd.sched, &p->tile_rc, &p->tile_mask,
                       &p->tile_ptr, &p->trb, &p->rindptr, &p->rindices, &p->light_nt, &p->ctile, &p->ctile_ptr,
                       &p->tcb, &p->rcindptr, &p->rcindices, &p->c_light_nt, &p->ws})
         dev_free(*b);

@@ -139,6 +139,15 @@ def bucketing(indptr, threshold: int, chunk: int, waves: int):
                 groups=groups.astype(np.int32), partial_ofs=partial_ofs.astype(np.int32))
 
 
+def launch_order(indptr, light):
+    """Launch order of the light nodes: descending degree, ties by ascending
+    id (longest rows start first; kernel results do not depend on it)."""
+    ip = np.asarray(indptr, np.int64)
+    l = np.asarray(light, np.int64)
+    deg = ip[l + 1] - ip[l]
+    return l[np.lexsort((l, -deg))].astype(np.int32)
+
+
 def csc(indptr, indices, n_nodes: int):
     """Transposed adjacency: for each source j, the destinations i of its
     out-edges j -> i in ascending order (with multiplicity).

@@ -68,11 +68,13 @@ def test_buckets_and_csc(g, T, C, W):
     ref = oracle.bucketing(rp, T, C, W)
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d[k], ref[k]), k
+    assert np.array_equal(d["light_sched"], oracle.launch_order(rp, ref["light"]))
     cip, cix = oracle.csc(rp, rx, n)
     assert np.array_equal(d["cindptr"], cip) and np.array_equal(d["cindices"], cix)
     cref = oracle.bucketing(cip, T, C, W)
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d["c_" + k], cref[k]), "c_" + k
+    assert np.array_equal(d["c_light_sched"], oracle.launch_order(cip, cref["light"]))
     assert d["n_light"] + d["n_heavy"] == n
 
 

@@ -209,3 +209,9 @@ def test_tile_census_multigraph_copies_stay_residual():
     assert t["tile_rc"].tolist() == [[0, 0]]
     assert all(int(w) == (1 << 64) - 1 for w in t["tile_mask"][0])
     assert t["rindices"].tolist() == [3, 3] and np.diff(t["rindptr"]).tolist()[2] == 2
+
+
+def test_launch_order():
+    indptr = np.array([0, 3, 3, 8, 10, 13, 14], np.int32)     # degrees 3, 0, 5, 2, 3, 1
+    light = np.array([0, 1, 3, 4, 5], np.int32)
+    assert oracle.launch_order(indptr, light).tolist() == [0, 4, 3, 5, 1]
