@@ -401,7 +401,7 @@ def bench(args) -> int:
     g.lib()
     torch.cuda.set_device(0)
     opts = dict(light_threshold=args.light_threshold, chunk=args.chunk, waves_per_group=args.waves,
-                tile_density=args.tile_density)
+                tile_density=args.tile_density, sched_order=args.sched_order)
     log(f"[bench] workload {args.workload}: generating and building the graph")
     wl, indptr, indices, plan, T, E, prep = setup(args.workload, opts, True if args.backward else None)
     info = g.gnn_plan_export(plan)
@@ -475,7 +475,7 @@ def bench(args) -> int:
             "n_nodes": N, "n_edges": E, "heads": H, "dim": D,
             "storage": wl.dtype, "math": "f32",
             "light_threshold": args.light_threshold, "chunk": args.chunk, "waves_per_group": args.waves,
-            "tile_density": args.tile_density, "tiles": int(info["n_tiles"]),
+            "tile_density": args.tile_density, "tiles": int(info["n_tiles"]), "sched_order": args.sched_order,
             "cache": "flushed 512 MiB between steps" if args.flush else "warm (back-to-back steps)",
             "parallelism": "single GPU",
         },
@@ -529,6 +529,8 @@ def main():
     ap.add_argument("--light-threshold", type=int, default=512)
     ap.add_argument("--chunk", type=int, default=512)
     ap.add_argument("--waves", type=int, default=4)
+    ap.add_argument("--sched-order", type=int, default=2, choices=(0, 1, 2),
+                    help="light launch order: 0 by id, 1 by descending degree, 2 long rows first")
     ap.add_argument("--tile-density", type=float, default=0.0,
                     help="16x16 tile threshold tau (0 disables the tile path)")
     ap.add_argument("--flush", action="store_true", help="flush caches with a 512 MiB write between steps")

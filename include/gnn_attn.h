@@ -79,8 +79,11 @@ typedef struct {
                                 <= 0 disables the tile path; default 0                         */
     int32_t want_csc;        /* build the transposed adjacency and its out-degree buckets,
                                 needed by gnn_attn_bwd; default 0                               */
-    int32_t sched_order;     /* launch order of light nodes: 1 = descending degree (longest
-                                first, default), 0 = ascending id; outputs do not depend on it  */
+    int32_t sched_order;     /* launch order of light nodes; ties always by ascending id.
+                                0 = ascending id; 1 = descending degree; 2 (default) = nodes
+                                of degree > max(1, light_threshold/4) first, by descending
+                                floor(log2(degree)), then the rest by id. Outputs do not
+                                depend on it                                                   */
 } gnn_plan_opts;
 
 /* Fill *opts with the defaults above. Returns GNN_ERR_INVALID_ARG if opts is NULL. */

@@ -201,7 +201,7 @@ class Plan:
 
 
 def gnn_plan_create(indptr, indices, light_threshold: int = 512, chunk: int = 512, waves_per_group: int = 4,
-                    tile_density: float = 0.0, want_csc: bool = False, sched_order: int = 1, stream=None) -> Plan:
+                    tile_density: float = 0.0, want_csc: bool = False, sched_order: int = 2, stream=None) -> Plan:
     n, e = _graph(indptr, indices)
     o = PlanOpts()
     lib().gnn_plan_opts_default(C.byref(o))

@@ -426,13 +426,23 @@ __global__ void k_bucket_emit(const int32_t *indptr, int32_t n, int32_t T, int64
     }
 }
 
+// order 1: descending degree; order 2: nodes of degree > hoist first, by
+// descending floor(log2(degree)), everything else after; ties by ascending id
 __global__ void k_sched_keys(const int32_t *indptr, const int32_t *light, int32_t n_light, int64_t cap,
-                             uint64_t *keys) {
+                             int32_t order, int64_t hoist, uint64_t *keys) {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n_light) return;
     const int32_t v = light[k];
     const int64_t deg = (int64_t)indptr[v + 1] - indptr[v];
-    keys[k] = ((uint64_t)(cap - deg) << 32) | (uint32_t)v;
+    uint64_t hi;
+    if (order == 1) {
+        hi = (uint64_t)(cap - deg);
+    } else {
+        int b = 0;
+        while (b < 62 && (2ll << b) <= deg) ++b;   // floor(log2(deg)) for deg >= 1
+        hi = deg > hoist ? (uint64_t)(63 - b) : 64ull;
+    }
+    keys[k] = (hi << 32) | (uint32_t)v;
 }
 
 __global__ void k_low32_i32(const uint64_t *keys, int64_t n, int32_t *out) {
@@ -440,7 +450,7 @@ __global__ void k_low32_i32(const uint64_t *keys, int64_t n, int32_t *out) {
     if (k < n) out[k] = (int32_t)(keys[k] & 0xFFFFFFFFull);
 }
 
-// light launch order: descending degree, ties by ascending id
+// light launch order (see k_sched_keys); order 0 keeps the light list
 static int build_sched(const int32_t *indptr, int32_t T, int64_t max_deg, int32_t sched_order, Buckets &b,
                        hipStream_t s) {
     GNN_TRY(dev_alloc(b.sched, (size_t)std::max(1, b.n_light) * 4));
@@ -456,8 +466,10 @@ static int build_sched(const int32_t *indptr, int32_t T, int64_t max_deg, int32_
     GNN_TRY(dev_alloc(tmp, (size_t)(16 * m + 4 * ss + 64)));
     uint64_t *keys = as<uint64_t>(tmp), *kt = keys + m;
     int32_t *scr = reinterpret_cast<int32_t *>(kt + m);
-    hipLaunchKernelGGL(k_sched_keys, grid1d(m), dim3(256), 0, s, indptr, as<int32_t>(b.light), b.n_light, cap, keys);
-    int rc = radix_sort(keys, kt, m, 32 + bits_for(cap + 2), scr, s);
+    const int64_t hoist = std::max<int64_t>(1, T / 4);
+    hipLaunchKernelGGL(k_sched_keys, grid1d(m), dim3(256), 0, s, indptr, as<int32_t>(b.light), b.n_light, cap,
+                       sched_order, hoist, keys);
+    int rc = radix_sort(keys, kt, m, 32 + (sched_order == 1 ? bits_for(cap + 2) : 7), scr, s);
     if (rc == GNN_OK) {
         hipLaunchKernelGGL(k_low32_i32, grid1d(m), dim3(256), 0, s, keys, m, as<int32_t>(b.sched));
         if (hipStreamSynchronize(s) != hipSuccess) {
@@ -614,7 +626,7 @@ int gnn_plan_opts_default(gnn_plan_opts *o) {
     o->waves_per_group = 4;
     o->tile_density = 0.0f;
     o->want_csc = 0;
-    o->sched_order = 1;
+    o->sched_order = 2;
     return GNN_OK;
 }
 
@@ -673,7 +685,7 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
     if (o.light_threshold < 0 || o.chunk < 1 ||
         !(o.waves_per_group == 1 || o.waves_per_group == 2 || o.waves_per_group == 4 || o.waves_per_group == 8))
         return GNN_ERR_INVALID_ARG;
-    if (o.tile_density > 1.0f || o.sched_order < 0 || o.sched_order > 1) return GNN_ERR_INVALID_ARG;
+    if (o.tile_density > 1.0f || o.sched_order < 0 || o.sched_order > 2) return GNN_ERR_INVALID_ARG;
     if ((int64_t)o.chunk * o.waves_per_group >= (1ll << 30)) return GNN_ERR_INVALID_ARG;
 
     gnn_plan_s *p = new (std::nothrow) gnn_plan_s();

@@ -139,13 +139,23 @@ def bucketing(indptr, threshold: int, chunk: int, waves: int):
                 groups=groups.astype(np.int32), partial_ofs=partial_ofs.astype(np.int32))
 
 
-def launch_order(indptr, light):
-    """Launch order of the light nodes: descending degree, ties by ascending
-    id (longest rows start first; kernel results do not depend on it)."""
+def launch_order(indptr, light, order: int = 2, threshold: int = 512):
+    """Launch order of the light nodes (kernel results do not depend on it).
+
+    order 0: the light list itself; order 1: descending degree; order 2:
+    nodes of degree > max(1, threshold // 4) first, by descending
+    floor(log2(degree)), then all others; ties by ascending id."""
     ip = np.asarray(indptr, np.int64)
     l = np.asarray(light, np.int64)
+    if order == 0:
+        return l.astype(np.int32)
     deg = ip[l + 1] - ip[l]
-    return l[np.lexsort((l, -deg))].astype(np.int32)
+    if order == 1:
+        return l[np.lexsort((l, -deg))].astype(np.int32)
+    hoist = max(1, int(threshold) // 4)
+    b = np.floor(np.log2(np.maximum(deg, 1))).astype(np.int64)
+    key = np.where(deg > hoist, 63 - b, 64)
+    return l[np.lexsort((l, key))].astype(np.int32)
 
 
 def csc(indptr, indices, n_nodes: int):
@@ -416,7 +426,8 @@ def scaled_error(x, ref, scale) -> float:
     ref = np.asarray(ref, np.float64)
     s = np.maximum(np.abs(ref), np.asarray(scale, np.float64))
     both_inf = np.isinf(x) & np.isinf(ref) & (np.sign(x) == np.sign(ref))
-    diff = np.where(both_inf, 0.0, np.abs(x - ref))
+    with np.errstate(invalid="ignore"):
+        diff = np.where(both_inf, 0.0, np.abs(x - ref))
     den = np.where(both_inf, 1.0, np.where(s > 0, s, 1.0))
     e = diff / den
     if e.size == 0:

@@ -68,7 +68,7 @@ def test_host_validation(g):
     # plans
     h = C.c_void_p()
     o = g.PlanOpts()
-    assert L.gnn_plan_opts_default(C.byref(o)) == 0 and o.light_threshold == 512 and o.waves_per_group == 4 and o.sched_order == 1
+    assert L.gnn_plan_opts_default(C.byref(o)) == 0 and o.light_threshold == 512 and o.waves_per_group == 4 and o.sched_order == 2
     assert L.gnn_plan_opts_default(None) == -1
     assert L.gnn_plan_create(None, A, 10, 20, None, None, C.byref(h)) == -1
     assert L.gnn_plan_create(A, A, 10, 20, None, None, None) == -1

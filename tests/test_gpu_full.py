@@ -67,12 +67,14 @@ def test_full_size(g, name):
     ref_b = oracle.bucketing(rp, 512, 512, 4)
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d[k], ref_b[k]), k
+    assert np.array_equal(d["light_sched"], oracle.launch_order(rp, ref_b["light"])), "light_sched"
     if wl.backward:
         cip, cix = oracle.csc(rp, rx, n)
         assert np.array_equal(d["cindptr"], cip) and np.array_equal(d["cindices"], cix), "csc"
         ref_c = oracle.bucketing(cip, 512, 512, 4)
         for k in ("light", "heavy", "groups", "partial_ofs"):
             assert np.array_equal(d["c_" + k], ref_c[k]), "c_" + k
+        assert np.array_equal(d["c_light_sched"], oracle.launch_order(cip, ref_c["light"])), "c_light_sched"
     say(f"  buckets bit-exact: light {d['n_light']} heavy {d['n_heavy']} groups {d['n_groups']}")
     rng = np.random.default_rng(77)
     rows = _sample(rng, n, ref_b["heavy"], N_SAMPLE)

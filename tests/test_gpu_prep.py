@@ -56,25 +56,27 @@ def test_csr_build_rejects_bad_endpoint(g):
     assert e.value.status == -6
 
 
+@pytest.mark.parametrize("order", [0, 1, 2])
 @pytest.mark.parametrize("T,C,W", [(0, 1, 1), (0, 5, 4), (3, 2, 2), (16, 8, 2), (64, 64, 8), (512, 512, 4),
                                    (10 ** 9, 512, 4)])
-def test_buckets_and_csc(g, T, C, W):
+def test_buckets_and_csc(g, T, C, W, order):
     wl = workloads.make("gatv2_zipf21_n100k", 12000, features=False)
     n = wl.n_nodes
     ip, ix, rp, rx = _csr_case(g, wl.src, wl.dst, n, True)
     say("plan", T, C, W)
-    plan = g.gnn_plan_create(ip, ix, light_threshold=T, chunk=C, waves_per_group=W, want_csc=True)
+    plan = g.gnn_plan_create(ip, ix, light_threshold=T, chunk=C, waves_per_group=W, want_csc=True,
+                             sched_order=order)
     d = g.gnn_plan_export(plan, arrays=True)
     ref = oracle.bucketing(rp, T, C, W)
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d[k], ref[k]), k
-    assert np.array_equal(d["light_sched"], oracle.launch_order(rp, ref["light"]))
+    assert np.array_equal(d["light_sched"], oracle.launch_order(rp, ref["light"], order, T))
     cip, cix = oracle.csc(rp, rx, n)
     assert np.array_equal(d["cindptr"], cip) and np.array_equal(d["cindices"], cix)
     cref = oracle.bucketing(cip, T, C, W)
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d["c_" + k], cref[k]), "c_" + k
-    assert np.array_equal(d["c_light_sched"], oracle.launch_order(cip, cref["light"]))
+    assert np.array_equal(d["c_light_sched"], oracle.launch_order(cip, cref["light"], order, T))
     assert d["n_light"] + d["n_heavy"] == n
 
 

@@ -214,4 +214,9 @@ def test_tile_census_multigraph_copies_stay_residual():
 def test_launch_order():
     indptr = np.array([0, 3, 3, 8, 10, 13, 14], np.int32)     # degrees 3, 0, 5, 2, 3, 1
     light = np.array([0, 1, 3, 4, 5], np.int32)
-    assert oracle.launch_order(indptr, light).tolist() == [0, 4, 3, 5, 1]
+    assert oracle.launch_order(indptr, light, 1).tolist() == [0, 4, 3, 5, 1]
+    assert oracle.launch_order(indptr, light, 0).tolist() == [0, 1, 3, 4, 5]
+    # threshold 8 -> hoist degree > 2: degree 3 rows (ids 0, 4) first, the rest by id
+    assert oracle.launch_order(indptr, light, 2, 8).tolist() == [0, 4, 1, 3, 5]
+    ip = np.array([0, 1, 9, 14, 14, 30], np.int32)            # degrees 1, 8, 5, 0, 16
+    assert oracle.launch_order(ip, np.arange(5), 2, 8).tolist() == [4, 1, 2, 0, 3]
