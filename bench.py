@@ -220,6 +220,88 @@ def traffic_summary(args) -> int:
     return 0
 
 
+CACHE_TEXT = {"flushed": "flushed: 512 MiB fill before every step, outside the timed events",
+              "warm": "warm: steps back to back"}
+UNIT_COUNTERS = ["SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE",
+                 "TCC_HIT_sum", "TCC_MISS_sum"]
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
+
+
+def _dispatch_means(d, pattern):
+    """Mean per dispatch of every counter for the kernel matching pattern
+    (rows of one dispatch and counter are summed first)."""
+    import re
+    per = {}
+    dur = {}
+    names = set()
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if re.search(pattern, r["Kernel_Name"]):
+                    names.add(r["Kernel_Name"])
+                    key = (fn, r["Dispatch_Id"])
+                    per.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+                    per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+                    dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    if not per:
+        raise SystemExit(f"no counter rows for /{pattern}/ under {d}")
+    out = {}
+    for c in {c for v in per.values() for c in v}:
+        vals = [v[c] for v in per.values() if c in v]
+        out[c] = sum(vals) / len(vals)
+    out["duration_s"] = sum(dur.values()) / len(dur)
+    return sorted(names), out, len(per)
+
+
+def units_summary(args) -> int:
+    """Execution-unit counters of one kernel (one rocprofv3 --pmc pass with
+    UNIT_COUNTERS), with rocprof's own derived-metric expressions."""
+    names, m, n = _dispatch_means(args.units, args.kernel_regex)
+    # GRBM_GUI_ACTIVE comes summed over the XCDs' instances; rocprof's derived
+    # metrics take the max over them, i.e. the busy cycles of one XCD
+    gui = m.get("GRBM_GUI_ACTIVE", float("nan")) / XCD_NUM
+    hit, miss = m.get("TCC_HIT_sum", 0.0), m.get("TCC_MISS_sum", 0.0)
+    lds_act, lds_cf = m.get("SQ_LDS_IDX_ACTIVE", 0.0), m.get("SQ_LDS_BANK_CONFLICT", 0.0)
+    derived = {
+        "VALUBusy_pct (100*SQ_ACTIVE_INST_VALU/CU_NUM/GUI)":
+            100 * m.get("SQ_ACTIVE_INST_VALU", 0.0) / CU_NUM / gui,
+        "MfmaUtil_pct (100*SQ_VALU_MFMA_BUSY_CYCLES/(GUI*SIMD_NUM))":
+            100 * m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * SIMD_NUM),
+        "LdsBankConflict_per_access (SQ_LDS_BANK_CONFLICT/(SQ_LDS_IDX_ACTIVE-SQ_LDS_BANK_CONFLICT))":
+            lds_cf / (lds_act - lds_cf) if lds_act > lds_cf else 0.0,
+        "LDSBankConflict_pct_of_time (100*SQ_LDS_BANK_CONFLICT/GUI/CU_NUM)":
+            100 * lds_cf / gui / CU_NUM,
+        "OccupancyPercent (400*SQ_WAVE_CYCLES/GUI/CU_NUM/32)":
+            400 * m.get("SQ_WAVE_CYCLES", 0.0) / gui / CU_NUM / 32,
+        "L2_hit_pct (100*TCC_HIT_sum/(TCC_HIT_sum+TCC_MISS_sum))":
+            100 * hit / (hit + miss) if hit + miss > 0 else float("nan"),
+    }
+    lines = [
+        f"# execution-unit counters of {args.kernel} on {args.workload}",
+        f"# command (from the repository root, under /tmp as working directory):",
+        f"#   rocprofv3 --pmc {' '.join(UNIT_COUNTERS)} -d {args.units} -o units --output-format csv "
+        f"-- python3 bench.py {args.bench_args}",
+        f"#   python3 bench.py --units {args.units} --kernel {args.kernel} --kernel-regex '{args.kernel_regex}' "
+        f"--workload {args.workload} --bench-args '{args.bench_args}'",
+        f"# CU_NUM {CU_NUM}, SIMD_NUM {SIMD_NUM}; values are means per dispatch (n={n}); "
+        f"GRBM_GUI_ACTIVE below is the sum over {XCD_NUM} XCDs, the formulas use sum/{XCD_NUM}",
+        f"dispatch_us: {m['duration_s'] * 1e6:.2f}",
+        f"clock_GHz (GRBM_GUI_ACTIVE/{XCD_NUM}/dispatch time): {gui / m['duration_s'] / 1e9:.3f}",
+        *[f"kernel_symbol: {k}" for k in names],
+        f"source_sha256: {kernel_source_hash()}",
+        *[f"{c}: {m[c]:.1f}" for c in UNIT_COUNTERS if c in m],
+        f"GUI (GRBM_GUI_ACTIVE/{XCD_NUM}): {gui:.1f}",
+        *[f"{k}: {v:.3f}" for k, v in derived.items()],
+    ]
+    text = "\n".join(lines) + "\n"
+    out = args.out or os.path.join(PROFILES, f"{args.kernel}__{args.workload}__units.txt")
+    with open(out, "w") as f:
+        f.write(text)
+    print(text)
+    return 0
+
+
 def summarize(args) -> int:
     """Summarise rocprofv3 output (kernel stats or counters) into text."""
     out = []
@@ -335,12 +417,24 @@ def make_step(g, wl, indptr, indices, plan, T):
     return step
 
 
-def cpu_baseline(wl, rp, rx, target_s):
+def cpu_baseline(wl, rp, rx, target_s, threads=None):
     """fp64 oracle on a seeded sample of destination rows (and the same nodes
     as sources for the gradient), sized to about target_s seconds."""
     import numpy as np
 
     import oracle
+
+    all_threads = oracle.num_threads()
+    if threads:
+        oracle.set_threads(threads)
+    try:
+        return _cpu_baseline(oracle, wl, rp, rx, target_s)
+    finally:
+        oracle.set_threads(all_threads)
+
+
+def _cpu_baseline(oracle, wl, rp, rx, target_s):
+    import numpy as np
 
     n = wl.n_nodes
     deg = np.diff(rp.astype(np.int64))
@@ -411,33 +505,42 @@ def bench(args) -> int:
         f"groups={info['n_groups']} prep={prep}")
     step = make_step(g, wl, indptr, indices, plan, T)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+    headline_flushed = args.cache == "flushed"
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for k in range(args.warmup):             # warm up in the headline's cache state
+        if headline_flushed:
+            flush_buf.fill_(k & 0xFF)
         step()
     torch.cuda.synchronize()
-    g.gnn_plan_timing_read(plan)
-    g.gnn_plan_set_timing(plan, True)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-    wall0 = time.perf_counter()
-    if flush is None:
-        ev[0].record(stream)
-        for _ in range(args.steps):
-            step()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        ms_total = ev[0].elapsed_time(ev[1])
-    else:
+
+    def timed(flushed):
+        """Milliseconds of args.steps steps. Flushed: a 512 MiB fill before
+        every step, outside the events; warm: the steps back to back."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+        if not flushed:
+            ev[0].record(stream)
+            for _ in range(args.steps):
+                step()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1])
         for k in range(args.steps):
-            flush.fill_(k & 0xFF)
+            flush_buf.fill_(k & 0xFF)
             ev[2 * k].record(stream)
             step()
             ev[2 * k + 1].record(stream)
         torch.cuda.synchronize()
-        ms_total = sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps))
+        return sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps))
+
+    g.gnn_plan_timing_read(plan)
+    g.gnn_plan_set_timing(plan, True)
+    wall0 = time.perf_counter()
+    ms_total = timed(headline_flushed)
     wall = time.perf_counter() - wall0
     g.gnn_plan_set_timing(plan, False)
     kt = g.gnn_plan_timing_read(plan)
+    ms_other = None if args.no_other_cache else timed(not headline_flushed) / args.steps
+    del flush_buf
     ms_step = ms_total / args.steps
     value = E / (ms_step * 1e-3) / 1e9
 
@@ -476,9 +579,12 @@ def bench(args) -> int:
             "storage": wl.dtype, "math": "f32",
             "light_threshold": args.light_threshold, "chunk": args.chunk, "waves_per_group": args.waves,
             "tile_density": args.tile_density, "tiles": int(info["n_tiles"]), "sched_order": args.sched_order,
-            "cache": "flushed 512 MiB between steps" if args.flush else "warm (back-to-back steps)",
+            "cache": CACHE_TEXT[args.cache],
             "parallelism": "single GPU",
         },
+        "other_cache": None if ms_other is None else {
+            "cache": CACHE_TEXT["warm" if headline_flushed else "flushed"],
+            "ms_per_step": round(ms_other, 5), "value": round(E / (ms_other * 1e-3) / 1e9, 4)},
         "step_model_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_model_frac_of_8TBps": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {
@@ -503,6 +609,8 @@ def bench(args) -> int:
         rx = indices.cpu().numpy()
         log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
         rec["cpu_baseline"] = cpu_baseline(wl, rp, rx, args.cpu_seconds)
+        if E <= 10_000_000:
+            rec["cpu_baseline_1core"] = cpu_baseline(wl, rp, rx, args.cpu_seconds / 2, threads=1)
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -533,7 +641,11 @@ def main():
                     help="light launch order: 0 by id, 1 by descending degree, 2 long rows first")
     ap.add_argument("--tile-density", type=float, default=0.0,
                     help="16x16 tile threshold tau (0 disables the tile path)")
-    ap.add_argument("--flush", action="store_true", help="flush caches with a 512 MiB write between steps")
+    ap.add_argument("--cache", choices=("flushed", "warm"), default="flushed",
+                    help="cache state of the headline timing: a 512 MiB fill before every step (flushed) or "
+                         "steps back to back (warm); the other state is timed after it and reported beside it")
+    ap.add_argument("--no-other-cache", action="store_true",
+                    help="skip the second timing in the other cache state (profiling runs)")
     ap.add_argument("--backward", action="store_true",
                     help="add the LSE-recompute backward to the step (seeded upstream gradient)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -543,6 +655,7 @@ def main():
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--out", help="summary output file")
+    ap.add_argument("--units", metavar="DIR", help="summarise an execution-unit counter pass (UNIT_COUNTERS)")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--kernel", help="kernel kind for --traffic (e.g. gatv2_fwd_main)")
     ap.add_argument("--kernel-regex", default="k_fwd_main", help="symbol pattern for --traffic")
@@ -552,6 +665,8 @@ def main():
         return summarize(args)
     if args.traffic:
         return traffic_summary(args)
+    if args.units:
+        return units_summary(args)
     if args.copy_probe:
         return copy_probe(args)
     return bench(args)

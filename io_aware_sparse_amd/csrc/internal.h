@@ -45,9 +45,8 @@ T *as(const DevBuf &b) { return reinterpret_cast<T *>(b.p); }
 struct Buckets {
     int32_t n_light = 0, n_heavy = 0, n_groups = 0;
     DevBuf light, heavy, groups, partial_ofs;
-    // launch order of the light list (descending degree, ties by ascending id,
-    // when the plan asks for it, else a copy of the light list); the results
-    // of every kernel are independent of the order
+    // launch order of the light list, as gnn_plan_opts::sched_order asks (order
+    // 0 is a copy of the light list); kernel results do not depend on it
     DevBuf sched;
 };
 

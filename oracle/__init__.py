@@ -73,6 +73,14 @@ def num_threads() -> int:
     return int(_load().orc_num_threads())
 
 
+def set_threads(n: int) -> None:
+    """Use n OpenMP threads in later calls (results do not depend on it:
+    each output row is reduced by one thread in a fixed order)."""
+    L = _load()
+    L.orc_set_threads.argtypes = [C.c_int]
+    L.orc_set_threads(int(n))
+
+
 def _p(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(C.c_void_p)
 

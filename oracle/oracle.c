@@ -67,6 +67,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Thread count of later oracle calls (n >= 1); only changes how rows are shared out. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Graph-Transformer logit s_ij^h = scale * <q_i^h, k_j^h>. */
 static double gt_logit(const double *Q, const double *K, int64_t i, int64_t j, int h, int H, int D,
                        double scale) {

@@ -1,0 +1,124 @@
+"""Device-memory audit of the attention calls at full size.
+
+The fused kernels never hold per-edge logits or messages: the only memory a
+call may add is the plan's workspace (heavy-node partials, per-node
+backward statistics, GATv2 per-node score gradients), whose size is a closed
+form in the plan's counts. Checked here:
+
+* the workspace equals that closed form after each call;
+* no workspace allocation reaches E*H*2 bytes (an fp16 logit per edge and
+  head would already need that much);
+* the device free memory drops by no more than the workspace growth across
+  a call, up to the allocator's 2 MiB pages (outputs come from torch's
+  allocator and are counted separately);
+* a second call with the same shapes leaves the workspace as it is and
+  takes no more than one such page.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from _gpu import say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+MIB = 1 << 20
+PAGE = 2 * MIB      # granularity at which the device free memory moves
+
+
+@pytest.fixture(scope="module")
+def g():
+    import io_aware_sparse_amd as g
+    g.lib()
+    return g
+
+
+def _dev(wl, nm):
+    import torch
+    if wl.dtype == "bf16":
+        return torch.from_numpy(wl.bits[nm].view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(wl.feats[nm]).cuda()
+
+
+def _library_bytes(fn):
+    """Run fn and return (result, device bytes taken outside torch's allocator)."""
+    import torch
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    res0 = torch.cuda.memory_reserved()
+    out = fn()
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    res1 = torch.cuda.memory_reserved()
+    return out, (free0 - free1) - (res1 - res0)
+
+
+def _ws_fwd(d, H, D):
+    return d["n_groups"] * (H * D + 2 * H) * 4
+
+
+def _ws_bwd(d, N, H, D, gat):
+    rowlen = H * D
+    n = 2 * N * H + d["n_groups"] * ((4 if gat else 2) * rowlen + H) + d["c_n_groups"] * 2 * rowlen
+    if gat:
+        n += N * rowlen + ((N + 63) // 64) * rowlen
+    return n * 4
+
+
+def _audit(g, plan, wl, E, name, fn, expect_ws):
+    before = g.gnn_plan_export(plan)["workspace_bytes"]
+    _, lib1 = _library_bytes(fn)
+    d = g.gnn_plan_export(plan)
+    grew = d["workspace_bytes"] - before
+    say(f"  {name}: workspace {d['workspace_bytes'] / MIB:.2f} MiB (expected {expect_ws / MIB:.2f}), "
+        f"library took {lib1 / MIB:.2f} MiB, E*H*2 = {2 * E * wl.heads / MIB:.1f} MiB")
+    assert d["workspace_bytes"] == max(before, expect_ws), name
+    assert d["largest_workspace_alloc"] < 2 * E * wl.heads, name
+    assert lib1 <= max(grew, 0) + 2 * PAGE, (name, lib1, grew)
+    _, lib2 = _library_bytes(fn)
+    say(f"  {name} again: library took {lib2 / MIB:.2f} MiB, workspace "
+        f"{g.gnn_plan_export(plan)['workspace_bytes'] / MIB:.2f} MiB")
+    assert g.gnn_plan_export(plan)["workspace_bytes"] == d["workspace_bytes"], name
+    assert lib2 <= PAGE, (name, "second call allocated", lib2)
+
+
+@pytest.mark.parametrize("name,tiles", [("gatv2_zipf21_n100k", 0.0), ("gt_chunglu22_n2450k", 0.0),
+                                        ("gt_comm16_n1m_deg27", 0.0), ("gt_comm16_n1m_deg27", 0.75)])
+def test_memory_audit(g, name, tiles):
+    import torch
+    say("memory audit", name, "tiles" if tiles else "")
+    backward = name != "gt_chunglu22_n2450k"
+    wl = workloads.make(name, backward=backward)
+    N, H, D = wl.n_nodes, wl.heads, wl.dim
+    ip, ix = g.gnn_csr_build(torch.from_numpy(wl.src).cuda(), torch.from_numpy(wl.dst).cuda(), N)
+    E = int(ix.numel())
+    plan = g.gnn_plan_create(ip, ix, want_csc=backward, tile_density=tiles)
+    d = g.gnn_plan_export(plan)
+    say(f"  structure {d['structure_bytes'] / MIB:.1f} MiB for E = {E}")
+    # buckets, CSC and launch orders are O(N + E) int32 arrays; tiles add O(#tiles) and a residual CSR
+    assert d["structure_bytes"] <= 4 * (8 * (N + 1) + 3 * E) + 48 * d["n_tiles"] + 64 * MIB
+    holder = {}
+    if wl.kind == "gatv2":
+        xd, xs, go = _dev(wl, "XD"), _dev(wl, "XS"), _dev(wl, "dO")
+        att = torch.from_numpy(wl.att).cuda()
+
+        def fwd():
+            holder["fwd"] = g.gatv2_attn_fwd(plan, ip, ix, xd, xs, att)
+
+        def bwd():
+            holder["bwd"] = g.gatv2_attn_bwd(plan, ip, ix, xd, xs, att, go, holder["fwd"][1])
+    else:
+        q, k, v = _dev(wl, "Q"), _dev(wl, "K"), _dev(wl, "V")
+
+        def fwd():
+            holder["fwd"] = g.gnn_attn_fwd(plan, ip, ix, q, k, v)
+
+        if backward:
+            go = _dev(wl, "dO")
+
+            def bwd():
+                O, L = holder["fwd"]
+                holder["bwd"] = g.gnn_attn_bwd(plan, ip, ix, q, k, v, O, go, L)
+    _audit(g, plan, wl, E, "forward", fwd, _ws_fwd(d, H, D))
+    if backward:
+        _audit(g, plan, wl, E, "backward", bwd, _ws_bwd(d, N, H, D, wl.kind == "gatv2"))

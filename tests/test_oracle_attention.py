@@ -443,3 +443,25 @@ def test_gatv2_bwd_closed_forms_and_subsets():
         assert np.array_equal(sub[k], full[k][rows]), k
     assert np.array_equal(sub["dXS"], full["dXS"][rows])
     assert np.array_equal(sub["d_att"], full["d_att"])
+
+
+def test_thread_count_does_not_change_results():
+    """Each output row is reduced by one thread in a fixed order, so the
+    oracle's results are bitwise the same at any thread count."""
+    rng = np.random.default_rng(5)
+    n, H, D = 300, 2, 16
+    src = rng.integers(0, n, 3000).astype(np.int32)
+    dst = rng.integers(0, n, 3000).astype(np.int32)
+    ip, ix = oracle.csr_build(src, dst, n)
+    Q, K, V, dO = (rng.standard_normal((n, H, D)) for _ in range(4))
+    full = oracle.num_threads()
+    a = oracle.gt_bwd(ip, ix, Q, K, V, dO)
+    oracle.set_threads(1)
+    try:
+        assert oracle.num_threads() == 1
+        b = oracle.gt_bwd(ip, ix, Q, K, V, dO)
+    finally:
+        oracle.set_threads(full)
+    assert oracle.num_threads() == full
+    for k in ("dQ", "dK", "dV"):
+        assert np.array_equal(a[k], b[k]), k
