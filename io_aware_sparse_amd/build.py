@@ -36,6 +36,24 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
+PROBE_SRC = os.path.join(CSRC, "bw_probe.hip")
+PROBE = os.path.join(PKG, "bw_probe")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the standalone bandwidth-reference executable (bench.py --bw-probe)."""
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [hipcc(), *flags, PROBE_SRC, "-o", PROBE + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on bw_probe.hip")
+    os.replace(PROBE + ".tmp", PROBE)
+    return PROBE
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into the package's shared library (always rebuilds)."""
     tmp = LIB + ".tmp"
@@ -52,6 +70,7 @@ def build(verbose: bool = False) -> str:
         if lines:
             sys.stderr.write("\n".join(lines) + "\n")
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 
