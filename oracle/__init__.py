@@ -11,13 +11,17 @@ Two halves:
   adjacency (CSC), and the 16x16 dense-tile census. These are the definitions
   the preprocessor must reproduce bit for bit.
 * floating point (``oracle.c``, fp64, OpenMP over rows): Graph-Transformer
-  forward and backward and GATv2 forward, each materialising per-row edge
-  logits and using a two-pass softmax.
+  forward and backward and GATv2 forward and backward, each materialising
+  per-row edge logits and using a two-pass softmax; the neighbourhood
+  max/min reduction with its winning indices (decided in fp32, the
+  messages' precision) and its gradient.
 
 Source: "On Efficient Scaling of GNNs via IO-Aware Layers Implementations",
 technical summary, Methodology (degree-aware tiling with a light/heavy split;
 fused CSR attention with an online-softmax forward and a log-sum-exp
-recompute backward; cached transposed adjacency; 16x16 block-sparse tiles).
+recompute backward; reduction-based aggregations (a per-edge computation and
+a neighbourhood min/max); cached transposed adjacency; 16x16 block-sparse
+tiles).
 """
 from __future__ import annotations
 
@@ -61,8 +65,9 @@ def _load():
         lib.orc_gt_bwd_srcs.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, P, P, P, P, i64, P, P, P, P, P]
         lib.orc_gatv2_bwd_rows.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, P, i64, P, P, P, P, P, P, P, P]
         lib.orc_gatv2_bwd_srcs.argtypes = [i64, P, P, i32, i32, P, P, P, P, f64, P, P, P, P, P, i64, P, P, P, P, P]
+        lib.orc_segment_reduce.argtypes = [i64, P, P, i64, P, i32, i32, i64, P, P, P]
         for f in (lib.orc_gt_fwd, lib.orc_gatv2_fwd, lib.orc_gt_bwd_rows, lib.orc_gt_bwd_srcs, lib.orc_gatv2_bwd_rows,
-                  lib.orc_gatv2_bwd_srcs):
+                  lib.orc_gatv2_bwd_srcs, lib.orc_segment_reduce):
             f.restype = C.c_int
         lib.orc_num_threads.restype = C.c_int
         _lib = lib
@@ -424,6 +429,66 @@ def gatv2_bwd(indptr, indices, XD, XS, att, dO, V=None, slope: float = 0.2, rows
     else:
         res.update(dXS=dXS, SdXS=SdXS, dV=dV, SdV=SdV)
     return res
+
+
+# ---------------------------------------------------------------------------
+# degree-aware reduction layer
+# ---------------------------------------------------------------------------
+REDUCE_OPS = {"max": 0, "min": 1}
+REDUCE_MSGS = {"src": 0, "diff": 1}
+
+
+def segment_reduce(indptr, indices, X, op: str = "max", msg: str = "src", rows=None):
+    """Neighbourhood max / min of per-edge messages with the winning source.
+
+    m_ij = X[j] (msg "src") or X[j] - X[i] (msg "diff", one fp32
+    subtraction); out[i, f] = max (or min) over row i's entries of m_ij[f];
+    arg[i, f] = the smallest j attaining it (-0 == +0); empty rows give 0 and
+    -1. X is [N, F] (or [N, H, D], flattened per node) fp32 values, bf16
+    inputs widened. Decided in fp32, the precision of the messages.
+    Returns dict out float32 [r, F], arg int32 [r, F]."""
+    X = np.ascontiguousarray(X, np.float32)
+    N = X.shape[0]
+    X = X.reshape(N, -1)
+    F = X.shape[1]
+    ip, ix = _graph(indptr, indices)
+    r, nr = _rows(rows, N)
+    out = np.empty((nr, F), np.float32)
+    arg = np.empty((nr, F), np.int32)
+    rc = _load().orc_segment_reduce(N, _p(ip), _p(ix), F, _p(X), REDUCE_OPS[op], REDUCE_MSGS[msg], nr, _p(r),
+                                    _p(out), _p(arg))
+    if rc:
+        raise MemoryError("oracle row buffer")
+    return dict(out=out, arg=arg)
+
+
+def segment_reduce_bwd(indptr, indices, dOut, arg, msg: str = "src", n_nodes: Optional[int] = None):
+    """Gradient of segment_reduce in fp64: each (i, f) with a winner j sends
+    dOut[i, f] to X[j, f], and for msg "diff" also -dOut[i, f] to X[i, f]
+    (the message is X[j] - X[i]). A source that appears several times in a
+    row receives the gradient once, through the winning entry.
+    Returns dX float64 [N, F]."""
+    dOut = np.asarray(dOut, np.float64)
+    arg = np.asarray(arg, np.int64)
+    N = int(n_nodes if n_nodes is not None else dOut.shape[0])
+    dOut = dOut.reshape(dOut.shape[0], -1)
+    arg = arg.reshape(arg.shape[0], -1)
+    F = dOut.shape[1]
+    dX = np.zeros((N, F), np.float64)
+    won = arg >= 0
+    i_idx, f_idx = np.nonzero(won)
+    np.add.at(dX, (arg[i_idx, f_idx], f_idx), dOut[i_idx, f_idx])
+    if msg == "diff":
+        np.add.at(dX, (i_idx, f_idx), -dOut[i_idx, f_idx])
+    return dX
+
+
+def round_bf16(x) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 (ties to even), returned as
+    fp32 (finite inputs)."""
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return (b.astype(np.uint32) << 16).view(np.float32)
 
 
 def scaled_error(x, ref, scale) -> float:

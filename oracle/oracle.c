@@ -30,6 +30,10 @@
  * Besides each result the oracle returns its summation scale: the sum of the
  * absolute values of the terms reduced into that output element (Higham's
  * condition scale). Tests divide the GPU-vs-oracle difference by it.
+ *
+ * The last function, the neighbourhood max/min reduction, is exact by nature
+ * and decides integers (the winning source), so it works in fp32, the
+ * precision its messages are formed in; see its own comment.
  */
 #include <math.h>
 #include <stdint.h>
@@ -475,6 +479,71 @@ int orc_gatv2_bwd_srcs(int64_t N, const int64_t *cindptr, const int32_t *cindice
                 }
             }
         }
+    }
+    return err;
+}
+
+/*
+ * Degree-aware reduction layer ("On Efficient Scaling of GNNs via IO-Aware
+ * Layers Implementations", technical summary, Methodology: reduction-based
+ * aggregations, a per-edge computation followed by a neighbourhood min/max).
+ *
+ * Message of entry (i, j) of row i: m_ij[f] = X[j][f] (msg 0) or the
+ * difference X[j][f] - X[i][f] (msg 1). out[i][f] is the maximum (op 0) or
+ * minimum (op 1) of m_ij[f] over the entries of row i, and arg[i][f] the
+ * smallest source index j attaining it; values compare as floats, so -0 and
+ * +0 are equal. An empty row gives out 0 and arg -1.
+ *
+ * Unlike the attention functions this one works in fp32: the winner is an
+ * integer decided by comparing messages, so it is decided in the precision the
+ * messages are formed in. X holds fp32 values (bf16 inputs widened exactly);
+ * the difference is one correctly rounded fp32 subtraction. Rows in parallel,
+ * entries of a row in CSR order.
+ */
+int orc_segment_reduce(int64_t N, const int64_t *indptr, const int32_t *indices, int64_t F, const float *X,
+                       int op, int msg, int64_t n_rows, const int64_t *rows, float *out, int32_t *arg) {
+    (void)N;
+    int err = 0;
+#pragma omp parallel
+    {
+        float *best = (float *)malloc((size_t)(F > 0 ? F : 1) * sizeof(float));
+        int32_t *bj = (int32_t *)malloc((size_t)(F > 0 ? F : 1) * sizeof(int32_t));
+        if (!best || !bj) {
+#pragma omp atomic write
+            err = -1;
+        }
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (!best || !bj) continue;
+            const int64_t i = row_of(rows, r);
+            for (int64_t f = 0; f < F; ++f) {
+                best[f] = 0.0f;
+                bj[f] = -1;
+            }
+            for (int64_t e = indptr[i]; e < indptr[i + 1]; ++e) {
+                const int32_t j = indices[e];
+                for (int64_t f = 0; f < F; ++f) {
+                    const float v = msg ? X[(int64_t)j * F + f] - X[i * F + f] : X[(int64_t)j * F + f];
+                    int take;
+                    if (bj[f] < 0)
+                        take = 1;
+                    else if (v == best[f])
+                        take = j < bj[f];
+                    else
+                        take = op == 0 ? (v > best[f]) : (v < best[f]);
+                    if (take) {
+                        best[f] = v;
+                        bj[f] = j;
+                    }
+                }
+            }
+            for (int64_t f = 0; f < F; ++f) {
+                out[r * F + f] = bj[f] < 0 ? 0.0f : best[f];
+                arg[r * F + f] = bj[f];
+            }
+        }
+        free(best);
+        free(bj);
     }
     return err;
 }
