@@ -30,7 +30,9 @@ STATUS = {0: "GNN_OK", -1: "GNN_ERR_INVALID_ARG", -2: "GNN_ERR_UNSUPPORTED", -3:
 # exported symbols, in the order include/gnn_attn.h declares them
 EXPORTS = ["gnn_plan_opts_default", "gnn_csr_build", "gnn_plan_create", "gnn_plan_export", "gnn_plan_destroy",
            "gnn_attn_fwd", "gnn_attn_bwd", "gatv2_attn_fwd", "gatv2_attn_bwd", "gnn_plan_set_timing",
-           "gnn_plan_timing_read", "gnn_status_string"]
+           "gnn_plan_timing_read", "gnn_status_string", "gnn_reduce_fwd", "gnn_reduce_bwd"]
+REDUCE_OPS = {"max": 0, "min": 1}     # gnn_reduce_op_t
+REDUCE_MSGS = {"src": 0, "diff": 1}   # gnn_msg_t
 
 
 class GnnError(RuntimeError):
@@ -92,6 +94,8 @@ def lib():
         L.gnn_attn_bwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, V, V, V, V, V, F, C.c_int, V]
         L.gatv2_attn_fwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, F, V, V, C.c_int, V]
         L.gatv2_attn_bwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, F, V, V, V, V, V, V, C.c_int, V]
+        L.gnn_reduce_fwd.argtypes = [V, V, V, I32, I64, I32, V, V, V, C.c_int, C.c_int, C.c_int, V]
+        L.gnn_reduce_bwd.argtypes = [V, V, V, I32, I64, I32, V, V, V, C.c_int, C.c_int, V]
         L.gnn_plan_set_timing.argtypes = [V, I32]
         L.gnn_plan_timing_read.argtypes = [V, I32, C.POINTER(C.c_char_p), C.POINTER(C.c_int32),
                                            C.POINTER(C.c_double), C.POINTER(C.c_int32)]
@@ -375,9 +379,62 @@ def gnn_plan_set_timing(plan: Plan, enable: bool = True):
     _check(lib().gnn_plan_set_timing(C.c_void_p(plan.handle), int(bool(enable))), "gnn_plan_set_timing")
 
 
+def _rows2d(t, name, shape=None, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [N, F] tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t
+
+
+def gnn_reduce_fwd(plan: Optional[Plan], indptr, indices, X, op: str = "max", msg: str = "src", out=None,
+                   arg=None, want_arg: bool = True, stream=None):
+    """Neighbourhood max / min of per-edge messages (X[j], or X[j] - X[i] for
+    msg "diff") with the smallest winning source. X is [N, F] float32 or
+    bfloat16. Returns (out, arg int32 or None)."""
+    torch = _torch()
+    n, e = _graph(indptr, indices)
+    _rows2d(X, "X")
+    _dtype_code(X)
+    N, F = X.shape
+    if N != n:
+        raise ValueError("X rows differ from the graph's node count")
+    out = torch.empty_like(X) if out is None else _rows2d(out, "out", X.shape, X.dtype)
+    if arg is None and want_arg:
+        arg = torch.empty((N, F), dtype=torch.int32, device=X.device)
+    elif arg is not None:
+        _rows2d(arg, "arg", X.shape, torch.int32)
+    _check(lib().gnn_reduce_fwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, F, _ptr(X),
+                                _ptr(out), _ptr(arg), REDUCE_OPS[op], REDUCE_MSGS[msg], _dtype_code(X),
+                                _stream(stream)), "gnn_reduce_fwd")
+    return out, arg
+
+
+def gnn_reduce_bwd(plan: Plan, indptr, indices, dOut, arg, msg: str = "src", dX=None, stream=None):
+    """Gradient of gnn_reduce_fwd through its winners `arg`. Returns dX."""
+    torch = _torch()
+    n, e = _graph(indptr, indices)
+    _rows2d(dOut, "dOut")
+    _dtype_code(dOut)
+    N, F = dOut.shape
+    if N != n:
+        raise ValueError("dOut rows differ from the graph's node count")
+    _rows2d(arg, "arg", dOut.shape, torch.int32)
+    dX = torch.empty_like(dOut) if dX is None else _rows2d(dX, "dX", dOut.shape, dOut.dtype)
+    _check(lib().gnn_reduce_bwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, F, _ptr(dOut),
+                                _ptr(arg), _ptr(dX), REDUCE_MSGS[msg], _dtype_code(dOut), _stream(stream)),
+           "gnn_reduce_bwd")
+    return dX
+
+
 def gnn_plan_timing_read(plan: Plan) -> dict:
     """{kernel name: (launches, total ms)} since the last read; clears the log."""
-    cap = 16
+    cap = 64
     names = (C.c_char_p * cap)()
     launches = (C.c_int32 * cap)()
     ms = (C.c_double * cap)()

@@ -73,6 +73,11 @@ enum KernelKind {
     K_GAT_BWD_SRC_MAIN,
     K_GAT_BWD_SRC_MERGE,
     K_GAT_DATT,
+    K_RED_INIT,
+    K_RED_MAIN,
+    K_RED_FINAL,
+    K_RED_BWD_MAIN,
+    K_RED_BWD_MERGE,
     K_NUM_KINDS
 };
 extern const char *kKernelNames[K_NUM_KINDS];

@@ -56,7 +56,8 @@ void dev_free(DevBuf &b) {
 const char *kKernelNames[K_NUM_KINDS] = {
     "gt_fwd_main", "gt_fwd_merge", "gatv2_fwd_main", "gatv2_fwd_merge", "gt_bwd_dst_main",
     "gt_bwd_dst_merge", "gt_bwd_src_main", "gt_bwd_src_merge", "gt_tile_fwd", "gt_tile_bwd_dst", "gt_tile_bwd_src",
-    "gatv2_bwd_dst_main", "gatv2_bwd_dst_merge", "gatv2_bwd_src_main", "gatv2_bwd_src_merge", "gatv2_bwd_datt"};
+    "gatv2_bwd_dst_main", "gatv2_bwd_dst_merge", "gatv2_bwd_src_main", "gatv2_bwd_src_merge", "gatv2_bwd_datt",
+    "reduce_fwd_init", "reduce_fwd_main", "reduce_fwd_final", "reduce_bwd_main", "reduce_bwd_merge"};
 
 hipEvent_t Timer::get() {
     if (!pool.empty()) {

@@ -462,12 +462,14 @@ def segment_reduce(indptr, indices, X, op: str = "max", msg: str = "src", rows=N
     return dict(out=out, arg=arg)
 
 
-def segment_reduce_bwd(indptr, indices, dOut, arg, msg: str = "src", n_nodes: Optional[int] = None):
+def segment_reduce_bwd(indptr, indices, dOut, arg, msg: str = "src", n_nodes: Optional[int] = None,
+                       want_scale: bool = False):
     """Gradient of segment_reduce in fp64: each (i, f) with a winner j sends
     dOut[i, f] to X[j, f], and for msg "diff" also -dOut[i, f] to X[i, f]
     (the message is X[j] - X[i]). A source that appears several times in a
     row receives the gradient once, through the winning entry.
-    Returns dX float64 [N, F]."""
+    Returns dX float64 [N, F]; with want_scale also the summation scale
+    S = the sum of |terms| added into each element."""
     dOut = np.asarray(dOut, np.float64)
     arg = np.asarray(arg, np.int64)
     N = int(n_nodes if n_nodes is not None else dOut.shape[0])
@@ -480,7 +482,13 @@ def segment_reduce_bwd(indptr, indices, dOut, arg, msg: str = "src", n_nodes: Op
     np.add.at(dX, (arg[i_idx, f_idx], f_idx), dOut[i_idx, f_idx])
     if msg == "diff":
         np.add.at(dX, (i_idx, f_idx), -dOut[i_idx, f_idx])
-    return dX
+    if not want_scale:
+        return dX
+    S = np.zeros((N, F), np.float64)
+    np.add.at(S, (arg[i_idx, f_idx], f_idx), np.abs(dOut[i_idx, f_idx]))
+    if msg == "diff":
+        np.add.at(S, (i_idx, f_idx), np.abs(dOut[i_idx, f_idx]))
+    return dX, S
 
 
 def round_bf16(x) -> np.ndarray:

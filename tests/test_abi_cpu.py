@@ -8,7 +8,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gnn_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gnn_attn.h", "gnn_reduce.h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,14 +22,21 @@ def g():
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
+
+
+def test_every_header_is_listed():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(os.path.basename(h) for h in HEADERS)
 
 
 def test_exports_every_declared_function(g):
     names = declared_functions()
     assert "gnn_attn_fwd" in names and "gatv2_attn_fwd" in names and "gnn_attn_bwd" in names
+    assert "gnn_reduce_fwd" in names and "gnn_reduce_bwd" in names
     for n in names:
         assert hasattr(g.lib(), n), n
     assert sorted(g.EXPORTS) == names
@@ -58,6 +65,15 @@ def test_host_validation(g):
     assert L.gatv2_attn_fwd(None, A, A, 10, 20, 2, 32, A, A, A, None, 0.2, A, None, 0, None) == -1
     # backward needs a plan
     assert L.gnn_attn_bwd(None, A, A, 10, 20, 2, 32, A, A, A, A, A, A, A, A, A, 0.0, 0, None) == -1
+    # reduction: rows of a multiple of 16 bytes, valid op / message, aligned arrays
+    red = lambda N=10, E=20, F=8, x=A, arg=A, op=0, msg=0, dt=0: L.gnn_reduce_fwd(None, A, A, N, E, F, x, A, arg,
+                                                                                   op, msg, dt, None)
+    assert red(F=6) == -2 and red(F=4, dt=1) == -2 and red(dt=3) == -2
+    assert red(F=0) == -1 and red(N=-1) == -1 and red(op=2) == -1 and red(msg=5) == -1
+    assert red(x=A + 8) == -3 and red(arg=A + 4) == -3
+    assert red(N=0, E=0) == 0                                                             # empty graph: no-op
+    assert L.gnn_reduce_fwd(None, A, A, 10, 20, 8, None, A, None, 0, 0, 0, None) == -1
+    assert L.gnn_reduce_bwd(None, A, A, 10, 20, 8, A, A, A, 0, 0, None) == -1             # needs a plan
     assert L.gatv2_attn_bwd(None, A, A, 10, 20, 2, 32, A, A, A, A, 0.2, A, A, A, A, None, A, 0, None) == -1
     # CSR build
     e = C.c_int64()
