@@ -38,8 +38,11 @@ sys.path.insert(0, ROOT)
 METRIC = "GEdges/s and achieved HBM GB/s (% of peak) for fused CSR attention fwd/bwd"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "gatv2_zipf21_n100k"
-KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_sparse_amd", "csrc", f)
-                  for f in ("attn.hip", "attn_core.h", "attn_tile.hip", "attn_gat.hip", "device.h")]
+_CSRC = os.path.join(ROOT, "io_aware_sparse_amd", "csrc")
+# sources whose change makes a committed counter summary stale, per kernel family
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("attn.hip", "attn_core.h", "attn_tile.hip", "attn_gat.hip",
+                                                   "device.h")]
+REDUCE_SOURCES = [os.path.join(_CSRC, f) for f in ("reduce.hip", "attn_core.h", "device.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -47,9 +50,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "") -> str:
+    """Hash of the sources of `kernel`'s family (reduction kernels: reduce_*)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (REDUCE_SOURCES if kernel.startswith("reduce_") else KERNEL_SOURCES):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -133,6 +137,18 @@ def kernel_bytes(kind, c, H, D, s, v_alias=True):
     if kind == "gatv2_bwd_datt":      # per-node d_att rows read once
         return 4 * H * D * c.get("N", 0)
     t, tr, te = c.get("tiles", 0), c.get("tile_rows", 0), c.get("tile_res_edges", 0)
+    F, rsz = H * D, H * D * s          # reduction layer: F features, rsz bytes per row
+    diff = 1 if c.get("msg") == "diff" else 0
+    if kind == "reduce_fwd_init":       # identity keys of the heavy rows
+        return 8 * F * nh
+    if kind == "reduce_fwd_main":       # gathers a row per edge; light rows write out and arg
+        return 4 * (rows + 1) + 4 * E + rsz * E + (rsz + 4 * F + 4) * nl + diff * rsz * rows
+    if kind == "reduce_fwd_final":      # heavy rows: keys in, winner's row slice, out and arg
+        return 8 * F * nh + (rsz * (1 + diff) + rsz + 4 * F + 4) * nh
+    if kind == "reduce_bwd_main":       # gathers dOut and arg rows per transposed edge; writes dX
+        return 4 * (sr + 1) + 4 * se + (rsz + 4 * F) * se + (rsz + 4) * sl + diff * (rsz + 8) * sr
+    if kind == "reduce_bwd_merge":
+        return rsz * sh
     if kind == "gt_tile_fwd":         # tiles: K, V blocks; rows: Q in, O and LSE out; residual gathers
         return 40 * t + 32 * R * t + 4 * (tr + 1) + (4 + 2 * R) * te + R * tr + (R + 4 * H) * tr
     if kind == "gt_tile_bwd_dst":     # tiles: K, V blocks; rows: Q, dO, LSE in, dQ, stats out
@@ -157,7 +173,7 @@ def read_traffic(kernel: str, workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != kernel_source_hash():
+    if vals.get("source_sha256") != kernel_source_hash(kernel):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -202,7 +218,7 @@ def traffic_summary(args) -> int:
         f"#   python3 bench.py --traffic {fdir} {wdir} {cfdir} {cwdir} --kernel {args.kernel} "
         f"--kernel-regex '{args.kernel_regex}' --workload {args.workload} --bench-args '{args.bench_args}'",
         f"kernel_symbol: {kname}",
-        f"source_sha256: {kernel_source_hash()}",
+        f"source_sha256: {kernel_source_hash(args.kernel)}",
         f"fetch_kib_per_dispatch: {fetch_kib:.1f}  (n={nf})",
         f"write_kib_per_dispatch: {write_kib:.1f}  (n={nw})",
         f"copy_probe_kib: {known_kib:.0f}",
@@ -289,7 +305,7 @@ def units_summary(args) -> int:
         f"dispatch_us: {m['duration_s'] * 1e6:.2f}",
         f"clock_GHz (GRBM_GUI_ACTIVE/{XCD_NUM}/dispatch time): {gui / m['duration_s'] / 1e9:.3f}",
         *[f"kernel_symbol: {k}" for k in names],
-        f"source_sha256: {kernel_source_hash()}",
+        f"source_sha256: {kernel_source_hash(args.kernel)}",
         *[f"{c}: {m[c]:.1f}" for c in UNIT_COUNTERS if c in m],
         f"GUI (GRBM_GUI_ACTIVE/{XCD_NUM}): {gui:.1f}",
         *[f"{k}: {v:.3f}" for k, v in derived.items()],
@@ -310,7 +326,7 @@ def summarize(args) -> int:
     out.append(f"# rocprofv3 summary of {args.summarize}")
     if args.command:
         out.append(f"# command: {args.command}")
-    out.append(f"source_sha256: {kernel_source_hash()}")
+    out.append(f"source_sha256: {kernel_source_hash(args.kernel or '')}")
     for fn in stats:
         out.append(f"## kernel stats ({os.path.basename(fn)})")
         with open(fn) as f:
@@ -372,6 +388,18 @@ def setup(name, plan_opts, backward=None):
     torch.cuda.synchronize()
     t_plan = time.time() - t0
     tensors = {}
+    if wl.kind == "reduce":
+        F = H * D
+        tensors["X"] = feat("X").reshape(n, F)
+        tensors["out"] = torch.empty_like(tensors["X"])
+        tensors["arg"] = torch.empty((n, F), dtype=torch.int32, device=dev)
+        if wl.backward:
+            tensors["dO"] = feat("dO").reshape(n, F)
+            tensors["dX"] = torch.empty_like(tensors["X"])
+        torch.cuda.synchronize()
+        prep = dict(generate_s=round(t_gen, 3), csr_build_ms=round(1e3 * t_csr, 3),
+                    plan_create_ms=round(1e3 * t_plan, 3))
+        return wl, indptr, indices, plan, tensors, int(indices.numel()), prep
     if wl.kind == "gt":
         for nm in ("Q", "K", "V"):
             tensors[nm] = feat(nm)
@@ -395,7 +423,13 @@ def setup(name, plan_opts, backward=None):
     return wl, indptr, indices, plan, tensors, E, prep
 
 
-def make_step(g, wl, indptr, indices, plan, T):
+def make_step(g, wl, indptr, indices, plan, T, op="max", msg="src"):
+    if wl.kind == "reduce":
+        def step():
+            g.gnn_reduce_fwd(plan, indptr, indices, T["X"], op, msg, out=T["out"], arg=T["arg"])
+            if wl.backward:
+                g.gnn_reduce_bwd(plan, indptr, indices, T["dO"], T["arg"], msg, dX=T["dX"])
+        return step
     if wl.kind == "gatv2" and not wl.backward:
         def step():
             g.gatv2_attn_fwd(plan, indptr, indices, T["XD"], T["XS"], T["att"], negative_slope=0.2, O=T["O"],
@@ -417,7 +451,7 @@ def make_step(g, wl, indptr, indices, plan, T):
     return step
 
 
-def cpu_baseline(wl, rp, rx, target_s, threads=None):
+def cpu_baseline(wl, rp, rx, target_s, threads=None, op="max", msg="src"):
     """fp64 oracle on a seeded sample of destination rows (and the same nodes
     as sources for the gradient), sized to about target_s seconds."""
     import numpy as np
@@ -428,12 +462,12 @@ def cpu_baseline(wl, rp, rx, target_s, threads=None):
     if threads:
         oracle.set_threads(threads)
     try:
-        return _cpu_baseline(oracle, wl, rp, rx, target_s)
+        return _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg)
     finally:
         oracle.set_threads(all_threads)
 
 
-def _cpu_baseline(oracle, wl, rp, rx, target_s):
+def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg):
     import numpy as np
 
     n = wl.n_nodes
@@ -442,19 +476,26 @@ def _cpu_baseline(oracle, wl, rp, rx, target_s):
     order = rng.permutation(n)
     csum = np.cumsum(deg[order])
 
-    if wl.kind == "gt":
+    if wl.kind == "reduce":
+        X = wl.feats["X"].reshape(n, -1)
+        dO = wl.feats["dO"].reshape(n, -1) if wl.backward else None
+    elif wl.kind == "gt":
         Q, K, V = (np.asarray(wl.feats[k], np.float64) for k in ("Q", "K", "V"))
         dO = np.asarray(wl.feats["dO"], np.float64) if wl.backward else None
     else:
         XD, XS = (np.asarray(wl.feats[k], np.float64) for k in ("XD", "XS"))
         dO = np.asarray(wl.feats["dO"], np.float64) if wl.backward else None
-    csc = oracle.csc(rp, rx, n) if wl.backward else None
+    csc = oracle.csc(rp, rx, n) if wl.backward and wl.kind != "reduce" else None
 
     def run(edges):
         k = int(np.searchsorted(csum, edges)) + 1
         rows = np.sort(order[:min(k, n)])
         t0 = time.perf_counter()
-        if wl.kind == "gatv2":
+        if wl.kind == "reduce":
+            arg = oracle.segment_reduce(rp, rx, X, op, msg, rows=rows)["arg"]
+            if wl.backward:
+                oracle.segment_reduce_bwd(rp, rx, dO[rows], arg, msg, n_nodes=n, rows=rows)
+        elif wl.kind == "gatv2":
             oracle.gatv2_fwd(rp, rx, XD, XS, wl.att, slope=0.2, rows=rows)
             if wl.backward:
                 oracle.gatv2_bwd(rp, rx, XD, XS, wl.att, dO, slope=0.2, rows=rows, srcs=rows, csc_arrays=csc,
@@ -503,7 +544,7 @@ def bench(args) -> int:
     s = 4 if wl.dtype == "f32" else 2
     log(f"[bench] N={N} E={E} H={H} D={D} dtype={wl.dtype} light={info['n_light']} heavy={info['n_heavy']} "
         f"groups={info['n_groups']} prep={prep}")
-    step = make_step(g, wl, indptr, indices, plan, T)
+    step = make_step(g, wl, indptr, indices, plan, T, args.reduce_op, args.msg)
     stream = torch.cuda.current_stream()
     headline_flushed = args.cache == "flushed"
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -547,6 +588,7 @@ def bench(args) -> int:
     v_alias = True
     tiled = bool(info["has_tiles"]) and wl.dtype == "bf16" and D in (32, 64, 128) and wl.kind == "gt"
     counts = step_counts(g.gnn_plan_export(plan, arrays=True), indptr.cpu().numpy(), indices.cpu().numpy(), tiled)
+    counts["msg"] = args.msg
     kernels = {}
     for name, (launches, tot_ms) in kt.items():
         avg_ms = tot_ms / max(1, launches)
@@ -573,8 +615,10 @@ def bench(args) -> int:
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "pass": ("GATv2" if wl.kind == "gatv2" else "GT") + (" forward + LSE-recompute backward"
-                                                                  if wl.backward else " forward"),
+            "pass": (f"neighbourhood {args.reduce_op} of {args.msg} messages with winners"
+                     + (" + gradient" if wl.backward else "")) if wl.kind == "reduce" else
+                    ("GATv2" if wl.kind == "gatv2" else "GT") + (" forward + LSE-recompute backward"
+                                                                 if wl.backward else " forward"),
             "n_nodes": N, "n_edges": E, "heads": H, "dim": D,
             "storage": wl.dtype, "math": "f32",
             "light_threshold": args.light_threshold, "chunk": args.chunk, "waves_per_group": args.waves,
@@ -599,7 +643,7 @@ def bench(args) -> int:
             "avg_launch_us": dk["avg_us"],
         },
         "kernels": kernels,
-        "kernel_source_sha256": kernel_source_hash(),
+        "kernel_source_sha256": kernel_source_hash(dom),
         "preprocess": prep,
         "wall_s_timed": round(wall, 4),
     }
@@ -608,9 +652,10 @@ def bench(args) -> int:
         rp = indptr.cpu().numpy()
         rx = indices.cpu().numpy()
         log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
-        rec["cpu_baseline"] = cpu_baseline(wl, rp, rx, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, rp, rx, args.cpu_seconds, op=args.reduce_op, msg=args.msg)
         if E <= 10_000_000:
-            rec["cpu_baseline_1core"] = cpu_baseline(wl, rp, rx, args.cpu_seconds / 2, threads=1)
+            rec["cpu_baseline_1core"] = cpu_baseline(wl, rp, rx, args.cpu_seconds / 2, threads=1,
+                                                     op=args.reduce_op, msg=args.msg)
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -657,6 +702,10 @@ def main():
     ap.add_argument("--waves", type=int, default=4)
     ap.add_argument("--sched-order", type=int, default=2, choices=(0, 1, 2),
                     help="light launch order: 0 by id, 1 by descending degree, 2 long rows first")
+    ap.add_argument("--reduce-op", choices=("max", "min"), default="max",
+                    help="reduction workloads (maxpool_*): max or min")
+    ap.add_argument("--msg", choices=("src", "diff"), default="src",
+                    help="reduction workloads: message x_j (src) or x_j - x_i (diff)")
     ap.add_argument("--tile-density", type=float, default=0.0,
                     help="16x16 tile threshold tau (0 disables the tile path)")
     ap.add_argument("--cache", choices=("flushed", "warm"), default="flushed",

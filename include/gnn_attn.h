@@ -166,6 +166,9 @@ typedef struct {
     int64_t structure_bytes;    /* buckets, transposed adjacency, tiles                 */
     int64_t workspace_bytes;    /* heavy partials and backward statistics (grows lazily) */
     int64_t largest_workspace_alloc;
+    int32_t rows_sorted;        /* 1: every CSR row lists its sources in non-decreasing order */
+    const int32_t *light_by_degree; /* [n_light] light nodes by descending in-degree, ties by
+                                       ascending id (launch order 1, whatever sched_order is) */
 } gnn_plan_info;
 
 int gnn_plan_export(gnn_plan_t plan, gnn_plan_info *info /*host*/);

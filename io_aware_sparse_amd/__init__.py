@@ -67,7 +67,8 @@ class PlanInfo(C.Structure):
                 ("tcb", C.c_void_p), ("rcindptr", C.c_void_p), ("rcindices", C.c_void_p),
                 ("c_light_nt", C.c_void_p), ("light_sched", C.c_void_p), ("c_light_sched", C.c_void_p),
                 ("structure_bytes", C.c_int64), ("workspace_bytes", C.c_int64),
-                ("largest_workspace_alloc", C.c_int64)]
+                ("largest_workspace_alloc", C.c_int64), ("rows_sorted", C.c_int32),
+                ("light_by_degree", C.c_void_p)]
 
 
 _lib = None
@@ -251,6 +252,7 @@ def gnn_plan_export(plan: Plan, arrays: bool = False) -> dict:
         d["groups"] = _copy_dev(info.groups, 3 * info.n_groups, np.int32).reshape(-1, 3)
         d["partial_ofs"] = _copy_dev(info.partial_ofs, info.n_heavy + 1, np.int32)
         d["light_sched"] = _copy_dev(info.light_sched, info.n_light, np.int32)
+        d["light_by_degree"] = _copy_dev(info.light_by_degree, info.n_light, np.int32)
         if info.has_csc:
             d["cindptr"] = _copy_dev(info.cindptr, n + 1, np.int32)
             d["cindices"] = _copy_dev(info.cindices, info.n_edges, np.int32)

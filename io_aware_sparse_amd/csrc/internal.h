@@ -48,6 +48,9 @@ struct Buckets {
     // launch order of the light list, as gnn_plan_opts::sched_order asks (order
     // 0 is a copy of the light list); kernel results do not depend on it
     DevBuf sched;
+    // in-degree buckets only: the light list by descending degree, ties by
+    // ascending id (launch order 1), for kernels that pack several rows per wave
+    DevBuf by_degree;
 };
 
 // Per-kernel timing log.
@@ -98,6 +101,7 @@ struct gnn_plan_s {
     int32_t n_nodes = 0;
     int64_t n_edges = 0;
     const int32_t *indptr = nullptr, *indices = nullptr;   // caller's arrays (not owned)
+    bool rows_sorted = false;  // every row's sources in non-decreasing order (checked at creation)
     gnn_plan_opts opts{};
     gnn::Buckets fwd;          // in-degree buckets over the CSR
     bool has_csc = false;
@@ -141,9 +145,9 @@ int emit_structure(uint64_t *keys, int64_t n, int nb, int dedupe, int32_t n_rows
 // transpose a CSR (indptr/indices over n rows) into cindptr/cindices
 int build_transpose(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, DevBuf &cindptr,
                     DevBuf &cindices, hipStream_t s);
-// bucket a CSR-like structure
+// bucket a CSR-like structure (by_degree: also the light list by descending degree)
 int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_t W, int32_t sched_order,
-                  Buckets &b, hipStream_t s);
+                  Buckets &b, hipStream_t s, bool by_degree = false);
 // 16x16 tile census of the plan's graph (fills the plan's tile arrays)
 int build_tiles(gnn_plan_s *p, int32_t min_nnz, hipStream_t s);
 }  // namespace gnn

@@ -453,11 +453,11 @@ __global__ void k_low32_i32(const uint64_t *keys, int64_t n, int32_t *out) {
 
 // light launch order (see k_sched_keys); order 0 keeps the light list
 static int build_sched(const int32_t *indptr, int32_t T, int64_t max_deg, int32_t sched_order, Buckets &b,
-                       hipStream_t s) {
-    GNN_TRY(dev_alloc(b.sched, (size_t)std::max(1, b.n_light) * 4));
+                       DevBuf &dst, hipStream_t s) {
+    GNN_TRY(dev_alloc(dst, (size_t)std::max(1, b.n_light) * 4));
     if (b.n_light == 0) return GNN_OK;
     if (!sched_order) {
-        GNN_HIP(hipMemcpyAsync(b.sched.p, b.light.p, (size_t)b.n_light * 4, hipMemcpyDeviceToDevice, s));
+        GNN_HIP(hipMemcpyAsync(dst.p, b.light.p, (size_t)b.n_light * 4, hipMemcpyDeviceToDevice, s));
         return GNN_OK;
     }
     const int64_t cap = std::min<int64_t>(T, max_deg);
@@ -472,7 +472,7 @@ static int build_sched(const int32_t *indptr, int32_t T, int64_t max_deg, int32_
                        sched_order, hoist, keys);
     int rc = radix_sort(keys, kt, m, 32 + (sched_order == 1 ? bits_for(cap + 2) : 7), scr, s);
     if (rc == GNN_OK) {
-        hipLaunchKernelGGL(k_low32_i32, grid1d(m), dim3(256), 0, s, keys, m, as<int32_t>(b.sched));
+        hipLaunchKernelGGL(k_low32_i32, grid1d(m), dim3(256), 0, s, keys, m, as<int32_t>(dst));
         if (hipStreamSynchronize(s) != hipSuccess) {
             set_hip_error(hipGetLastError(), "light schedule");
             rc = GNN_ERR_HIP;
@@ -483,7 +483,7 @@ static int build_sched(const int32_t *indptr, int32_t T, int64_t max_deg, int32_
 }
 
 int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_t W, int32_t sched_order,
-                  Buckets &b, hipStream_t s) {
+                  Buckets &b, hipStream_t s, bool by_degree) {
     const int64_t span = (int64_t)C * W;
     DevBuf tmp;
     const int64_t sc = scan_scratch(n);
@@ -529,7 +529,9 @@ int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_
             rc = GNN_ERR_HIP;
             goto done;
         }
-        rc = build_sched(indptr, T, (int64_t)ends[1] - ends[0], sched_order, b, s);
+        rc = build_sched(indptr, T, (int64_t)ends[1] - ends[0], sched_order, b, b.sched, s);
+        if (rc == GNN_OK && by_degree)
+            rc = build_sched(indptr, T, (int64_t)ends[1] - ends[0], 1, b, b.by_degree, s);
     }
 done:
     dev_free(tmp);
@@ -544,6 +546,45 @@ __global__ void k_validate(const int32_t *indptr, const int32_t *indices, int32_
         const int32_t v = indices[i];
         if (v < 0 || v >= n) *err = 1;
     }
+}
+
+// sortedness of the rows: mark row starts, then look for a descending pair inside a row
+__global__ void k_row_starts(const int32_t *indptr, int32_t n, uint8_t *start) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n && indptr[i + 1] > indptr[i]) start[indptr[i]] = 1;
+}
+
+__global__ void k_fill_u8(uint8_t *p, int64_t n, uint8_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+__global__ void k_unsorted(const int32_t *indices, int64_t e, const uint8_t *start, int32_t *flag) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k > 0 && k < e && !start[k] && indices[k - 1] > indices[k]) *flag = 1;
+}
+
+static int check_rows_sorted(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, hipStream_t s,
+                             bool *sorted) {
+    *sorted = true;
+    if (e < 2) return GNN_OK;
+    DevBuf tmp;
+    GNN_TRY(dev_alloc(tmp, (size_t)e + 64));
+    int32_t *flag = reinterpret_cast<int32_t *>(tmp.p);
+    uint8_t *start = reinterpret_cast<uint8_t *>(tmp.p) + 64;
+    hipLaunchKernelGGL(k_set_i32, dim3(1), dim3(1), 0, s, flag, 0);
+    hipLaunchKernelGGL(k_fill_u8, grid1d(e), dim3(256), 0, s, start, e, (uint8_t)0);
+    hipLaunchKernelGGL(k_row_starts, grid1d(n), dim3(256), 0, s, indptr, n, start);
+    hipLaunchKernelGGL(k_unsorted, grid1d(e), dim3(256), 0, s, indices, e, start, flag);
+    int32_t h = 0;
+    int rc = GNN_OK;
+    if (hipMemcpyAsync(&h, flag, 4, hipMemcpyDeviceToHost, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+        set_hip_error(hipGetLastError(), "gnn_plan_create sortedness");
+        rc = GNN_ERR_HIP;
+    }
+    dev_free(tmp);
+    *sorted = h == 0;
+    return rc;
 }
 
 int build_transpose(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t m, DevBuf &cindptr,
@@ -580,7 +621,8 @@ using namespace gnn;
 
 int64_t gnn_plan_s::structure_bytes() const {
     int64_t t = 0;
-    for (const DevBuf *b : {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &fwd.sched, &cindptr, &cindices,
+    for (const DevBuf *b : {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &fwd.sched, &fwd.by_degree,
+                            &cindptr, &cindices,
                             &bwd.light, &bwd.heavy, &bwd.groups, &bwd.partial_ofs, &bwd.sched, &tile_rc, &tile_mask,
                             &tile_ptr, &trb, &rindptr, &rindices, &light_nt, &ctile, &ctile_ptr, &tcb,
                             &rcindptr, &rcindices, &c_light_nt})
@@ -698,9 +740,12 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
     p->opts = o;
     int rc = GNN_OK;
     DevBuf tmp;
+    if (dev_alloc(tmp, 64) != GNN_OK) {
+        delete p;
+        return GNN_ERR_OOM;
+    }
     {
         // validate structure
-        GNN_TRY(dev_alloc(tmp, 64));
         int32_t *err = as<int32_t>(tmp);
         int32_t herr = 0;
         hipLaunchKernelGGL(k_set_i32, dim3(1), dim3(1), 0, stream, err, 0);
@@ -715,9 +760,10 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
         }
         dev_free(tmp);
     }
+    if (rc == GNN_OK) rc = check_rows_sorted(indptr, indices, n_nodes, n_edges, stream, &p->rows_sorted);
     if (rc == GNN_OK)
         rc = build_buckets(indptr, n_nodes, o.light_threshold, o.chunk, o.waves_per_group, o.sched_order, p->fwd,
-                           stream);
+                           stream, true);
     if (rc == GNN_OK && o.want_csc) {
         rc = build_transpose(indptr, indices, n_nodes, n_edges, p->cindptr, p->cindices, stream);
         if (rc == GNN_OK) {
@@ -789,6 +835,8 @@ int gnn_plan_export(gnn_plan_t p, gnn_plan_info *info) {
     info->structure_bytes = p->structure_bytes();
     info->workspace_bytes = (int64_t)p->ws.bytes;
     info->largest_workspace_alloc = p->largest_ws;
+    info->rows_sorted = p->rows_sorted ? 1 : 0;
+    info->light_by_degree = as<int32_t>(p->fwd.by_degree);
     return GNN_OK;
 }
 

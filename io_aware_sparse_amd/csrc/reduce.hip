@@ -70,19 +70,24 @@ struct RedParams {
     float *part;                       // backward: [n_groups][F] fp32 group partials
 };
 
+// With RPW rows per wave the 64 lanes split into RPW row groups of 64/RPW
+// lanes, each holding G/RPW edge groups of LR lanes (RPW = 1: one row, G
+// edge groups).
 struct RLane {
-    int lane, g, c;     // lane, edge group, lane within the group
+    int lane, g, c;     // lane, edge group within the row group, lane within the edge group
+    int rg0;            // first lane of the row group
     int slice;          // 16-byte slice of the row this lane holds
     bool act;           // slice < L
     int64_t col;        // first element of the slice
 };
 
-template <int NV>
+template <int NV, int RPW = 1>
 __device__ __forceinline__ RLane rlane(const RedGeom &G, int fg) {
     RLane r;
     r.lane = lane_id();
     const int LR = 1 << G.lr_shift;
-    r.g = r.lane >> G.lr_shift;
+    r.rg0 = r.lane & ~(kWave / RPW - 1);
+    r.g = (r.lane - r.rg0) >> G.lr_shift;
     r.c = r.lane & (LR - 1);
     r.slice = fg * kWave + r.c;
     r.act = r.slice < G.L;
@@ -92,41 +97,63 @@ __device__ __forceinline__ RLane rlane(const RedGeom &G, int fg) {
 
 // Does (v, j) beat the current best (b, bj)? Empty candidates (j < 0) never
 // do; any candidate beats an empty best; equal values go to the smaller source.
+// (bitwise & and | on purpose: no short-circuit branches, the callers' updates stay selects)
 template <int OP>
 __device__ __forceinline__ bool better(float v, int j, float b, int bj) {
     const bool strict = OP == GNN_REDUCE_MAX ? (v > b) : (v < b);
-    return j >= 0 && (bj < 0 || strict || (v == b && j < bj));
+    return (j >= 0) & ((bj < 0) | strict | ((v == b) & (j < bj)));
 }
 
 __device__ __forceinline__ int xor_int(int x, int off) { return __shfl_xor(x, off, kWave); }
 
-template <class T, int OP, int MSG, int U>
+// SORTED: the row lists its sources in non-decreasing order, so a lane meets
+// its edges' sources in non-decreasing order and a strict comparison alone
+// keeps the smallest source among equal values; the group merge below still
+// applies the full rule. Otherwise every step applies the full rule.
+template <class T, int OP, int MSG, int U, bool SORTED, int RPW = 1>
 __device__ __forceinline__ void red_stream(const RedParams &P, const RLane &lp, int node, int e0, int e1,
                                            float (&best)[Vec<T>::N], int (&bj)[Vec<T>::N]) {
     using VT = Vec<T>;
     constexpr int NV = VT::N;
+    constexpr float kWorst = OP == GNN_REDUCE_MAX ? -INFINITY : INFINITY;
     const RedGeom &G = P.g;
     const int64_t F = G.F;
     float xi[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         xi[k] = 0.f;
-        best[k] = 0.f;
+        best[k] = SORTED ? kWorst : 0.f;
         bj[k] = -1;
     }
-    if (MSG == GNN_MSG_DIFF && lp.act) VT::unpack(load_vec<T>(P.X, (int64_t)node * F + lp.col), xi);
-    const int S = min(kWave, G.G * U);
-    const int UE = S / G.G;
-    int jn = (lp.lane < S && e0 + lp.lane < e1) ? P.indices[e0 + lp.lane] : -1;
-    for (int base = e0; base < e1; base += S) {
+    if (MSG == GNN_MSG_DIFF && lp.act && node >= 0) VT::unpack(load_vec<T>(P.X, (int64_t)node * F + lp.col), xi);
+    constexpr int kLanesRG = kWave / RPW;
+    const int GR = G.G / RPW;                 // edge groups of this row
+    const int S = min(kLanesRG, GR * U);      // edges per step of this row
+    const int UE = S / GR;
+    const int li = lp.lane - lp.rg0;
+    int jn = (li < S && e0 + li < e1) ? P.indices[e0 + li] : -1;
+    // steps until every row group of the wave has used up its edges (one row: until base >= e1)
+    for (int base = e0; RPW == 1 ? base < e1 : __any(base < e1); base += S) {
         const int jc = jn;
-        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? P.indices[base + S + lp.lane] : -1;
+        if (RPW == 1) {
+            if (base + S < e1) jn = (li < S && base + S + li < e1) ? P.indices[base + S + li] : -1;
+        } else {
+            jn = (li < S && base + S + li < e1) ? P.indices[base + S + li] : -1;
+        }
         int j[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) j[u] = (u < UE) ? __shfl(jc, u * G.G + lp.g, kWave) : -1;
+        for (int u = 0; u < U; ++u) j[u] = (u < UE) ? __shfl(jc, lp.rg0 + u * GR + lp.g, kWave) : -1;
+        // every lane loads (a lane without an edge, or past the row's slices, reads slice 0 of row 0 and
+        // ignores it), so the loads need no branch; the updates below are selects
         typename VT::raw r[U];
+        bool ok[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) r[u] = (lp.act && j[u] >= 0) ? load_vec<T>(P.X, (int64_t)j[u] * F + lp.col) : VT::zero();
+        for (int u = 0; u < U; ++u) {
+            ok[u] = lp.act & (j[u] >= 0);
+            const int row = ok[u] ? j[u] : 0;
+            const int64_t col = ok[u] ? lp.col : 0;
+            r[u] = load_vec<T>(P.X, (int64_t)row * F + col);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float v[NV];
@@ -134,24 +161,51 @@ __device__ __forceinline__ void red_stream(const RedParams &P, const RLane &lp, 
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
                 const float m = MSG == GNN_MSG_DIFF ? v[k] - xi[k] : v[k];
-                if (better<OP>(m, j[u], best[k], bj[k])) {
-                    best[k] = m;
-                    bj[k] = j[u];
-                }
+                const bool take = SORTED ? (ok[u] & (OP == GNN_REDUCE_MAX ? m > best[k] : m < best[k]))
+                                         : (ok[u] & better<OP>(m, j[u], best[k], bj[k]));
+                best[k] = take ? m : best[k];
+                bj[k] = take ? j[u] : bj[k];
             }
         }
     }
-    // merge the edge groups of the wave (lane c of every group ends with the same pair)
-    for (int off = 1 << G.lr_shift; off < kWave; off <<= 1) {
+    if (SORTED) {
+        // a group whose messages all equal the worst value (an infinity) took none of them: its first
+        // edge wins; a group without edges stays empty with value 0
+        const int e_first = e0 + lp.g;
+        const int j_first = e_first < e1 ? P.indices[e_first] : -1;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            if (bj[k] < 0) {
+                bj[k] = j_first;
+                if (j_first < 0) best[k] = 0.f;
+            }
+        }
+    }
+    // merge the edge groups of the row (lane c of every group ends with the same pair)
+    for (int off = 1 << G.lr_shift; off < kLanesRG; off <<= 1) {
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const float ov = xor_lane(best[k], off);
             const int oj = xor_int(bj[k], off);
-            if (better<OP>(ov, oj, best[k], bj[k])) {
-                best[k] = ov;
-                bj[k] = oj;
-            }
+            const bool take = better<OP>(ov, oj, best[k], bj[k]);
+            best[k] = take ? ov : best[k];
+            bj[k] = take ? oj : bj[k];
         }
+    }
+}
+
+// Output row slice: source messages are values of X itself (exact in the
+// storage type: bf16 keeps the high half of the fp32 image); difference
+// messages are rounded to the storage type (nearest even).
+template <class T, int MSG>
+__device__ __forceinline__ typename Vec<T>::raw pack_out(const float (&x)[Vec<T>::N]) {
+    if constexpr (Vec<T>::bytes == 2 && MSG == GNN_MSG_SRC) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = (__float_as_uint(x[2 * k]) >> 16) | (__float_as_uint(x[2 * k + 1]) & 0xFFFF0000u);
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+        return Vec<T>::pack(x);
     }
 }
 
@@ -191,7 +245,7 @@ __device__ __forceinline__ int heavy_of_group(const int32_t *partial_ofs, int n_
     return lo;
 }
 
-template <class T, int OP, int MSG, int U>
+template <class T, int OP, int MSG, int U, bool SORTED, int RPW>
 __global__ __launch_bounds__(512) void k_red_main(RedParams P) {
     using VT = Vec<T>;
     constexpr int NV = VT::N;
@@ -205,7 +259,7 @@ __global__ __launch_bounds__(512) void k_red_main(RedParams P) {
         const int node = P.groups[3 * grp], g0 = P.groups[3 * grp + 1], g1 = P.groups[3 * grp + 2];
         const int e0 = min(g1, g0 + w * P.C), e1 = min(g1, e0 + P.C);
         const RLane lp = rlane<NV>(G, fg);
-        red_stream<T, OP, MSG, U>(P, lp, node, e0, e1, best, bj);
+        red_stream<T, OP, MSG, U, SORTED, 1>(P, lp, node, e0, e1, best, bj);
         if (lp.g != 0 || !lp.act) return;
         const int h = heavy_of_group(P.partial_ofs, P.n_heavy, grp);
         unsigned long long *slot = P.keys + (int64_t)h * G.F + lp.col;
@@ -220,15 +274,26 @@ __global__ __launch_bounds__(512) void k_red_main(RedParams P) {
         return;
     }
     const int64_t item = (int64_t)(blockIdx.x - heavy_blocks) * P.W + w;
-    const int64_t ni = item / G.NFG;
-    if (ni >= P.n_light) return;
-    const int fg = (int)(item % G.NFG);
-    const int node = P.light ? P.light[ni] : (int)ni;
-    const RLane lp = rlane<NV>(G, fg);
-    red_stream<T, OP, MSG, U>(P, lp, node, P.indptr[node], P.indptr[node + 1], best, bj);
-    if (lp.g != 0 || !lp.act) return;
-    const int64_t off = (int64_t)node * G.F + lp.col;
-    store_vec<T>(P.out, off, VT::pack(best));
+    int node;
+    int fg = 0;
+    const RLane lp = rlane<NV, RPW>(G, 0);
+    if (RPW == 1) {
+        const int64_t ni = item / G.NFG;
+        if (ni >= P.n_light) return;
+        fg = (int)(item % G.NFG);
+        node = P.light ? P.light[ni] : (int)ni;
+    } else {                                  // RPW rows of the light list per wave (NFG == 1)
+        const int64_t ni0 = item * RPW;
+        if (ni0 >= P.n_light) return;
+        const int64_t ni = ni0 + lp.rg0 / (kWave / RPW);
+        node = ni < P.n_light ? P.light[ni] : -1;
+    }
+    const RLane lq = RPW == 1 ? rlane<NV>(G, fg) : lp;
+    const int e0 = node >= 0 ? P.indptr[node] : 0, e1 = node >= 0 ? P.indptr[node + 1] : 0;
+    red_stream<T, OP, MSG, U, SORTED, RPW>(P, lq, node, e0, e1, best, bj);
+    if (lq.g != 0 || !lq.act || node < 0) return;
+    const int64_t off = (int64_t)node * G.F + lq.col;
+    store_vec<T>(P.out, off, pack_out<T, MSG>(best));
     if (P.arg) {
         int4 *a = reinterpret_cast<int4 *>(P.arg + off);
 #pragma unroll
@@ -448,15 +513,36 @@ static int red_check(gnn_plan_t plan, const int32_t *indptr, const int32_t *indi
     return GNN_OK;
 }
 
+template <class T, int OP, int MSG, bool SORTED, int RPW>
+static int launch_red_main(gnn_plan_t plan, const RedParams &P, hipStream_t s) {
+    constexpr int U = 4;
+    const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NFG : ((int64_t)P.n_light + RPW - 1) / RPW;
+    const int64_t blocks = (int64_t)P.n_groups * P.g.NFG + (light_waves + P.W - 1) / P.W;
+    if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
+    return launch(plan, K_RED_MAIN, k_red_main<T, OP, MSG, U, SORTED, RPW>, dim3((unsigned)blocks), dim3(64 * P.W),
+                  0, s, P);
+}
+
+// Sorted rows on a plan, rows of up to 16 lanes (256 bytes): the light rows
+// run from the descending-degree list, 4 per wave, so rows of similar length
+// share a wave and each row merges only its own edge groups. Otherwise (wider
+// rows, where one row already fills the wave's edge groups and packing was
+// measured slower, or unsorted rows) one row per wave.
 template <class T, int OP, int MSG>
 static int run_red_fwd(gnn_plan_t plan, RedParams &P, hipStream_t s) {
-    constexpr int U = 4;
-    const int64_t lb = ((int64_t)P.n_light * P.g.NFG + P.W - 1) / P.W;
-    const int64_t blocks = (int64_t)P.n_groups * P.g.NFG + lb;
-    if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
     const int64_t nk = (int64_t)P.n_heavy * P.g.F;
     if (nk) GNN_TRY(launch(plan, K_RED_INIT, k_red_init<OP>, grid1d(nk), dim3(256), 0, s, P.keys, nk));
-    GNN_TRY(launch(plan, K_RED_MAIN, k_red_main<T, OP, MSG, U>, dim3((unsigned)blocks), dim3(64 * P.W), 0, s, P));
+    if (plan && plan->rows_sorted) {
+        if (P.g.NFG == 1 && P.g.G >= 4) {
+            RedParams Q = P;
+            Q.light = as<int32_t>(plan->fwd.by_degree);
+            GNN_TRY((launch_red_main<T, OP, MSG, true, 4>(plan, Q, s)));
+        } else {
+            GNN_TRY((launch_red_main<T, OP, MSG, true, 1>(plan, P, s)));
+        }
+    } else {
+        GNN_TRY((launch_red_main<T, OP, MSG, false, 1>(plan, P, s)));
+    }
     if (nk) GNN_TRY(launch(plan, K_RED_FINAL, k_red_final<T, OP, MSG>, grid1d(nk), dim3(256), 0, s, P));
     return GNN_OK;
 }

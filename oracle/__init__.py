@@ -463,13 +463,14 @@ def segment_reduce(indptr, indices, X, op: str = "max", msg: str = "src", rows=N
 
 
 def segment_reduce_bwd(indptr, indices, dOut, arg, msg: str = "src", n_nodes: Optional[int] = None,
-                       want_scale: bool = False):
+                       want_scale: bool = False, rows=None):
     """Gradient of segment_reduce in fp64: each (i, f) with a winner j sends
     dOut[i, f] to X[j, f], and for msg "diff" also -dOut[i, f] to X[i, f]
     (the message is X[j] - X[i]). A source that appears several times in a
     row receives the gradient once, through the winning entry.
-    Returns dX float64 [N, F]; with want_scale also the summation scale
-    S = the sum of |terms| added into each element."""
+    dOut and arg hold rows 0..N-1, or the rows listed in `rows` (then only
+    their terms are summed). Returns dX float64 [N, F]; with want_scale also
+    the summation scale S = the sum of |terms| added into each element."""
     dOut = np.asarray(dOut, np.float64)
     arg = np.asarray(arg, np.int64)
     N = int(n_nodes if n_nodes is not None else dOut.shape[0])
@@ -478,16 +479,17 @@ def segment_reduce_bwd(indptr, indices, dOut, arg, msg: str = "src", n_nodes: Op
     F = dOut.shape[1]
     dX = np.zeros((N, F), np.float64)
     won = arg >= 0
-    i_idx, f_idx = np.nonzero(won)
-    np.add.at(dX, (arg[i_idx, f_idx], f_idx), dOut[i_idx, f_idx])
+    r_idx, f_idx = np.nonzero(won)
+    i_idx = r_idx if rows is None else np.asarray(rows, np.int64)[r_idx]
+    np.add.at(dX, (arg[r_idx, f_idx], f_idx), dOut[r_idx, f_idx])
     if msg == "diff":
-        np.add.at(dX, (i_idx, f_idx), -dOut[i_idx, f_idx])
+        np.add.at(dX, (i_idx, f_idx), -dOut[r_idx, f_idx])
     if not want_scale:
         return dX
     S = np.zeros((N, F), np.float64)
-    np.add.at(S, (arg[i_idx, f_idx], f_idx), np.abs(dOut[i_idx, f_idx]))
+    np.add.at(S, (arg[r_idx, f_idx], f_idx), np.abs(dOut[r_idx, f_idx]))
     if msg == "diff":
-        np.add.at(S, (i_idx, f_idx), np.abs(dOut[i_idx, f_idx]))
+        np.add.at(S, (i_idx, f_idx), np.abs(dOut[r_idx, f_idx]))
     return dX, S
 
 

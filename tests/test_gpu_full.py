@@ -68,6 +68,7 @@ def test_full_size(g, name):
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d[k], ref_b[k]), k
     assert np.array_equal(d["light_sched"], oracle.launch_order(rp, ref_b["light"])), "light_sched"
+    assert np.array_equal(d["light_by_degree"], oracle.launch_order(rp, ref_b["light"], 1)), "light_by_degree"
     if wl.backward:
         cip, cix = oracle.csc(rp, rx, n)
         assert np.array_equal(d["cindptr"], cip) and np.array_equal(d["cindices"], cix), "csc"
@@ -145,3 +146,58 @@ def test_full_size_gatv2_backward(g):
     _check("dXD", _host(gxd)[rows], ref["dXD"], ref["SdXD"], "f32")
     _check("dXS", _host(gxs)[srcs], ref["dXS"], ref["SdXS"], "f32")
     _check("d_att", gda.cpu().numpy(), ref["d_att"], ref["Sd_att"], "f32")
+
+
+def _bits32(x):
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+@pytest.mark.parametrize("name", ["maxpool_zipf21_n100k", "maxpool_chunglu22_n2450k"])
+def test_full_size_reduce(g, name):
+    """Max / min reduction at full size, default plan: values and winners bit
+    for bit on every heavy row and a seeded sample of light rows; the
+    gradient against the oracle on sampled sources (Zipf graph) or through
+    its column-sum identity (every non-empty row's dOut lands exactly once)."""
+    import torch
+    say("full-size reduce", name)
+    wl = workloads.make(name, backward=True)
+    n, F = wl.n_nodes, wl.heads * wl.dim
+    ip, ix = g.gnn_csr_build(torch.from_numpy(wl.src).cuda(), torch.from_numpy(wl.dst).cuda(), n)
+    rp, rx = oracle.csr_build(wl.src, wl.dst, n)
+    assert np.array_equal(ip.cpu().numpy(), rp) and np.array_equal(ix.cpu().numpy(), rx)
+    plan = g.gnn_plan_create(ip, ix, want_csc=True)
+    heavy = oracle.bucketing(rp, 512, 512, 4)["heavy"]
+    rng = np.random.default_rng(79)
+    rows = _sample(rng, n, heavy, N_SAMPLE)
+    X = wl.feats["X"].reshape(n, F)
+    Xd = _dev(wl, "X").reshape(n, F)
+    gO = _dev(wl, "dO").reshape(n, F)
+    for op, msg in (("max", "src"), ("min", "diff")):
+        out, arg = g.gnn_reduce_fwd(plan, ip, ix, Xd, op, msg)
+        torch.cuda.synchronize()
+        ref = oracle.segment_reduce(rp, rx, X, op, msg, rows=rows)
+        ro = oracle.round_bf16(ref["out"]) if (wl.dtype == "bf16" and msg == "diff") else ref["out"]
+        ga = arg.cpu().numpy()[rows]
+        go = out.float().cpu().numpy()[rows]
+        say(f"  {op} {msg}: {rows.size} rows ({heavy.size} heavy), winners equal "
+            f"{np.mean(ga == ref['arg']):.6f}, values equal {np.mean(_bits32(go) == _bits32(ro)):.6f}")
+        assert np.array_equal(ga, ref["arg"]) and np.array_equal(_bits32(go), _bits32(ro)), (op, msg)
+        dX = g.gnn_reduce_bwd(plan, ip, ix, gO, arg, msg)
+        torch.cuda.synchronize()
+        if wl.n_nodes <= 200_000:
+            full = oracle.segment_reduce(rp, rx, X, op, msg)["arg"]
+            rdX, S = oracle.segment_reduce_bwd(rp, rx, wl.feats["dO"].reshape(n, F), full, msg, want_scale=True)
+            cip, _ = oracle.csc(rp, rx, n)
+            srcs = _sample(rng, n, oracle.bucketing(cip, 512, 512, 4)["heavy"], N_SAMPLE)
+            _check(f"dX {op} {msg}", _host(dX)[srcs], rdX[srcs], S[srcs], wl.dtype)
+        else:
+            nonempty = np.diff(rp) > 0
+            col = dX.double().sum(0).cpu().numpy()
+            want = wl.feats["dO"].reshape(n, F)[nonempty].astype(np.float64).sum(0)
+            if msg == "diff":
+                want = want - want                   # each row's dOut comes in once and goes out once
+            mag = np.abs(wl.feats["dO"].reshape(n, F)).astype(np.float64).sum(0)
+            err = np.max(np.abs(col - want) / mag)
+            say(f"  dX column sums: max |sum - expected| / sum|dOut| = {err:.2e}")
+            assert err <= (1e-6 if wl.dtype == "f32" else 1e-2), err
+        del out, arg, dX

@@ -189,3 +189,48 @@ def test_reduce_bwd_needs_csc(g):
     _, arg = g.gnn_reduce_fwd(plan, ip_d, ix_d, X)
     with pytest.raises(g.GnnError):
         g.gnn_reduce_bwd(plan, ip_d, ix_d, X, arg)
+
+
+def test_rows_sorted_flag_and_unsorted_rows(g):
+    """A plan records whether rows are sorted; rows in any order give the same
+    exact result (the smallest winning source), through the general path."""
+    rng = np.random.default_rng(21)
+    n, F = 900, 32
+    ip, ix = _graph(rng, n, 12, hub_deg=2000)
+    X = _feats(rng, n, F, "f32")
+    ixs = ix.copy()
+    for i in range(n):                       # shuffle every row
+        seg = ixs[ip[i]:ip[i + 1]]
+        rng.shuffle(seg)
+    assert not np.array_equal(ixs, ix)
+    sorted_plan = g.gnn_plan_create(dev_i32(ip), dev_i32(ix))
+    assert g.gnn_plan_export(sorted_plan)["rows_sorted"] == 1
+    ip_d, ixs_d = dev_i32(ip), dev_i32(ixs)
+    for plan in (None, g.gnn_plan_create(ip_d, ixs_d, light_threshold=16, chunk=8, waves_per_group=4)):
+        if plan is not None:
+            assert g.gnn_plan_export(plan)["rows_sorted"] == 0
+        for op in ("max", "min"):
+            for msg in ("src", "diff"):
+                out, arg = g.gnn_reduce_fwd(plan, ip_d, ixs_d, dev_feat(X, "f32"), op, msg)
+                ro, ra = _ref(ip, ixs, X, op, msg, "f32")
+                assert np.array_equal(arg.cpu().numpy(), ra), (op, msg)
+                assert np.array_equal(_bits(out.cpu().numpy()), _bits(ro)), (op, msg)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_reduce_infinities(g, dtype):
+    """Rows whose messages are all -inf (max) or all +inf (min) still pick the
+    smallest source; mixed rows pick the finite extreme."""
+    rng = np.random.default_rng(22)
+    n, F = 800, 16
+    ip, ix = _graph(rng, n, 6, hub_deg=1200)
+    levels = np.array([-np.inf, -1.0, 0.0, 2.0, np.inf], np.float32)
+    X = rng.choice(levels, (n, F), p=[0.4, 0.1, 0.05, 0.05, 0.4])
+    ip_d, ix_d = dev_i32(ip), dev_i32(ix)
+    for plan in (None, g.gnn_plan_create(ip_d, ix_d, light_threshold=4, chunk=3, waves_per_group=2),
+                 g.gnn_plan_create(ip_d, ix_d)):
+        for op in ("max", "min"):
+            out, arg = g.gnn_reduce_fwd(plan, ip_d, ix_d, dev_feat(X, dtype), op, "src")
+            ro, ra = _ref(ip, ix, X, op, "src", dtype)
+            assert np.array_equal(arg.cpu().numpy(), ra), op
+            assert np.array_equal(_bits(_gpu_out_f32(out)), _bits(ro)), op

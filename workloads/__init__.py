@@ -23,6 +23,9 @@ of the case it names:
                           inter-community in-edges per node, H=8, D=64, bf16,
                           with an upstream gradient
   gt_comm16_n1m_deg27     same communities + 11 inter-community in-edges
+  maxpool_zipf21_n100k    the Zipf(2.1) graph with F = 128 fp32 features per
+                          node, for the neighbourhood max / min reduction
+  maxpool_chunglu22_n2450k  the degree-2.2 Chung-Lu graph with F = 128 bf16
 
 Self-loops are never emitted here; the CSR builder adds exactly one per node.
 
@@ -136,7 +139,7 @@ def round_to_bf16(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 @dataclass
 class Workload:
     name: str
-    kind: str                 # "gt" (dot-product) or "gatv2"
+    kind: str                 # "gt" (dot-product), "gatv2" or "reduce" (max / min of features X)
     n_nodes: int
     src: np.ndarray           # int32 [E0], edge src -> dst, no self-pairs
     dst: np.ndarray           # int32 [E0]
@@ -303,6 +306,11 @@ SPECS = {
     "gt_chunglu22_n2450k": dict(seed=1004, kind="gt", n=2_450_000, heads=4, dim=32, dtype="bf16", backward=False),
     "gt_comm16_n1m_deg100": dict(seed=1005, kind="gt", n=1_000_000, heads=8, dim=64, dtype="bf16", backward=True),
     "gt_comm16_n1m_deg27": dict(seed=1005, kind="gt", n=1_000_000, heads=8, dim=64, dtype="bf16", backward=True),
+    # neighbourhood max / min reduction on the graphs above (same recipe and seed, hence the same graph)
+    "maxpool_zipf21_n100k": dict(seed=1003, kind="reduce", graph="gatv2_zipf21_n100k", n=100_000, heads=1,
+                                 dim=128, dtype="f32", backward=False),
+    "maxpool_chunglu22_n2450k": dict(seed=1004, kind="reduce", graph="gt_chunglu22_n2450k", n=2_450_000,
+                                     heads=1, dim=128, dtype="bf16", backward=False),
 }
 
 
@@ -370,7 +378,7 @@ def make(name: str, n_nodes: Optional[int] = None, features: bool = True,
     n = int(n_nodes or spec["n"])
     root = np.random.SeedSequence([spec["seed"], n])
     g_ss, f_ss = root.spawn(2)
-    src, dst, meta = _graph(name, n, g_ss)
+    src, dst, meta = _graph(spec.get("graph", name), n, g_ss)
     wl = Workload(name=name, kind=spec["kind"], n_nodes=n, src=src, dst=dst,
                   heads=spec["heads"], dim=spec["dim"], dtype=spec["dtype"],
                   backward=spec["backward"], seed=spec["seed"], meta=meta)
@@ -383,7 +391,7 @@ def add_features(wl: Workload, f_ss: Optional[np.random.SeedSequence] = None) ->
     if f_ss is None:
         f_ss = np.random.SeedSequence([wl.seed, wl.n_nodes]).spawn(2)[1]
     shape = (wl.n_nodes, wl.heads, wl.dim)
-    names = ["Q", "K", "V"] if wl.kind == "gt" else ["XD", "XS"]
+    names = {"gt": ["Q", "K", "V"], "gatv2": ["XD", "XS"], "reduce": ["X"]}[wl.kind]
     kids = f_ss.spawn(len(names) + 2)
     if wl.backward:
         names.append("dO")
