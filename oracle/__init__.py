@@ -432,6 +432,97 @@ def gatv2_bwd(indptr, indices, XD, XS, att, dO, V=None, slope: float = 0.2, rows
 
 
 # ---------------------------------------------------------------------------
+# graph reordering
+# ---------------------------------------------------------------------------
+ORDERS = {"degree": 0, "rcm": 1}
+
+
+def total_degree(indptr, indices, n_nodes: int) -> np.ndarray:
+    """deg(v) = entries of v's row (in-degree) + entries naming v (out-degree)."""
+    ip = np.asarray(indptr, np.int64)
+    return np.diff(ip) + np.bincount(np.asarray(indices, np.int64), minlength=n_nodes)[:n_nodes]
+
+
+def reorder(indptr, indices, n_nodes: int, method: str = "rcm") -> np.ndarray:
+    """Node order for relabelling, as perm[new id] = old id (int32).
+
+    "degree": descending total degree, ties by ascending id.
+    "rcm": reverse Cuthill-McKee on the symmetrised graph (a node's
+    neighbours are its row's sources and the rows naming it). Cuthill-McKee
+    visits components one after another, each from its unvisited node of
+    smallest (degree, id), breadth first: when a node is taken from the
+    queue its not yet visited neighbours are appended in ascending (degree,
+    id). The permutation is that visiting order reversed. Plain queue code
+    (pure Python loops: small and medium graphs only)."""
+    n = int(n_nodes)
+    ip = np.asarray(indptr, np.int64)
+    ix = np.asarray(indices, np.int64)
+    deg = total_degree(ip, ix, n)
+    if method == "degree":
+        return np.lexsort((np.arange(n), -deg)).astype(np.int32)
+    if method != "rcm":
+        raise ValueError(method)
+    # symmetrised adjacency: in-neighbours (row) and out-neighbours (column)
+    rows = np.repeat(np.arange(n, dtype=np.int64), np.diff(ip))
+    src = np.concatenate([ix, rows])
+    dst = np.concatenate([rows, ix])
+    o = np.argsort(dst, kind="stable")
+    nb = src[o]
+    nptr = np.concatenate([[0], np.cumsum(np.bincount(dst, minlength=n))])
+    key = deg * n + np.arange(n)                       # (degree, id) as one sortable number
+    visited = np.zeros(n, bool)
+    order = []
+    starts = np.argsort(key, kind="stable")            # candidate start nodes by (degree, id)
+    si = 0
+    from collections import deque
+    while len(order) < n:
+        while visited[starts[si]]:
+            si += 1
+        s = int(starts[si])
+        visited[s] = True
+        order.append(s)
+        q = deque([s])
+        while q:
+            u = q.popleft()
+            cand = np.unique(nb[nptr[u]:nptr[u + 1]])
+            cand = cand[~visited[cand]]
+            cand = cand[np.argsort(key[cand], kind="stable")]
+            for v in cand:
+                visited[v] = True
+                order.append(int(v))
+                q.append(int(v))
+    return np.asarray(order[::-1], np.int32)
+
+
+def permute_graph(indptr, indices, perm):
+    """CSR of the relabelled graph: new row r is old row perm[r], each source
+    j renamed to its new id, rows sorted ascending (entries kept, repeats
+    included). Returns (indptr int32, indices int32)."""
+    perm = np.asarray(perm, np.int64)
+    n = perm.size
+    inv = np.empty(n, np.int64)
+    inv[perm] = np.arange(n)
+    ip = np.asarray(indptr, np.int64)
+    ix = np.asarray(indices, np.int64)
+    rows_old = np.repeat(np.arange(n, dtype=np.int64), np.diff(ip))
+    r = inv[rows_old]
+    c = inv[ix]
+    o = np.lexsort((c, r))
+    new_ip = np.concatenate([[0], np.cumsum(np.bincount(r, minlength=n))]).astype(np.int32)
+    return new_ip, c[o].astype(np.int32)
+
+
+def bandwidth(indptr, indices) -> int:
+    """max |i - j| over the entries (i, j) of the CSR (0 for no entries)."""
+    ip = np.asarray(indptr, np.int64)
+    ix = np.asarray(indices, np.int64)
+    if ix.size == 0:
+        return 0
+    rows = np.repeat(np.arange(ip.size - 1), np.diff(ip))
+    return int(np.max(np.abs(rows - ix)))
+
+
+# ---------------------------------------------------------------------------
 # degree-aware reduction layer
 # ---------------------------------------------------------------------------
 REDUCE_OPS = {"max": 0, "min": 1}
