@@ -357,7 +357,7 @@ def summarize(args) -> int:
 
 # ----------------------------------------------------------------- workload
 
-def setup(name, plan_opts, backward=None):
+def setup(name, plan_opts, backward=None, reorder="none"):
     import numpy as np
     import torch
 
@@ -372,8 +372,10 @@ def setup(name, plan_opts, backward=None):
 
     def feat(nm):
         if wl.dtype == "bf16":
-            return torch.from_numpy(wl.bits[nm].view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(wl.feats[nm]).to(dev)
+            t = torch.from_numpy(wl.bits[nm].view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(wl.feats[nm]).to(dev)
+        return t if perm is None else g.gnn_permute_rows(t, perm)
 
     src = torch.from_numpy(wl.src).to(dev)
     dst = torch.from_numpy(wl.dst).to(dev)
@@ -383,6 +385,16 @@ def setup(name, plan_opts, backward=None):
     torch.cuda.synchronize()
     t_csr = time.time() - t0
     del src, dst
+    perm, t_reorder, t_relabel = None, 0.0, 0.0
+    if reorder != "none":
+        t0 = time.time()
+        perm = g.gnn_reorder(indptr, indices, reorder)
+        torch.cuda.synchronize()
+        t_reorder = time.time() - t0
+        t0 = time.time()
+        indptr, indices = g.gnn_permute_graph(indptr, indices, perm)
+        torch.cuda.synchronize()
+        t_relabel = time.time() - t0
     t0 = time.time()
     plan = g.gnn_plan_create(indptr, indices, want_csc=wl.backward, **plan_opts)
     torch.cuda.synchronize()
@@ -398,7 +410,8 @@ def setup(name, plan_opts, backward=None):
             tensors["dX"] = torch.empty_like(tensors["X"])
         torch.cuda.synchronize()
         prep = dict(generate_s=round(t_gen, 3), csr_build_ms=round(1e3 * t_csr, 3),
-                    plan_create_ms=round(1e3 * t_plan, 3))
+                    plan_create_ms=round(1e3 * t_plan, 3), reorder=reorder, reorder_ms=round(1e3 * t_reorder, 3),
+                    relabel_ms=round(1e3 * t_relabel, 3))
         return wl, indptr, indices, plan, tensors, int(indices.numel()), prep
     if wl.kind == "gt":
         for nm in ("Q", "K", "V"):
@@ -419,7 +432,8 @@ def setup(name, plan_opts, backward=None):
             tensors[nm] = torch.empty_like(ref)
         tensors["d_att"] = torch.empty((H, D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    prep = dict(generate_s=round(t_gen, 3), csr_build_ms=round(1e3 * t_csr, 3), plan_create_ms=round(1e3 * t_plan, 3))
+    prep = dict(generate_s=round(t_gen, 3), csr_build_ms=round(1e3 * t_csr, 3), plan_create_ms=round(1e3 * t_plan, 3),
+                reorder=reorder, reorder_ms=round(1e3 * t_reorder, 3), relabel_ms=round(1e3 * t_relabel, 3))
     return wl, indptr, indices, plan, tensors, E, prep
 
 
@@ -538,7 +552,7 @@ def bench(args) -> int:
     opts = dict(light_threshold=args.light_threshold, chunk=args.chunk, waves_per_group=args.waves,
                 tile_density=args.tile_density, sched_order=args.sched_order)
     log(f"[bench] workload {args.workload}: generating and building the graph")
-    wl, indptr, indices, plan, T, E, prep = setup(args.workload, opts, True if args.backward else None)
+    wl, indptr, indices, plan, T, E, prep = setup(args.workload, opts, True if args.backward else None, args.reorder)
     info = g.gnn_plan_export(plan)
     N, H, D = wl.n_nodes, wl.heads, wl.dim
     s = 4 if wl.dtype == "f32" else 2
@@ -623,7 +637,7 @@ def bench(args) -> int:
             "storage": wl.dtype, "math": "f32",
             "light_threshold": args.light_threshold, "chunk": args.chunk, "waves_per_group": args.waves,
             "tile_density": args.tile_density, "tiles": int(info["n_tiles"]), "sched_order": args.sched_order,
-            "cache": CACHE_TEXT[args.cache],
+            "cache": CACHE_TEXT[args.cache], "reorder": args.reorder,
             "parallelism": "single GPU",
         },
         "other_cache": None if ms_other is None else {
@@ -647,7 +661,7 @@ def bench(args) -> int:
         "preprocess": prep,
         "wall_s_timed": round(wall, 4),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.reorder == "none":
         import oracle
         rp = indptr.cpu().numpy()
         rx = indices.cpu().numpy()
@@ -706,6 +720,8 @@ def main():
                     help="reduction workloads (maxpool_*): max or min")
     ap.add_argument("--msg", choices=("src", "diff"), default="src",
                     help="reduction workloads: message x_j (src) or x_j - x_i (diff)")
+    ap.add_argument("--reorder", choices=("none", "degree", "rcm"), default="none",
+                    help="relabel the graph and its feature rows before planning (gnn_reorder)")
     ap.add_argument("--tile-density", type=float, default=0.0,
                     help="16x16 tile threshold tau (0 disables the tile path)")
     ap.add_argument("--cache", choices=("flushed", "warm"), default="flushed",

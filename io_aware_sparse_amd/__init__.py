@@ -30,7 +30,9 @@ STATUS = {0: "GNN_OK", -1: "GNN_ERR_INVALID_ARG", -2: "GNN_ERR_UNSUPPORTED", -3:
 # exported symbols, in the order include/gnn_attn.h declares them
 EXPORTS = ["gnn_plan_opts_default", "gnn_csr_build", "gnn_plan_create", "gnn_plan_export", "gnn_plan_destroy",
            "gnn_attn_fwd", "gnn_attn_bwd", "gatv2_attn_fwd", "gatv2_attn_bwd", "gnn_plan_set_timing",
-           "gnn_plan_timing_read", "gnn_status_string", "gnn_reduce_fwd", "gnn_reduce_bwd"]
+           "gnn_plan_timing_read", "gnn_status_string", "gnn_reduce_fwd", "gnn_reduce_bwd", "gnn_reorder",
+           "gnn_permute_graph", "gnn_permute_rows"]
+ORDERS = {"degree": 0, "rcm": 1}      # gnn_order_t
 REDUCE_OPS = {"max": 0, "min": 1}     # gnn_reduce_op_t
 REDUCE_MSGS = {"src": 0, "diff": 1}   # gnn_msg_t
 
@@ -97,6 +99,9 @@ def lib():
         L.gatv2_attn_bwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, F, V, V, V, V, V, V, C.c_int, V]
         L.gnn_reduce_fwd.argtypes = [V, V, V, I32, I64, I32, V, V, V, C.c_int, C.c_int, C.c_int, V]
         L.gnn_reduce_bwd.argtypes = [V, V, V, I32, I64, I32, V, V, V, C.c_int, C.c_int, V]
+        L.gnn_reorder.argtypes = [V, V, I32, I64, C.c_int, V, V]
+        L.gnn_permute_graph.argtypes = [V, V, I32, I64, V, V, V, V]
+        L.gnn_permute_rows.argtypes = [V, V, I32, I64, V, I32, V]
         L.gnn_plan_set_timing.argtypes = [V, I32]
         L.gnn_plan_timing_read.argtypes = [V, I32, C.POINTER(C.c_char_p), C.POINTER(C.c_int32),
                                            C.POINTER(C.c_double), C.POINTER(C.c_int32)]
@@ -432,6 +437,45 @@ def gnn_reduce_bwd(plan: Plan, indptr, indices, dOut, arg, msg: str = "src", dX=
                                 _ptr(arg), _ptr(dX), REDUCE_MSGS[msg], _dtype_code(dOut), _stream(stream)),
            "gnn_reduce_bwd")
     return dX
+
+
+def gnn_reorder(indptr, indices, method: str = "rcm", stream=None):
+    """Node order for relabelling (perm[new] = old, int32 device tensor)."""
+    torch = _torch()
+    n, e = _graph(indptr, indices)
+    perm = torch.empty(max(n, 0), dtype=torch.int32, device=indptr.device)
+    _check(lib().gnn_reorder(_ptr(indptr), _ptr(indices) if e else None, n, e, ORDERS[method], _ptr(perm),
+                             _stream(stream)), "gnn_reorder")
+    return perm
+
+
+def gnn_permute_graph(indptr, indices, perm, stream=None):
+    """CSR of the graph relabelled by perm (new row r = old row perm[r], rows sorted)."""
+    torch = _torch()
+    n, e = _graph(indptr, indices)
+    if perm.dtype != torch.int32 or not perm.is_cuda or perm.numel() != n or not perm.is_contiguous():
+        raise TypeError("perm must be a contiguous int32 device tensor of N entries")
+    nip = torch.empty_like(indptr)
+    nix = torch.empty_like(indices)
+    _check(lib().gnn_permute_graph(_ptr(indptr), _ptr(indices) if e else None, n, e, _ptr(perm), _ptr(nip),
+                                   _ptr(nix) if e else None, _stream(stream)), "gnn_permute_graph")
+    return nip, nix
+
+
+def gnn_permute_rows(src, perm, back: bool = False, dst=None, stream=None):
+    """Rows of src (first dimension = nodes) in the new order (dst[r] = src[perm[r]]),
+    or back to the old order (dst[perm[r]] = src[r])."""
+    torch = _torch()
+    if not src.is_cuda or not src.is_contiguous():
+        raise TypeError("src must be a contiguous device tensor")
+    n = src.shape[0]
+    if perm.dtype != torch.int32 or perm.numel() != n or not perm.is_contiguous():
+        raise TypeError("perm must be a contiguous int32 tensor of src.shape[0] entries")
+    dst = torch.empty_like(src) if dst is None else dst
+    row_bytes = src[0].numel() * src.element_size() if n else 0
+    _check(lib().gnn_permute_rows(_ptr(src), _ptr(dst), n, row_bytes, _ptr(perm), int(bool(back)), _stream(stream)),
+           "gnn_permute_rows")
+    return dst
 
 
 def gnn_plan_timing_read(plan: Plan) -> dict:

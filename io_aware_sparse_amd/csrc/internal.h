@@ -142,6 +142,10 @@ int radix_sort(uint64_t *keys, uint64_t *tmp, int64_t n, int bits, int32_t *scra
 // sorted (row << nb | col) keys -> rowptr [n_rows+1] / col [<= cap]; dedupe drops repeated keys
 int emit_structure(uint64_t *keys, int64_t n, int nb, int dedupe, int32_t n_rows, int32_t *rowptr, int32_t *col,
                    int64_t cap, int32_t *flags, int32_t *pos, int32_t *total_dev, int32_t *scratch, hipStream_t s);
+// indptr monotone from 0 to e, every index in [0, n): GNN_OK, else GNN_ERR_BAD_GRAPH (synchronises s)
+int validate_csr(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, hipStream_t s);
+__global__ void k_set_i32(int32_t *p, int32_t v);
+__global__ void k_fill_i32(int32_t *p, int64_t n, int32_t v);   // p[0..n) = v
 // transpose a CSR (indptr/indices over n rows) into cindptr/cindices
 int build_transpose(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, DevBuf &cindptr,
                     DevBuf &cindices, hipStream_t s);

@@ -587,6 +587,24 @@ static int check_rows_sorted(const int32_t *indptr, const int32_t *indices, int3
     return rc;
 }
 
+int validate_csr(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, hipStream_t s) {
+    DevBuf tmp;
+    GNN_TRY(dev_alloc(tmp, 64));
+    int32_t *err = as<int32_t>(tmp);
+    int32_t herr = 0;
+    int rc = GNN_OK;
+    hipLaunchKernelGGL(k_set_i32, dim3(1), dim3(1), 0, s, err, 0);
+    hipLaunchKernelGGL(k_validate, grid1d(std::max<int64_t>(n, e) + 1), dim3(256), 0, s, indptr, indices, n, e, err);
+    if (hipMemcpyAsync(&herr, err, 4, hipMemcpyDeviceToHost, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+        set_hip_error(hipGetLastError(), "graph validation");
+        rc = GNN_ERR_HIP;
+    } else if (herr) {
+        rc = GNN_ERR_BAD_GRAPH;
+    }
+    dev_free(tmp);
+    return rc;
+}
+
 int build_transpose(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t m, DevBuf &cindptr,
                     DevBuf &cindices, hipStream_t s) {
     const int nb = bits_for(std::max<int64_t>(2, n));
@@ -738,28 +756,7 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
     p->indptr = indptr;
     p->indices = indices;
     p->opts = o;
-    int rc = GNN_OK;
-    DevBuf tmp;
-    if (dev_alloc(tmp, 64) != GNN_OK) {
-        delete p;
-        return GNN_ERR_OOM;
-    }
-    {
-        // validate structure
-        int32_t *err = as<int32_t>(tmp);
-        int32_t herr = 0;
-        hipLaunchKernelGGL(k_set_i32, dim3(1), dim3(1), 0, stream, err, 0);
-        hipLaunchKernelGGL(k_validate, grid1d(std::max<int64_t>(n_nodes, n_edges) + 1), dim3(256), 0, stream,
-                           indptr, indices, n_nodes, n_edges, err);
-        if (hipMemcpyAsync(&herr, err, 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            hipStreamSynchronize(stream) != hipSuccess) {
-            set_hip_error(hipGetLastError(), "gnn_plan_create validate");
-            rc = GNN_ERR_HIP;
-        } else if (herr) {
-            rc = GNN_ERR_BAD_GRAPH;
-        }
-        dev_free(tmp);
-    }
+    int rc = validate_csr(indptr, indices, n_nodes, n_edges, stream);
     if (rc == GNN_OK) rc = check_rows_sorted(indptr, indices, n_nodes, n_edges, stream, &p->rows_sorted);
     if (rc == GNN_OK)
         rc = build_buckets(indptr, n_nodes, o.light_threshold, o.chunk, o.waves_per_group, o.sched_order, p->fwd,

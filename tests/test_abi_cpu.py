@@ -8,7 +8,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("gnn_attn.h", "gnn_reduce.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gnn_attn.h", "gnn_reduce.h", "gnn_reorder.h")]
 
 
 @pytest.fixture(scope="module")
@@ -74,6 +74,15 @@ def test_host_validation(g):
     assert red(N=0, E=0) == 0                                                             # empty graph: no-op
     assert L.gnn_reduce_fwd(None, A, A, 10, 20, 8, None, A, None, 0, 0, 0, None) == -1
     assert L.gnn_reduce_bwd(None, A, A, 10, 20, 8, A, A, A, 0, 0, None) == -1             # needs a plan
+    # reordering: sizes and method checked before the graph is touched
+    assert L.gnn_reorder(A, A, 10, 20, 2, A, None) == -1 and L.gnn_reorder(A, A, -1, 0, 0, A, None) == -1
+    assert L.gnn_reorder(A, A, 10, 20, 0, None, None) == -1
+    assert L.gnn_reorder(A, None, 0, 0, 1, None, None) == 0                               # empty graph
+    assert L.gnn_permute_graph(A, A, 10, 20, None, A, A, None) == -1
+    assert L.gnn_permute_rows(A, A + 16, 10, 24, A, 0, None) == -2                        # rows of 16n bytes
+    assert L.gnn_permute_rows(A, A + 8, 10, 32, A, 0, None) == -3
+    assert L.gnn_permute_rows(A, A, 10, 32, A, 0, None) == -1                             # src == dst
+    assert L.gnn_permute_rows(A, A + 16, 0, 32, A, 0, None) == 0
     assert L.gatv2_attn_bwd(None, A, A, 10, 20, 2, 32, A, A, A, A, 0.2, A, A, A, A, None, A, 0, None) == -1
     # CSR build
     e = C.c_int64()
