@@ -432,6 +432,46 @@ def gatv2_bwd(indptr, indices, XD, XS, att, dO, V=None, slope: float = 0.2, rows
 
 
 # ---------------------------------------------------------------------------
+# cached SpMM aggregation (GCN / GraphConv)
+# ---------------------------------------------------------------------------
+SPMM_NORMS = {"sum": 0, "mean": 1, "gcn": 2}
+
+
+def spmm_weights(indptr, indices, norm: str = "gcn") -> np.ndarray:
+    """Per-entry weights w_e of entry e = (row i, source j), CSR order, fp64:
+    "sum" 1; "mean" 1 / indeg(i); "gcn" 1 / sqrt(indeg(i) * indeg(j)), with
+    indeg the number of row entries (self-loops included when the CSR holds
+    them, i.e. the degrees of A + I)."""
+    ip = np.asarray(indptr, np.int64)
+    ix = np.asarray(indices, np.int64)
+    deg = np.diff(ip).astype(np.float64)
+    rows = np.repeat(np.arange(ip.size - 1), np.diff(ip))
+    if norm == "sum":
+        return np.ones(ix.size)
+    if norm == "mean":
+        return 1.0 / deg[rows]
+    if norm == "gcn":
+        return 1.0 / np.sqrt(deg[rows] * deg[ix])
+    raise ValueError(norm)
+
+
+def spmm(indptr, indices, X, norm: str = "gcn", transpose: bool = False):
+    """Y = A_w X (or A_w^T X) in fp64 with the weights of spmm_weights, A_w
+    the N x N sparse matrix with entry (i, j) += w_e per CSR entry (repeats
+    add up). scipy's sparse product is the reduction. Returns dict Y [N, F]
+    and the summation scale S = |A_w| |X|."""
+    import scipy.sparse as sp
+    ip = np.asarray(indptr, np.int64)
+    ix = np.asarray(indices, np.int64)
+    n = ip.size - 1
+    X = np.asarray(X, np.float64).reshape(n, -1)
+    A = sp.csr_matrix((spmm_weights(ip, ix, norm), ix, ip), shape=(n, n))
+    if transpose:
+        A = A.T.tocsr()
+    return dict(Y=A @ X, S=abs(A) @ np.abs(X))
+
+
+# ---------------------------------------------------------------------------
 # graph reordering
 # ---------------------------------------------------------------------------
 ORDERS = {"degree": 0, "rcm": 1}
