@@ -439,9 +439,10 @@ SPMM_NORMS = {"sum": 0, "mean": 1, "gcn": 2}
 
 def spmm_weights(indptr, indices, norm: str = "gcn") -> np.ndarray:
     """Per-entry weights w_e of entry e = (row i, source j), CSR order, fp64:
-    "sum" 1; "mean" 1 / indeg(i); "gcn" 1 / sqrt(indeg(i) * indeg(j)), with
-    indeg the number of row entries (self-loops included when the CSR holds
-    them, i.e. the degrees of A + I)."""
+    "sum" 1; "mean" 1 / indeg(i); "gcn" d(i) d(j) with d(v) = indeg(v)^-1/2,
+    taken as 0 for a node without entries (a source whose own row is empty
+    contributes nothing), indeg the number of row entries (self-loops
+    included when the CSR holds them, i.e. the degrees of A + I)."""
     ip = np.asarray(indptr, np.int64)
     ix = np.asarray(indices, np.int64)
     deg = np.diff(ip).astype(np.float64)
@@ -451,7 +452,9 @@ def spmm_weights(indptr, indices, norm: str = "gcn") -> np.ndarray:
     if norm == "mean":
         return 1.0 / deg[rows]
     if norm == "gcn":
-        return 1.0 / np.sqrt(deg[rows] * deg[ix])
+        dinv = np.zeros_like(deg)
+        dinv[deg > 0] = 1.0 / np.sqrt(deg[deg > 0])
+        return dinv[rows] * dinv[ix]
     raise ValueError(norm)
 
 

@@ -71,6 +71,15 @@ def test_torch_sparse_and_repeats():
     assert np.allclose(oracle.spmm(ip, ix, X, "gcn")["Y"], ref, rtol=0, atol=1e-12)
 
 
+def test_gcn_source_without_entries():
+    # row 0 = {1}, row 1 empty: source 1 has no entries of its own, so its factor is 0 (no 1/sqrt(0))
+    ip = np.array([0, 1, 1], np.int64)
+    ix = np.array([1], np.int64)
+    assert oracle.spmm_weights(ip, ix, "gcn").tolist() == [0.0]
+    assert np.all(oracle.spmm(ip, ix, np.ones((2, 3)), "gcn")["Y"] == 0)
+    assert oracle.spmm_weights(ip, ix, "mean").tolist() == [1.0]
+
+
 def test_closed_forms_and_adjoint():
     rng = np.random.default_rng(5)
     n, F = 200, 4
