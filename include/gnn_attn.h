@@ -169,6 +169,10 @@ typedef struct {
     int32_t rows_sorted;        /* 1: every CSR row lists its sources in non-decreasing order */
     const int32_t *light_by_degree; /* [n_light] light nodes by descending in-degree, ties by
                                        ascending id (launch order 1, whatever sched_order is) */
+    const int32_t *c_light_by_degree; /* [c_n_light] the same over out-degrees (with want_csc) */
+    int32_t spmm_norm;          /* gnn_norm_t cached by gnn_spmm_prepare, -1: none          */
+    const float *spmm_w;        /* [n_edges] cached SpMM weights in CSR order (or NULL)     */
+    const float *spmm_cw;       /* [n_edges] the same in transposed-adjacency order (or NULL) */
 } gnn_plan_info;
 
 int gnn_plan_export(gnn_plan_t plan, gnn_plan_info *info /*host*/);

@@ -31,8 +31,9 @@ STATUS = {0: "GNN_OK", -1: "GNN_ERR_INVALID_ARG", -2: "GNN_ERR_UNSUPPORTED", -3:
 EXPORTS = ["gnn_plan_opts_default", "gnn_csr_build", "gnn_plan_create", "gnn_plan_export", "gnn_plan_destroy",
            "gnn_attn_fwd", "gnn_attn_bwd", "gatv2_attn_fwd", "gatv2_attn_bwd", "gnn_plan_set_timing",
            "gnn_plan_timing_read", "gnn_status_string", "gnn_reduce_fwd", "gnn_reduce_bwd", "gnn_reorder",
-           "gnn_permute_graph", "gnn_permute_rows"]
+           "gnn_permute_graph", "gnn_permute_rows", "gnn_spmm_prepare", "gnn_spmm"]
 ORDERS = {"degree": 0, "rcm": 1}      # gnn_order_t
+NORMS = {"sum": 0, "mean": 1, "gcn": 2}   # gnn_norm_t
 REDUCE_OPS = {"max": 0, "min": 1}     # gnn_reduce_op_t
 REDUCE_MSGS = {"src": 0, "diff": 1}   # gnn_msg_t
 
@@ -70,7 +71,8 @@ class PlanInfo(C.Structure):
                 ("c_light_nt", C.c_void_p), ("light_sched", C.c_void_p), ("c_light_sched", C.c_void_p),
                 ("structure_bytes", C.c_int64), ("workspace_bytes", C.c_int64),
                 ("largest_workspace_alloc", C.c_int64), ("rows_sorted", C.c_int32),
-                ("light_by_degree", C.c_void_p)]
+                ("light_by_degree", C.c_void_p), ("c_light_by_degree", C.c_void_p), ("spmm_norm", C.c_int32),
+                ("spmm_w", C.c_void_p), ("spmm_cw", C.c_void_p)]
 
 
 _lib = None
@@ -102,6 +104,8 @@ def lib():
         L.gnn_reorder.argtypes = [V, V, I32, I64, C.c_int, V, V]
         L.gnn_permute_graph.argtypes = [V, V, I32, I64, V, V, V, V]
         L.gnn_permute_rows.argtypes = [V, V, I32, I64, V, I32, V]
+        L.gnn_spmm_prepare.argtypes = [V, C.c_int, V]
+        L.gnn_spmm.argtypes = [V, V, V, I32, I64, I32, V, V, I32, C.c_int, V]
         L.gnn_plan_set_timing.argtypes = [V, I32]
         L.gnn_plan_timing_read.argtypes = [V, I32, C.POINTER(C.c_char_p), C.POINTER(C.c_int32),
                                            C.POINTER(C.c_double), C.POINTER(C.c_int32)]
@@ -266,6 +270,11 @@ def gnn_plan_export(plan: Plan, arrays: bool = False) -> dict:
             d["c_groups"] = _copy_dev(info.c_groups, 3 * info.c_n_groups, np.int32).reshape(-1, 3)
             d["c_partial_ofs"] = _copy_dev(info.c_partial_ofs, info.c_n_heavy + 1, np.int32)
             d["c_light_sched"] = _copy_dev(info.c_light_sched, info.c_n_light, np.int32)
+            d["c_light_by_degree"] = _copy_dev(info.c_light_by_degree, info.c_n_light, np.int32)
+        if info.spmm_w:
+            d["spmm_w"] = _copy_dev(info.spmm_w, info.n_edges, np.float32)
+        if info.spmm_cw:
+            d["spmm_cw"] = _copy_dev(info.spmm_cw, info.n_edges, np.float32)
         if info.has_tiles:
             d["tile_rc"] = _copy_dev(info.tile_rc, 2 * info.n_tiles, np.int32).reshape(-1, 2)
             d["tile_mask"] = _copy_dev(info.tile_mask, 4 * info.n_tiles, np.uint64).reshape(-1, 4)
@@ -437,6 +446,26 @@ def gnn_reduce_bwd(plan: Plan, indptr, indices, dOut, arg, msg: str = "src", dX=
                                 _ptr(arg), _ptr(dX), REDUCE_MSGS[msg], _dtype_code(dOut), _stream(stream)),
            "gnn_reduce_bwd")
     return dX
+
+
+def gnn_spmm_prepare(plan: Plan, norm: str = "gcn", stream=None) -> None:
+    """Cache the SpMM weights of `norm` ("sum", "mean", "gcn") in the plan."""
+    _check(lib().gnn_spmm_prepare(C.c_void_p(plan.handle), NORMS[norm], _stream(stream)), "gnn_spmm_prepare")
+
+
+def gnn_spmm(plan: Plan, indptr, indices, X, transpose: bool = False, Y=None, stream=None):
+    """Y = A_w X (or A_w^T X) with the plan's cached weights; X [N, F]."""
+    torch = _torch()
+    n, e = _graph(indptr, indices)
+    _rows2d(X, "X")
+    _dtype_code(X)
+    N, F = X.shape
+    if N != n:
+        raise ValueError("X rows differ from the graph's node count")
+    Y = torch.empty_like(X) if Y is None else _rows2d(Y, "Y", X.shape, X.dtype)
+    _check(lib().gnn_spmm(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, F, _ptr(X), _ptr(Y),
+                          int(bool(transpose)), _dtype_code(X), _stream(stream)), "gnn_spmm")
+    return Y
 
 
 def gnn_reorder(indptr, indices, method: str = "rcm", stream=None):

@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgnn_attn.so")
-SOURCES = ["prep.hip", "tiles.hip", "attn.hip", "attn_tile.hip", "attn_gat.hip", "reduce.hip", "reorder.hip"]
+SOURCES = ["prep.hip", "tiles.hip", "attn.hip", "attn_tile.hip", "attn_gat.hip", "reduce.hip", "reorder.hip",
+           "spmm.hip"]
 HEADERS = ["device.h", "internal.h", "attn_core.h"]
 
 HIPCC_FLAGS = [

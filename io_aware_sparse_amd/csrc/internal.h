@@ -48,8 +48,8 @@ struct Buckets {
     // launch order of the light list, as gnn_plan_opts::sched_order asks (order
     // 0 is a copy of the light list); kernel results do not depend on it
     DevBuf sched;
-    // in-degree buckets only: the light list by descending degree, ties by
-    // ascending id (launch order 1), for kernels that pack several rows per wave
+    // the light list by descending degree, ties by ascending id (launch
+    // order 1), for kernels that pack several rows per wave
     DevBuf by_degree;
 };
 
@@ -81,6 +81,10 @@ enum KernelKind {
     K_RED_FINAL,
     K_RED_BWD_MAIN,
     K_RED_BWD_MERGE,
+    K_SPMM_MAIN,
+    K_SPMM_MERGE,
+    K_SPMM_T_MAIN,
+    K_SPMM_T_MERGE,
     K_NUM_KINDS
 };
 extern const char *kKernelNames[K_NUM_KINDS];
@@ -116,11 +120,16 @@ struct gnn_plan_s {
     int64_t n_residual = 0;
     gnn::DevBuf tile_rc, tile_mask, tile_ptr, trb, rindptr, rindices, light_nt;
     gnn::DevBuf ctile, ctile_ptr, tcb, rcindptr, rcindices, c_light_nt;
+    // cached SpMM weights (CSR order; transposed-adjacency order with the transpose), -1: none
+    int32_t spmm_norm = -1;
+    gnn::DevBuf spmm_w, spmm_cw;
     // workspace (heavy partials, backward statistics), grows on demand
     gnn::DevBuf ws;
     int64_t largest_ws = 0;
     gnn::Timer timer;
-    int64_t structure_bytes() const;
+    // every structure array the plan owns (the workspace excluded)
+    std::vector<gnn::DevBuf *> structures();
+    int64_t structure_bytes();
 };
 
 namespace gnn {

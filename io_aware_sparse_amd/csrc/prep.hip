@@ -57,7 +57,8 @@ const char *kKernelNames[K_NUM_KINDS] = {
     "gt_fwd_main", "gt_fwd_merge", "gatv2_fwd_main", "gatv2_fwd_merge", "gt_bwd_dst_main",
     "gt_bwd_dst_merge", "gt_bwd_src_main", "gt_bwd_src_merge", "gt_tile_fwd", "gt_tile_bwd_dst", "gt_tile_bwd_src",
     "gatv2_bwd_dst_main", "gatv2_bwd_dst_merge", "gatv2_bwd_src_main", "gatv2_bwd_src_merge", "gatv2_bwd_datt",
-    "reduce_fwd_init", "reduce_fwd_main", "reduce_fwd_final", "reduce_bwd_main", "reduce_bwd_merge"};
+    "reduce_fwd_init", "reduce_fwd_main", "reduce_fwd_final", "reduce_bwd_main", "reduce_bwd_merge",
+    "spmm_main", "spmm_merge", "spmm_t_main", "spmm_t_merge"};
 
 hipEvent_t Timer::get() {
     if (!pool.empty()) {
@@ -637,14 +638,16 @@ int build_transpose(const int32_t *indptr, const int32_t *indices, int32_t n, in
 
 using namespace gnn;
 
-int64_t gnn_plan_s::structure_bytes() const {
+std::vector<DevBuf *> gnn_plan_s::structures() {
+    return {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &fwd.sched, &fwd.by_degree, &cindptr, &cindices,
+            &bwd.light, &bwd.heavy, &bwd.groups, &bwd.partial_ofs, &bwd.sched, &bwd.by_degree, &tile_rc, &tile_mask,
+            &tile_ptr, &trb, &rindptr, &rindices, &light_nt, &ctile, &ctile_ptr, &tcb, &rcindptr, &rcindices,
+            &c_light_nt, &spmm_w, &spmm_cw};
+}
+
+int64_t gnn_plan_s::structure_bytes() {
     int64_t t = 0;
-    for (const DevBuf *b : {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &fwd.sched, &fwd.by_degree,
-                            &cindptr, &cindices,
-                            &bwd.light, &bwd.heavy, &bwd.groups, &bwd.partial_ofs, &bwd.sched, &tile_rc, &tile_mask,
-                            &tile_ptr, &trb, &rindptr, &rindices, &light_nt, &ctile, &ctile_ptr, &tcb,
-                            &rcindptr, &rcindices, &c_light_nt})
-        t += (int64_t)b->bytes;
+    for (const DevBuf *b : structures()) t += (int64_t)b->bytes;
     return t;
 }
 
@@ -766,7 +769,7 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
         if (rc == GNN_OK) {
             p->has_csc = true;
             rc = build_buckets(as<int32_t>(p->cindptr), n_nodes, o.light_threshold, o.chunk, o.waves_per_group,
-                               o.sched_order, p->bwd, stream);
+                               o.sched_order, p->bwd, stream, true);
         }
     }
     if (rc == GNN_OK && o.tile_density > 0.0f) {
@@ -834,16 +837,17 @@ int gnn_plan_export(gnn_plan_t p, gnn_plan_info *info) {
     info->largest_workspace_alloc = p->largest_ws;
     info->rows_sorted = p->rows_sorted ? 1 : 0;
     info->light_by_degree = as<int32_t>(p->fwd.by_degree);
+    info->c_light_by_degree = as<int32_t>(p->bwd.by_degree);
+    info->spmm_norm = p->spmm_norm;
+    info->spmm_w = as<float>(p->spmm_w);
+    info->spmm_cw = as<float>(p->spmm_cw);
     return GNN_OK;
 }
 
 int gnn_plan_destroy(gnn_plan_t p) {
     if (!p) return GNN_ERR_INVALID_ARG;
-    for (DevBuf *b : {&p->fwd.light, &p->fwd.heavy, &p->fwd.groups, &p->fwd.partial_ofs, &p->fwd.sched, &p->cindptr,
-                      &p->cindices, &p->bwd.light, &p->bwd.heavy, &p->bwd.groups, &p->bwd.partial_ofs, &p->bwd.sched, &p->tile_rc, &p->tile_mask,
-                      &p->tile_ptr, &p->trb, &p->rindptr, &p->rindices, &p->light_nt, &p->ctile, &p->ctile_ptr,
-                      &p->tcb, &p->rcindptr, &p->rcindices, &p->c_light_nt, &p->ws})
-        dev_free(*b);
+    for (DevBuf *b : p->structures()) dev_free(*b);
+    dev_free(p->ws);
     delete p;
     return GNN_OK;
 }

@@ -8,7 +8,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("gnn_attn.h", "gnn_reduce.h", "gnn_reorder.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gnn_attn.h", "gnn_reduce.h", "gnn_reorder.h", "gnn_spmm.h")]
 
 
 @pytest.fixture(scope="module")
@@ -83,6 +83,9 @@ def test_host_validation(g):
     assert L.gnn_permute_rows(A, A + 8, 10, 32, A, 0, None) == -3
     assert L.gnn_permute_rows(A, A, 10, 32, A, 0, None) == -1                             # src == dst
     assert L.gnn_permute_rows(A, A + 16, 0, 32, A, 0, None) == 0
+    # SpMM needs a plan, prepared
+    assert L.gnn_spmm_prepare(None, 2, None) == -1
+    assert L.gnn_spmm(None, A, A, 10, 20, 8, A, A, 0, 0, None) == -1
     assert L.gatv2_attn_bwd(None, A, A, 10, 20, 2, 32, A, A, A, A, 0.2, A, A, A, A, None, A, 0, None) == -1
     # CSR build
     e = C.c_int64()

@@ -1,0 +1,106 @@
+"""GPU parity of the cached SpMM aggregation (gnn_spmm_prepare / gnn_spmm)
+against the oracle: cached weights, Y = A_w X and A_w^T X for sum, mean and
+GCN weights, fp32 and bf16, rows from one 16-byte slice to several waves,
+plans whose tiny threshold sends most rows through the chunked heavy path,
+repeated entries and empty rows; reproducibility and the error paths."""
+import numpy as np
+import pytest
+
+import oracle
+from _gpu import TOL, dev_feat, dev_i32, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import io_aware_sparse_amd as g
+    g.lib()
+    return g
+
+
+def _graph(rng, n, mean_deg, hub_deg=0, empty=0.03):
+    deg = rng.poisson(mean_deg, n)
+    if hub_deg:
+        deg[rng.choice(n, 3, replace=False)] = hub_deg
+    deg[rng.random(n) < empty] = 0
+    rows = [np.sort(np.concatenate([rng.integers(0, n, d), rng.integers(0, n, int(d > 4))])) for d in deg]
+    ip = np.concatenate([[0], np.cumsum([r.size for r in rows])]).astype(np.int32)
+    ix = np.concatenate(rows).astype(np.int32)
+    return ip, ix
+
+
+def _feats(rng, n, F, dtype):
+    x = rng.standard_normal((n, F)).astype(np.float32)
+    return oracle.round_bf16(x) if dtype == "bf16" else x
+
+
+def _plan(g, ip_d, ix_d, kind):
+    if kind == "tiny":
+        return g.gnn_plan_create(ip_d, ix_d, light_threshold=3, chunk=2, waves_per_group=2, want_csc=True)
+    return g.gnn_plan_create(ip_d, ix_d, want_csc=True)
+
+
+@pytest.mark.parametrize("norm", ["sum", "mean", "gcn"])
+def test_cached_weights(g, norm):
+    rng = np.random.default_rng(1)
+    n = 400
+    ip, ix = _graph(rng, n, 6, hub_deg=700)
+    plan = g.gnn_plan_create(dev_i32(ip), dev_i32(ix), want_csc=True)
+    g.gnn_spmm_prepare(plan, norm)
+    d = g.gnn_plan_export(plan, arrays=True)
+    assert d["spmm_norm"] == g.NORMS[norm]
+    w = oracle.spmm_weights(ip, ix, norm)
+    assert np.all((d["spmm_w"] == 0) == (w == 0))
+    nz = w > 0
+    assert np.max(np.abs(d["spmm_w"][nz] - w[nz]) / w[nz]) < 1e-6
+    rows = np.repeat(np.arange(n), np.diff(ip))
+    o = np.lexsort((rows, ix))                       # CSR entries in transposed order (source, then row)
+    wo = w[o]
+    assert np.all((d["spmm_cw"] == 0) == (wo == 0))
+    assert np.max(np.abs(d["spmm_cw"][wo > 0] - wo[wo > 0]) / wo[wo > 0]) < 1e-6
+    if norm == "gcn":
+        assert (w == 0).any()                        # the graph has sources without entries
+
+
+CASES = [("f32", 4), ("f32", 128), ("f32", 320), ("bf16", 8), ("bf16", 128), ("bf16", 1032)]
+
+
+@pytest.mark.parametrize("dtype,F", CASES)
+@pytest.mark.parametrize("plan_kind", ["tiny", "default"])
+def test_spmm_parity(g, dtype, F, plan_kind):
+    rng = np.random.default_rng(F + len(plan_kind))
+    n = 600
+    ip, ix = _graph(rng, n, 9, hub_deg=1500)
+    X = _feats(rng, n, F, dtype)
+    ip_d, ix_d = dev_i32(ip), dev_i32(ix)
+    plan = _plan(g, ip_d, ix_d, plan_kind)
+    Xd = dev_feat(X, dtype)
+    for norm in ("sum", "mean", "gcn"):
+        g.gnn_spmm_prepare(plan, norm)
+        for tr in (False, True):
+            Y = g.gnn_spmm(plan, ip_d, ix_d, Xd, transpose=tr)
+            ref = oracle.spmm(ip, ix, X, norm, transpose=tr)
+            err = oracle.scaled_error(host(Y), ref["Y"], ref["S"])
+            say(f"spmm {dtype} F={F} {plan_kind} {norm} transpose={tr}: scaled err {err:.2e}")
+            assert err <= TOL[dtype], (norm, tr, err)
+            Y2 = g.gnn_spmm(plan, ip_d, ix_d, Xd, transpose=tr)
+            assert np.array_equal(host(Y2), host(Y)), "not reproducible"
+
+
+def test_spmm_errors_and_empty(g):
+    import torch
+    rng = np.random.default_rng(3)
+    n = 50
+    ip, ix = _graph(rng, n, 3)
+    ip_d, ix_d = dev_i32(ip), dev_i32(ix)
+    X = dev_feat(_feats(rng, n, 4, "f32"), "f32")
+    plan = g.gnn_plan_create(ip_d, ix_d)
+    with pytest.raises(g.GnnError):                  # not prepared
+        g.gnn_spmm(plan, ip_d, ix_d, X)
+    g.gnn_spmm_prepare(plan, "gcn")
+    with pytest.raises(g.GnnError):                  # no transposed adjacency in this plan
+        g.gnn_spmm(plan, ip_d, ix_d, X, transpose=True)
+    Y = g.gnn_spmm(plan, ip_d, ix_d, X)
+    empty = np.diff(ip) == 0
+    assert empty.any() and torch.all(Y[torch.from_numpy(empty).cuda()] == 0).item()
