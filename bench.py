@@ -43,6 +43,7 @@ _CSRC = os.path.join(ROOT, "io_aware_sparse_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("attn.hip", "attn_core.h", "attn_tile.hip", "attn_gat.hip",
                                                    "device.h")]
 REDUCE_SOURCES = [os.path.join(_CSRC, f) for f in ("reduce.hip", "attn_core.h", "device.h")]
+SPMM_SOURCES = [os.path.join(_CSRC, f) for f in ("spmm.hip", "attn_core.h", "device.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -51,9 +52,10 @@ def log(*a):
 
 
 def kernel_source_hash(kernel: str = "") -> str:
-    """Hash of the sources of `kernel`'s family (reduction kernels: reduce_*)."""
+    """Hash of the sources of `kernel`'s family (reduce_*, spmm_*, else attention)."""
     h = hashlib.sha256()
-    for f in (REDUCE_SOURCES if kernel.startswith("reduce_") else KERNEL_SOURCES):
+    for f in (REDUCE_SOURCES if kernel.startswith("reduce_") else SPMM_SOURCES if kernel.startswith("spmm_")
+              else KERNEL_SOURCES):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -139,6 +141,14 @@ def kernel_bytes(kind, c, H, D, s, v_alias=True):
     t, tr, te = c.get("tiles", 0), c.get("tile_rows", 0), c.get("tile_res_edges", 0)
     F, rsz = H * D, H * D * s          # reduction layer: F features, rsz bytes per row
     diff = 1 if c.get("msg") == "diff" else 0
+    if kind == "spmm_main":             # index + weight per entry, one gathered row; light rows written
+        return 4 * (rows + 1) + 8 * E + rsz * E + rsz * nl
+    if kind == "spmm_merge":
+        return rsz * nh
+    if kind == "spmm_t_main":           # the same over the transposed adjacency
+        return 4 * (sr + 1) + 8 * se + rsz * se + rsz * sl
+    if kind == "spmm_t_merge":
+        return rsz * sh
     if kind == "reduce_fwd_init":       # identity keys of the heavy rows
         return 8 * F * nh
     if kind == "reduce_fwd_main":       # gathers a row per edge; light rows write out and arg
@@ -357,7 +367,7 @@ def summarize(args) -> int:
 
 # ----------------------------------------------------------------- workload
 
-def setup(name, plan_opts, backward=None, reorder="none"):
+def setup(name, plan_opts, backward=None, reorder="none", spmm_norm="gcn"):
     import numpy as np
     import torch
 
@@ -400,6 +410,19 @@ def setup(name, plan_opts, backward=None, reorder="none"):
     torch.cuda.synchronize()
     t_plan = time.time() - t0
     tensors = {}
+    if wl.kind == "spmm":
+        g.gnn_spmm_prepare(plan, spmm_norm)           # cached per graph: outside the timed steps
+        F = H * D
+        tensors["X"] = feat("X").reshape(n, F)
+        tensors["Y"] = torch.empty_like(tensors["X"])
+        if wl.backward:
+            tensors["dO"] = feat("dO").reshape(n, F)
+            tensors["dX"] = torch.empty_like(tensors["X"])
+        torch.cuda.synchronize()
+        prep = dict(generate_s=round(t_gen, 3), csr_build_ms=round(1e3 * t_csr, 3),
+                    plan_create_ms=round(1e3 * t_plan, 3), reorder=reorder, reorder_ms=round(1e3 * t_reorder, 3),
+                    relabel_ms=round(1e3 * t_relabel, 3), norm=spmm_norm)
+        return wl, indptr, indices, plan, tensors, int(indices.numel()), prep
     if wl.kind == "reduce":
         F = H * D
         tensors["X"] = feat("X").reshape(n, F)
@@ -438,6 +461,12 @@ def setup(name, plan_opts, backward=None, reorder="none"):
 
 
 def make_step(g, wl, indptr, indices, plan, T, op="max", msg="src"):
+    if wl.kind == "spmm":
+        def step():
+            g.gnn_spmm(plan, indptr, indices, T["X"], Y=T["Y"])
+            if wl.backward:
+                g.gnn_spmm(plan, indptr, indices, T["dO"], transpose=True, Y=T["dX"])
+        return step
     if wl.kind == "reduce":
         def step():
             g.gnn_reduce_fwd(plan, indptr, indices, T["X"], op, msg, out=T["out"], arg=T["arg"])
@@ -465,7 +494,7 @@ def make_step(g, wl, indptr, indices, plan, T, op="max", msg="src"):
     return step
 
 
-def cpu_baseline(wl, rp, rx, target_s, threads=None, op="max", msg="src"):
+def cpu_baseline(wl, rp, rx, target_s, threads=None, op="max", msg="src", norm="gcn"):
     """fp64 oracle on a seeded sample of destination rows (and the same nodes
     as sources for the gradient), sized to about target_s seconds."""
     import numpy as np
@@ -476,12 +505,12 @@ def cpu_baseline(wl, rp, rx, target_s, threads=None, op="max", msg="src"):
     if threads:
         oracle.set_threads(threads)
     try:
-        return _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg)
+        return _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg, norm)
     finally:
         oracle.set_threads(all_threads)
 
 
-def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg):
+def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg, norm):
     import numpy as np
 
     n = wl.n_nodes
@@ -490,7 +519,7 @@ def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg):
     order = rng.permutation(n)
     csum = np.cumsum(deg[order])
 
-    if wl.kind == "reduce":
+    if wl.kind in ("reduce", "spmm"):
         X = wl.feats["X"].reshape(n, -1)
         dO = wl.feats["dO"].reshape(n, -1) if wl.backward else None
     elif wl.kind == "gt":
@@ -505,7 +534,11 @@ def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg):
         k = int(np.searchsorted(csum, edges)) + 1
         rows = np.sort(order[:min(k, n)])
         t0 = time.perf_counter()
-        if wl.kind == "reduce":
+        if wl.kind == "spmm":
+            oracle.spmm(rp, rx, X, norm, rows=rows)
+            if wl.backward:
+                oracle.spmm(rp, rx, dO, norm, transpose=True, rows=rows)
+        elif wl.kind == "reduce":
             arg = oracle.segment_reduce(rp, rx, X, op, msg, rows=rows)["arg"]
             if wl.backward:
                 oracle.segment_reduce_bwd(rp, rx, dO[rows], arg, msg, n_nodes=n, rows=rows)
@@ -531,7 +564,8 @@ def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg):
         tt += t2
         reps += 1
     t = tt / reps
-    return dict(value=round(e / t / 1e9, 6), unit="GEdges/s", cores=oracle.num_threads(), kind="oracle",
+    cores = 1 if wl.kind == "spmm" else oracle.num_threads()      # scipy's sparse product runs on one thread
+    return dict(value=round(e / t / 1e9, 6), unit="GEdges/s", cores=cores, kind="oracle",
                 sample=f"{r} destination rows drawn uniformly (seed 12345) covering {e} of {int(csum[-1])} edges"
                        + (" (forward + backward, the same nodes as sources)" if wl.backward else " (forward)")
                        + f", {t:.2f} s per pass, mean of {reps}")
@@ -552,7 +586,8 @@ def bench(args) -> int:
     opts = dict(light_threshold=args.light_threshold, chunk=args.chunk, waves_per_group=args.waves,
                 tile_density=args.tile_density, sched_order=args.sched_order)
     log(f"[bench] workload {args.workload}: generating and building the graph")
-    wl, indptr, indices, plan, T, E, prep = setup(args.workload, opts, True if args.backward else None, args.reorder)
+    wl, indptr, indices, plan, T, E, prep = setup(args.workload, opts, True if args.backward else None, args.reorder,
+                                                  args.norm)
     info = g.gnn_plan_export(plan)
     N, H, D = wl.n_nodes, wl.heads, wl.dim
     s = 4 if wl.dtype == "f32" else 2
@@ -629,7 +664,9 @@ def bench(args) -> int:
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "pass": (f"neighbourhood {args.reduce_op} of {args.msg} messages with winners"
+            "pass": (f"SpMM aggregation Y = A_w X, {args.norm} weights"
+                     + (" + transposed product (gradient)" if wl.backward else "")) if wl.kind == "spmm" else
+                    (f"neighbourhood {args.reduce_op} of {args.msg} messages with winners"
                      + (" + gradient" if wl.backward else "")) if wl.kind == "reduce" else
                     ("GATv2" if wl.kind == "gatv2" else "GT") + (" forward + LSE-recompute backward"
                                                                  if wl.backward else " forward"),
@@ -666,8 +703,9 @@ def bench(args) -> int:
         rp = indptr.cpu().numpy()
         rx = indices.cpu().numpy()
         log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
-        rec["cpu_baseline"] = cpu_baseline(wl, rp, rx, args.cpu_seconds, op=args.reduce_op, msg=args.msg)
-        if E <= 10_000_000:
+        rec["cpu_baseline"] = cpu_baseline(wl, rp, rx, args.cpu_seconds, op=args.reduce_op, msg=args.msg,
+                                           norm=args.norm)
+        if E <= 10_000_000 and wl.kind != "spmm":
             rec["cpu_baseline_1core"] = cpu_baseline(wl, rp, rx, args.cpu_seconds / 2, threads=1,
                                                      op=args.reduce_op, msg=args.msg)
     print(json.dumps(rec), flush=True)
@@ -720,6 +758,8 @@ def main():
                     help="reduction workloads (maxpool_*): max or min")
     ap.add_argument("--msg", choices=("src", "diff"), default="src",
                     help="reduction workloads: message x_j (src) or x_j - x_i (diff)")
+    ap.add_argument("--norm", choices=("sum", "mean", "gcn"), default="gcn",
+                    help="SpMM workloads (spmm_*): cached weights")
     ap.add_argument("--reorder", choices=("none", "degree", "rcm"), default="none",
                     help="relabel the graph and its feature rows before planning (gnn_reorder)")
     ap.add_argument("--tile-density", type=float, default=0.0,

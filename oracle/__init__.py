@@ -458,11 +458,11 @@ def spmm_weights(indptr, indices, norm: str = "gcn") -> np.ndarray:
     raise ValueError(norm)
 
 
-def spmm(indptr, indices, X, norm: str = "gcn", transpose: bool = False):
+def spmm(indptr, indices, X, norm: str = "gcn", transpose: bool = False, rows=None):
     """Y = A_w X (or A_w^T X) in fp64 with the weights of spmm_weights, A_w
     the N x N sparse matrix with entry (i, j) += w_e per CSR entry (repeats
     add up). scipy's sparse product is the reduction. Returns dict Y [N, F]
-    and the summation scale S = |A_w| |X|."""
+    (or only the listed rows) and the summation scale S = |A_w| |X|."""
     import scipy.sparse as sp
     ip = np.asarray(indptr, np.int64)
     ix = np.asarray(indices, np.int64)
@@ -471,6 +471,8 @@ def spmm(indptr, indices, X, norm: str = "gcn", transpose: bool = False):
     A = sp.csr_matrix((spmm_weights(ip, ix, norm), ix, ip), shape=(n, n))
     if transpose:
         A = A.T.tocsr()
+    if rows is not None:
+        A = A[np.asarray(rows, np.int64)]
     return dict(Y=A @ X, S=abs(A) @ np.abs(X))
 
 

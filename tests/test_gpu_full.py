@@ -201,3 +201,31 @@ def test_full_size_reduce(g, name):
             say(f"  dX column sums: max |sum - expected| / sum|dOut| = {err:.2e}")
             assert err <= (1e-6 if wl.dtype == "f32" else 1e-2), err
         del out, arg, dX
+
+
+@pytest.mark.parametrize("name", ["spmm_chunglu25_n169k", "spmm_chunglu22_n2450k"])
+def test_full_size_spmm(g, name):
+    """GCN-normalised SpMM and its transpose at full size, default plan, on
+    every heavy row (source) and a seeded sample of light ones."""
+    import torch
+    say("full-size spmm", name)
+    wl = workloads.make(name, backward=True)
+    n, F = wl.n_nodes, wl.heads * wl.dim
+    ip, ix = g.gnn_csr_build(torch.from_numpy(wl.src).cuda(), torch.from_numpy(wl.dst).cuda(), n)
+    rp, rx = oracle.csr_build(wl.src, wl.dst, n)
+    assert np.array_equal(ip.cpu().numpy(), rp) and np.array_equal(ix.cpu().numpy(), rx)
+    plan = g.gnn_plan_create(ip, ix, want_csc=True)
+    g.gnn_spmm_prepare(plan, "gcn")
+    rng = np.random.default_rng(80)
+    rows = _sample(rng, n, oracle.bucketing(rp, 512, 512, 4)["heavy"], N_SAMPLE)
+    cip, _ = oracle.csc(rp, rx, n)
+    srcs = _sample(rng, n, oracle.bucketing(cip, 512, 512, 4)["heavy"], N_SAMPLE)
+    X = wl.feats["X"].reshape(n, F)
+    dO = wl.feats["dO"].reshape(n, F)
+    Y = g.gnn_spmm(plan, ip, ix, _dev(wl, "X").reshape(n, F))
+    dX = g.gnn_spmm(plan, ip, ix, _dev(wl, "dO").reshape(n, F), transpose=True)
+    torch.cuda.synchronize()
+    ref = oracle.spmm(rp, rx, X, "gcn", rows=rows)
+    _check("Y", _host(Y)[rows], ref["Y"], ref["S"], wl.dtype)
+    ref = oracle.spmm(rp, rx, dO, "gcn", transpose=True, rows=srcs)
+    _check("dX", _host(dX)[srcs], ref["Y"], ref["S"], wl.dtype)

@@ -26,6 +26,9 @@ of the case it names:
   maxpool_zipf21_n100k    the Zipf(2.1) graph with F = 128 fp32 features per
                           node, for the neighbourhood max / min reduction
   maxpool_chunglu22_n2450k  the degree-2.2 Chung-Lu graph with F = 128 bf16
+  spmm_chunglu25_n169k    the degree-2.5 Chung-Lu graph, F = 128 fp32, for
+                          the SpMM aggregation (GCN / GraphConv)
+  spmm_chunglu22_n2450k   the degree-2.2 Chung-Lu graph, F = 128 bf16
 
 Self-loops are never emitted here; the CSR builder adds exactly one per node.
 
@@ -139,7 +142,7 @@ def round_to_bf16(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 @dataclass
 class Workload:
     name: str
-    kind: str                 # "gt" (dot-product), "gatv2" or "reduce" (max / min of features X)
+    kind: str                 # "gt" (dot-product), "gatv2", "reduce" (max / min of X) or "spmm" (A_w X)
     n_nodes: int
     src: np.ndarray           # int32 [E0], edge src -> dst, no self-pairs
     dst: np.ndarray           # int32 [E0]
@@ -311,6 +314,11 @@ SPECS = {
                                  dim=128, dtype="f32", backward=False),
     "maxpool_chunglu22_n2450k": dict(seed=1004, kind="reduce", graph="gt_chunglu22_n2450k", n=2_450_000,
                                      heads=1, dim=128, dtype="bf16", backward=False),
+    # SpMM aggregation (GCN / GraphConv) on the Chung-Lu graphs
+    "spmm_chunglu25_n169k": dict(seed=1002, kind="spmm", graph="gt_chunglu25_n169k", n=169_343, heads=1,
+                                 dim=128, dtype="f32", backward=False),
+    "spmm_chunglu22_n2450k": dict(seed=1004, kind="spmm", graph="gt_chunglu22_n2450k", n=2_450_000, heads=1,
+                                  dim=128, dtype="bf16", backward=False),
 }
 
 
@@ -391,7 +399,7 @@ def add_features(wl: Workload, f_ss: Optional[np.random.SeedSequence] = None) ->
     if f_ss is None:
         f_ss = np.random.SeedSequence([wl.seed, wl.n_nodes]).spawn(2)[1]
     shape = (wl.n_nodes, wl.heads, wl.dim)
-    names = {"gt": ["Q", "K", "V"], "gatv2": ["XD", "XS"], "reduce": ["X"]}[wl.kind]
+    names = {"gt": ["Q", "K", "V"], "gatv2": ["XD", "XS"], "reduce": ["X"], "spmm": ["X"]}[wl.kind]
     kids = f_ss.spawn(len(names) + 2)
     if wl.backward:
         names.append("dO")
