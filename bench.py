@@ -604,32 +604,36 @@ def bench(args) -> int:
     torch.cuda.synchronize()
 
     def timed(flushed):
-        """Milliseconds of args.steps steps. Flushed: a 512 MiB fill before
-        every step, outside the events; warm: the steps back to back."""
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+        """(milliseconds of args.steps steps, per-step milliseconds). Flushed:
+        a 512 MiB fill before every step, outside the events; warm: the steps
+        back to back (an event between consecutive steps)."""
         if not flushed:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
             ev[0].record(stream)
-            for _ in range(args.steps):
+            for k in range(args.steps):
                 step()
-            ev[1].record(stream)
+                ev[k + 1].record(stream)
             torch.cuda.synchronize()
-            return ev[0].elapsed_time(ev[1])
+            per = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+            return ev[0].elapsed_time(ev[-1]), per
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
         for k in range(args.steps):
             flush_buf.fill_(k & 0xFF)
             ev[2 * k].record(stream)
             step()
             ev[2 * k + 1].record(stream)
         torch.cuda.synchronize()
-        return sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps))
+        per = [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]
+        return sum(per), per
 
     g.gnn_plan_timing_read(plan)
     g.gnn_plan_set_timing(plan, True)
     wall0 = time.perf_counter()
-    ms_total = timed(headline_flushed)
+    ms_total, per_step = timed(headline_flushed)
     wall = time.perf_counter() - wall0
     g.gnn_plan_set_timing(plan, False)
     kt = g.gnn_plan_timing_read(plan)
-    ms_other = None if args.no_other_cache else timed(not headline_flushed) / args.steps
+    ms_other = None if args.no_other_cache else timed(not headline_flushed)[0] / args.steps
     del flush_buf
     ms_step = ms_total / args.steps
     value = E / (ms_step * 1e-3) / 1e9
@@ -657,6 +661,8 @@ def bench(args) -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_ms": {"median": round(float(np.median(per_step)), 5), "min": round(min(per_step), 5),
+                    "max": round(max(per_step), 5)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

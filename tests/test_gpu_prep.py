@@ -78,6 +78,7 @@ def test_buckets_and_csc(g, T, C, W, order):
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d["c_" + k], cref[k]), "c_" + k
     assert np.array_equal(d["c_light_sched"], oracle.launch_order(cip, cref["light"], order, T))
+    assert np.array_equal(d["c_light_by_degree"], oracle.launch_order(cip, cref["light"], 1, T))
     assert d["n_light"] + d["n_heavy"] == n
 
 
