@@ -70,15 +70,22 @@ __device__ __forceinline__ uint4 ldg16(const void *base, int64_t elem, bool ok) 
               : make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Staged rows are padded by kRowPad elements (16 bytes): consecutive rows then
+// start 4 banks apart, so the 16 rows read by a product's 16-byte operand
+// loads, and the 4 rows read at once by the strided 16-bit transposed-operand
+// reads, fall on different banks (unpadded, 4 rows 8*width bytes apart
+// shared their banks); rows stay 16-byte aligned.
+constexpr int kRowPad = 8;
+
 // Stage rows r0..r0+15 (head-group columns) of a [N, H*D] bf16 table into
-// LDS as [16][HW*D]; rows >= N and heads >= H are zero.
+// LDS as [16][stride] (stride = HW*D + kRowPad); rows >= N and heads >= H are zero.
 __device__ __forceinline__ void stage_rows(uint16_t *dst, const void *src, int r0, int N, int64_t rowlen, int64_t c0,
-                                           int width, int64_t valid_width) {
+                                           int width, int stride, int64_t valid_width) {
     const int nvec = width / 8;
     for (int v = threadIdx.x; v < 16 * nvec; v += kTileThreads) {
         const int r = v / nvec, e = (v % nvec) * 8;
         const bool ok = (r0 + r < N) && (e < valid_width);
-        *reinterpret_cast<uint4 *>(dst + r * width + e) = ldg16(src, (int64_t)(r0 + r) * rowlen + c0 + e, ok);
+        *reinterpret_cast<uint4 *>(dst + r * stride + e) = ldg16(src, (int64_t)(r0 + r) * rowlen + c0 + e, ok);
     }
 }
 
@@ -106,11 +113,15 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
     const int rb = A.blocks[blockIdx.x / G.NHG], hg = blockIdx.x % G.NHG;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), l = lane_id();
     const int64_t rowlen = (int64_t)G.H * D;
-    const int width = HW * D;
+    const int width = HW * D, stride = width + kRowPad;
     const int64_t c0 = (int64_t)hg * HW * D;
     const int64_t valid = rowlen - c0;
-    float *state = lds;                                                     // [16][HW][D+2]
-    uint16_t *vst = reinterpret_cast<uint16_t *>(lds + 16 * HW * (D + 2));  // [16][HW*D]
+    // per-row state [16][HW][SW]: acc[D], m, l; SW odd so that the 16 rows a
+    // store writes at once fall on different banks (an even SW put HW*SW a
+    // multiple of the bank count)
+    const int SW = D + 3;
+    float *state = lds;
+    uint16_t *vst = reinterpret_cast<uint16_t *>(lds + 16 * HW * SW);     // [16][stride]
     const int row0 = rb * 16;
     const int m = l & 15, q4 = l >> 4;
 
@@ -135,7 +146,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
     }
     for (int t = A.tile_ptr[rb]; t < A.tile_ptr[rb + 1]; ++t) {
         const int col0 = A.tile_rc[2 * t + 1] * 16;
-        stage_rows(vst, P.V, col0, N, rowlen, c0, width, valid);
+        stage_rows(vst, P.V, col0, N, rowlen, c0, width, stride, valid);
         __syncthreads();
         const uint64_t word = A.tile_mask[4 * (int64_t)t + (m >> 2)];
 #pragma unroll
@@ -175,7 +186,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
             for (int c = 0; c < DC; ++c) {
                 i16x4_t va;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) va[i] = (short)vst[(4 * q4 + i) * width + hh[s] * D + c * 16 + m];
+                for (int i = 0; i < 4; ++i) va[i] = (short)vst[(4 * q4 + i) * stride + hh[s] * D + c * 16 + m];
                 acc[s][c] = acc[s][c] * cf;
                 acc[s][c] = mfma16(va, pb, acc[s][c]);
             }
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
 #pragma unroll
     for (int s = 0; s < HS; ++s) {
         if (!hv[s]) continue;
-        float *row = state + ((int64_t)m * HW + hh[s]) * (D + 2);
+        float *row = state + ((int64_t)m * HW + hh[s]) * SW;
 #pragma unroll
         for (int c = 0; c < DC; ++c)
 #pragma unroll
@@ -209,7 +220,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
 #pragma unroll
         for (int k = 0; k < NV; ++k) st.acc[k] = 0.f;
         if (lp.g == 0 && lp.act) {
-            const float *row = state + ((int64_t)r * HW + lp.hh) * (D + 2);
+            const float *row = state + ((int64_t)r * HW + lp.hh) * SW;
             st.m = row[D];
             st.l = row[D + 1];
 #pragma unroll
@@ -232,13 +243,13 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, Tile
     const int rb = A.blocks[blockIdx.x / G.NHG], hg = blockIdx.x % G.NHG;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), l = lane_id();
     const int64_t rowlen = (int64_t)G.H * D;
-    const int width = HW * D;
+    const int width = HW * D, stride = width + kRowPad;
     const int64_t c0 = (int64_t)hg * HW * D;
     const int64_t valid = rowlen - c0;
     const int SW = 2 * D + 1;
     float *state = lds;                                                    // [16][HW][2D+1]: A, B, Delta
-    uint16_t *kst = reinterpret_cast<uint16_t *>(lds + 16 * HW * SW);      // [16][HW*D]
-    uint16_t *vst = kst + 16 * width;
+    uint16_t *kst = reinterpret_cast<uint16_t *>(lds + 16 * HW * SW);      // [16][stride]
+    uint16_t *vst = kst + 16 * stride;
     const int row0 = rb * 16;
     const int m = l & 15, q4 = l >> 4;
 
@@ -266,8 +277,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, Tile
     }
     for (int t = A.tile_ptr[rb]; t < A.tile_ptr[rb + 1]; ++t) {
         const int col0 = A.tile_rc[2 * t + 1] * 16;
-        stage_rows(kst, P.K, col0, N, rowlen, c0, width, valid);
-        stage_rows(vst, P.V, col0, N, rowlen, c0, width, valid);
+        stage_rows(kst, P.K, col0, N, rowlen, c0, width, stride, valid);
+        stage_rows(vst, P.V, col0, N, rowlen, c0, width, stride, valid);
         __syncthreads();
         const uint64_t word = A.tile_mask[4 * (int64_t)t + (m >> 2)];
 #pragma unroll
@@ -276,7 +287,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, Tile
             f32x4_t sc = {0.f, 0.f, 0.f, 0.f}, dc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk) {
-                const int off = m * width + hh[s] * D + kk * 32 + 8 * q4;
+                const int off = m * stride + hh[s] * D + kk * 32 + 8 * q4;
                 sc = mfma32(*reinterpret_cast<const uint4 *>(kst + off), qop[s][kk], sc);
                 dc = mfma32(*reinterpret_cast<const uint4 *>(vst + off), gop[s][kk], dc);
             }
@@ -293,7 +304,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, Tile
             for (int c = 0; c < DC; ++c) {
                 i16x4_t ka;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ka[i] = (short)kst[(4 * q4 + i) * width + hh[s] * D + c * 16 + m];
+                for (int i = 0; i < 4; ++i) ka[i] = (short)kst[(4 * q4 + i) * stride + hh[s] * D + c * 16 + m];
                 Aa[s][c] = mfma16(ka, pdb, Aa[s][c]);
                 Ba[s][c] = mfma16(ka, pb, Ba[s][c]);
             }
@@ -351,13 +362,13 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
     const int cb = A.blocks[blockIdx.x / G.NHG], hg = blockIdx.x % G.NHG;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), l = lane_id();
     const int64_t rowlen = (int64_t)G.H * D;
-    const int width = HW * D;
+    const int width = HW * D, stride = width + kRowPad;
     const int64_t c0 = (int64_t)hg * HW * D;
     const int64_t valid = rowlen - c0;
-    const int SW = 2 * D;
-    float *state = lds;                                                    // [16][HW][2D]: dK, dV
-    uint16_t *qst = reinterpret_cast<uint16_t *>(lds + 16 * HW * SW);      // [16][HW*D]
-    uint16_t *gst = qst + 16 * width;
+    const int SW = 2 * D + 1;                                              // odd: see the forward's state
+    float *state = lds;                                                    // [16][HW][SW]: dK, dV
+    uint16_t *qst = reinterpret_cast<uint16_t *>(lds + 16 * HW * SW);      // [16][stride]
+    uint16_t *gst = qst + 16 * stride;
     const int col0 = cb * 16;
     const int n = l & 15, q4 = l >> 4;
 
@@ -383,8 +394,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
     for (int x = A.tile_ptr[cb]; x < A.tile_ptr[cb + 1]; ++x) {
         const int t = A.tile_ids[x];
         const int row0 = A.tile_rc[2 * t] * 16;
-        stage_rows(qst, P.Q, row0, N, rowlen, c0, width, valid);
-        stage_rows(gst, P.dO, row0, N, rowlen, c0, width, valid);
+        stage_rows(qst, P.Q, row0, N, rowlen, c0, width, stride, valid);
+        stage_rows(gst, P.dO, row0, N, rowlen, c0, width, stride, valid);
         __syncthreads();
         const uint64_t word = A.tile_mask[4 * (int64_t)t + q4];   // rows 4*q4 .. 4*q4+3
 #pragma unroll
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
             f32x4_t sc = {0.f, 0.f, 0.f, 0.f}, dc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk) {
-                const int off = n * width + hh[s] * D + kk * 32 + 8 * q4;   // row m = l % 16 of Q_b / dO_b
+                const int off = n * stride + hh[s] * D + kk * 32 + 8 * q4;   // row m = l % 16 of Q_b / dO_b
                 sc = mfma32(*reinterpret_cast<const uint4 *>(qst + off), kop[s][kk], sc);
                 dc = mfma32(*reinterpret_cast<const uint4 *>(gst + off), vop[s][kk], dc);
             }
@@ -415,8 +426,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
                 i16x4_t ga, qa;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    ga[i] = (short)gst[(4 * q4 + i) * width + hh[s] * D + c * 16 + n];
-                    qa[i] = (short)qst[(4 * q4 + i) * width + hh[s] * D + c * 16 + n];
+                    ga[i] = (short)gst[(4 * q4 + i) * stride + hh[s] * D + c * 16 + n];
+                    qa[i] = (short)qst[(4 * q4 + i) * stride + hh[s] * D + c * 16 + n];
                 }
                 dVa[s][c] = mfma16(ga, pb, dVa[s][c]);
                 dKa[s][c] = mfma16(qa, dsb, dKa[s][c]);
@@ -467,10 +478,10 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
 bool tile_supported(gnn_dtype_t dt, int D) { return dt == GNN_BF16 && (D == 32 || D == 64 || D == 128); }
 
 static size_t tile_lds(int kind, int HW, int D) {
-    const size_t stage = (size_t)16 * HW * D * 2;
-    if (kind == 0) return (size_t)16 * HW * (D + 2) * 4 + stage;
+    const size_t stage = (size_t)16 * (HW * D + kRowPad) * 2;
+    if (kind == 0) return (size_t)16 * HW * (D + 3) * 4 + stage;
     if (kind == 1) return (size_t)16 * HW * (2 * D + 1) * 4 + 2 * stage;
-    return (size_t)16 * HW * (2 * D) * 4 + 2 * stage;
+    return (size_t)16 * HW * (2 * D + 1) * 4 + 2 * stage;
 }
 
 // head-group geometry of the tile kernels: as the CSR path, with the head
