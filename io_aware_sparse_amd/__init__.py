@@ -239,12 +239,12 @@ def _copy_dev(ptr, count, np_dtype):
     if count == 0 or not ptr:
         return out
     torch.cuda.synchronize()
-    hip = C.CDLL("libamdhip64.so")
-    hip.hipMemcpy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int]
-    hip.hipMemcpy.restype = C.c_int
-    rc = hip.hipMemcpy(out.ctypes.data_as(C.c_void_p), C.c_void_p(ptr), out.nbytes, 2)  # device to host
-    if rc != 0:
-        raise RuntimeError(f"hipMemcpy failed ({rc})")
+
+    class _View:   # the plan's device array, seen by torch without a copy (torch reads it only)
+        __cuda_array_interface__ = {"shape": (int(count),), "typestr": np.dtype(np_dtype).str,
+                                    "data": (int(ptr), False), "version": 3}
+
+    out[:] = torch.as_tensor(_View(), device="cuda").cpu().numpy()   # copied by torch's own HIP runtime
     return out
 
 
