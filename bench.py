@@ -171,10 +171,19 @@ def kernel_bytes(kind, c, H, D, s, v_alias=True):
 
 # ---------------------------------------------------------------- profiles
 
-def read_traffic(kernel: str, workload: str):
-    """Scaled HBM bytes per launch from a committed counter summary, or None
-    if there is none or it was taken on different kernel sources."""
-    path = os.path.join(PROFILES, f"{kernel}__{workload}__counters.txt")
+def profile_tag(workload: str, tiles: bool, extra_backward: bool, reorder: str) -> str:
+    """Name of a run variant in the profile summaries: the workload, then
+    __tiles (tile path on), __bwd (gradient pass added to a forward-only
+    workload) and __<order> (graph relabelled), in that order."""
+    return (workload + ("__tiles" if tiles else "") + ("__bwd" if extra_backward else "")
+            + (f"__{reorder}" if reorder != "none" else ""))
+
+
+def read_traffic(kernel: str, tag: str):
+    """Scaled HBM bytes per launch from a committed counter summary of the
+    same run variant (`profile_tag`), or None if there is none or it was
+    taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"{kernel}__{tag}__counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -651,7 +660,10 @@ def bench(args) -> int:
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dk = kernels[dom]
     achieved = dk["GBps"]
-    traffic = read_traffic(dom, args.workload)
+    import workloads
+    tag = profile_tag(args.workload, int(info["n_tiles"]) > 0,
+                      wl.backward and not workloads.SPECS[args.workload]["backward"], args.reorder)
+    traffic = read_traffic(dom, tag)
     step_bytes = sum(kernel_bytes(k, counts, H, D, s, v_alias=v_alias) for k in kernels)
     rec = {
         "metric": METRIC,
@@ -696,6 +708,7 @@ def bench(args) -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
             "traffic": traffic,
+            "traffic_source": f"profiles/{dom}__{tag}__counters.txt" if traffic is not None else None,
             "alg_bytes_per_launch": dk["alg_bytes"],
             "avg_launch_us": dk["avg_us"],
         },

@@ -63,7 +63,7 @@ def test_cached_weights(g, norm):
         assert (w == 0).any()                        # the graph has sources without entries
 
 
-CASES = [("f32", 4), ("f32", 128), ("f32", 320), ("bf16", 8), ("bf16", 128), ("bf16", 1032)]
+CASES = [("f32", 4), ("f32", 96), ("f32", 128), ("f32", 320), ("bf16", 8), ("bf16", 128), ("bf16", 200), ("bf16", 1032)]
 
 
 @pytest.mark.parametrize("dtype,F", CASES)
