@@ -1,0 +1,119 @@
+"""Host logic of bench.py, on the CPU: the one-GPU guard, the counter
+calibration behind `roofline.traffic`, the staleness check of committed
+counter summaries, the run-variant names of the summaries, and the rocprofv3
+kernel-statistics summary."""
+import csv
+import os
+import subprocess
+import sys
+import types
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def _counters(d, counter, rows):
+    _write_csv(os.path.join(d, "pass", "x_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               [(k, counter, v) for k, v in rows])
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""                    # no JSON line
+
+
+def test_traffic_is_scaled_by_the_copy_probe(tmp_path):
+    """A copy of 1 GiB whose FETCH_SIZE reads half the copied KiB gives a fetch
+    scale of 2; WRITE_SIZE reading the full size gives 1. Kernel dispatches
+    are averaged; other kernels in the same pass are ignored."""
+    kern = "void gnn::k_fwd_main<float, 4, 1, 4>(gnn::FwdParams)"
+    other = "void gnn::k_fwd_merge<float, 4>(gnn::FwdParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    _counters(tmp_path / "f", "FETCH_SIZE", [(kern, 1000.0), (kern, 3000.0), (other, 99.0)])
+    _counters(tmp_path / "w", "WRITE_SIZE", [(kern, 500.0), (kern, 500.0)])
+    _counters(tmp_path / "cf", "FETCH_SIZE", [(copy, 524288.0)])
+    _counters(tmp_path / "cw", "WRITE_SIZE", [(copy, 1048576.0)])
+    out = tmp_path / "s.txt"
+    args = types.SimpleNamespace(traffic=[str(tmp_path / x) for x in ("f", "w", "cf", "cw")], kernel="gatv2_fwd_main",
+                                 kernel_regex="k_fwd_main", copy_mib=1024, workload="w", bench_args="", out=str(out))
+    assert bench.traffic_summary(args) == 0
+    vals = dict(line.split(":", 1) for line in out.read_text().splitlines() if ":" in line and line[0] != "#")
+    assert float(vals["fetch_bytes_per_launch"]) == 2000.0 * 1024 * 2
+    assert float(vals["write_bytes_per_launch"]) == 500.0 * 1024
+    assert float(vals["traffic_bytes_per_launch"]) == 2000.0 * 1024 * 2 + 500.0 * 1024
+    assert vals["kernel_symbol"].strip() == kern
+
+
+def test_missing_kernel_in_a_counter_pass_is_an_error(tmp_path):
+    _counters(tmp_path / "f", "FETCH_SIZE", [("void other()", 1.0)])
+    with pytest.raises(SystemExit):
+        bench._counter_means(str(tmp_path / "f"), "FETCH_SIZE", "k_fwd_main")
+
+
+def test_committed_traffic_is_ignored_once_sources_change(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    tag = bench.profile_tag("wl", False, False, "none")
+    path = tmp_path / f"gt_fwd_main__{tag}__counters.txt"
+    good = bench.kernel_source_hash("gt_fwd_main")
+    path.write_text(f"# header: with a colon\nsource_sha256: {good}\ntraffic_bytes_per_launch: 1234\n")
+    assert bench.read_traffic("gt_fwd_main", tag) == 1234.0
+    path.write_text("source_sha256: 0000000000000000\ntraffic_bytes_per_launch: 1234\n")
+    assert bench.read_traffic("gt_fwd_main", tag) is None
+    assert bench.read_traffic("gt_fwd_main", "no_such_run") is None
+
+
+def test_source_hash_follows_the_kernel_family():
+    attn = bench.kernel_source_hash("gt_fwd_main")
+    assert bench.kernel_source_hash("gatv2_bwd_src_main") == attn
+    assert bench.kernel_source_hash("reduce_fwd_main") != attn
+    assert bench.kernel_source_hash("spmm_t_main") == bench.kernel_source_hash("spmm_main") != attn
+
+
+def test_profile_tag_names_each_variant():
+    assert bench.profile_tag("gt_comm16_n1m_deg27", False, False, "none") == "gt_comm16_n1m_deg27"
+    assert bench.profile_tag("gt_comm16_n1m_deg27", True, False, "none") == "gt_comm16_n1m_deg27__tiles"
+    assert bench.profile_tag("gatv2_zipf21_n100k", False, True, "none") == "gatv2_zipf21_n100k__bwd"
+    assert bench.profile_tag("gatv2_zipf21_n100k", False, False, "degree") == "gatv2_zipf21_n100k__degree"
+    assert bench.profile_tag("a", True, True, "rcm") == "a__tiles__bwd__rcm"
+
+
+def test_every_committed_counter_summary_names_a_known_variant():
+    """Each committed counter summary belongs to a workload and variant the
+    bench can produce, so the bench finds it by the same name."""
+    import inspect
+
+    import workloads
+    modelled = inspect.getsource(bench.kernel_bytes)
+    tags = {bench.profile_tag(w, t, b, r) for w in workloads.SPECS for t in (False, True) for b in (False, True)
+            for r in ("none", "degree", "rcm")}
+    for fn in os.listdir(os.path.join(ROOT, "profiles")):
+        if fn.endswith("__counters.txt"):
+            kernel, tag = fn[: -len("__counters.txt")].split("__", 1)
+            assert tag in tags, fn
+            assert f'"{kernel}"' in modelled, fn          # a kernel the byte model knows
+
+
+def test_kernel_stats_summary_sorts_by_total_time(tmp_path):
+    hdr = ["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs", "Percentage"]
+    _write_csv(str(tmp_path / "t" / "x_kernel_stats.csv"), hdr,
+               [("small", 2, 2000, 1000, 900, 1100, 10.0), ("big", 3, 18000, 6000, 5000, 7000, 90.0)])
+    out = tmp_path / "sum.txt"
+    args = types.SimpleNamespace(summarize=str(tmp_path / "t"), command="cmd", kernel="gt_fwd_main", out=str(out))
+    assert bench.summarize(args) == 0
+    rows = [line.split() for line in out.read_text().splitlines() if line.strip().endswith(("big", "small"))]
+    assert [r[-1] for r in rows] == ["big", "small"]
+    assert float(rows[0][1]) == 6.0 and float(rows[1][1]) == 1.0      # average in microseconds
