@@ -2,11 +2,13 @@
 //
 // Standalone executable, not part of libgnn_attn.so. It times, with HIP
 // events over 5 launches each, three access patterns on one GPU:
-//   read    a grid-stride 16-byte-per-lane streaming read of 4 GiB;
+//   read    a grid-stride 16-byte-per-lane streaming read of 4 GiB, with
+//           one load or four independent loads per lane in flight;
 //   copy    a grid-stride copy of 2 GiB (read + write bytes counted);
 //   gather  one wave per destination gathering 64 rows of R bytes each at
 //           seeded random indices from a table of T bytes, R in {1024, 512,
-//           256} and T in {1 GiB, 4 GiB}; the bytes counted are the rows and
+//           256} and T from 64 MiB (held by the 256 MB Infinity Cache after
+//           the first launch) to 4 GiB; the bytes counted are the rows and
 //           the int32 indices. This is the access pattern of the light-node
 //           kernels (a row of H*D elements per edge), without their arithmetic.
 // Every index is below the table's row count and every table lies inside the
@@ -35,6 +37,20 @@ __global__ void k_read(const uint4 *__restrict__ a, int64_t n4, float *out) {
         s += __uint_as_float(v.x ^ v.y ^ v.z ^ v.w);
     }
     if (s == 12345.678f) out[0] = s;   // keeps the loads; never true for the fill used
+}
+
+// four independent loads per lane before any use
+__global__ void k_read4(const uint4 *__restrict__ a, int64_t n4, float *out) {
+    float s = 0.f;
+    const int64_t st = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += 4 * st) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = i + u * st < n4 ? a[i + u * st] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s += __uint_as_float(v[u].x ^ v[u].y ^ v[u].z ^ v[u].w);
+    }
+    if (s == 12345.678f) out[0] = s;
 }
 
 __global__ void k_copy(const uint4 *__restrict__ a, uint4 *__restrict__ b, int64_t n4) {
@@ -86,6 +102,14 @@ int main() {
         CHECK(hipEventSynchronize(e1));
         CHECK(hipEventElapsedTime(&ms, e0, e1));
         std::printf("read 4 GiB, grid %d x 256: %.1f GB/s\n", grid, 5.0 * bytes / (ms * 1e-3) / 1e9);
+        hipLaunchKernelGGL(k_read4, dim3(grid), dim3(256), 0, 0, a, n4, out);
+        CHECK(hipEventRecord(e0));
+        for (int r = 0; r < 5; ++r) hipLaunchKernelGGL(k_read4, dim3(grid), dim3(256), 0, 0, a, n4, out);
+        CHECK(hipEventRecord(e1));
+        CHECK(hipEventSynchronize(e1));
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        std::printf("read 4 GiB, 4 loads per lane in flight, grid %d x 256: %.1f GB/s\n", grid,
+                    5.0 * bytes / (ms * 1e-3) / 1e9);
         const int64_t h4 = n4 / 2;
         hipLaunchKernelGGL(k_copy, dim3(grid), dim3(256), 0, 0, a, b, h4);
         CHECK(hipEventRecord(e0));
@@ -98,7 +122,7 @@ int main() {
     }
     for (int row_bytes : {1024, 512, 256}) {
         const int row4 = row_bytes / 16;
-        for (int64_t table_bytes : {1ll << 30, 4ll << 30}) {
+        for (int64_t table_bytes : {64ll << 20, 256ll << 20, 1ll << 30, 4ll << 30}) {
             const int64_t n_rows = table_bytes / row_bytes;
             const int deg = 64;
             const int32_t nd = (int32_t)std::min<int64_t>(1 << 20, (3ll << 30) / row_bytes / deg);
