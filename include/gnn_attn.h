@@ -35,9 +35,12 @@
  *   - D must be 16, 32, 64 or 128; H >= 1. Feature pointers must be 16-byte
  *     aligned. E < 2^31.
  *   - A node with no in-edges gets O = 0, LSE = -inf and zero gradients.
- *   - Attention calls are asynchronous on `stream` and never synchronise the
- *     host. gnn_csr_build and gnn_plan_create synchronise `stream` once to
- *     read back counts.
+ *   - Attention calls are asynchronous on `stream` and do not synchronise
+ *     the host, with one exception: a call on a plan whose workspace is
+ *     smaller than the call needs (the first call at a larger H*D, or the
+ *     first backward) synchronises `stream` once before replacing it.
+ *     gnn_csr_build and gnn_plan_create synchronise `stream` once to read
+ *     back counts.
  *   - Every call returns a gnn_status_t; argument errors are detected on the
  *     host before any HIP call is made. No exception crosses the ABI.
  *   - A plan may be used by one stream at a time (it owns reusable

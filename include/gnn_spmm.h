@@ -32,8 +32,10 @@ typedef enum {
 /*
  * Compute and cache the per-entry weights of `norm` in the plan (fp32, in CSR
  * order and, when the plan was created with want_csc, in transposed-adjacency
- * order), replacing any earlier cache. Allocates 4*E bytes per order once.
- * GNN_ERR_INVALID_ARG for a NULL plan or an unknown norm.
+ * order), replacing any earlier cache. Allocates 4*E bytes per order on the
+ * first call; later calls rewrite those buffers in place, ordered after
+ * earlier work on `stream` (products still running on another stream race
+ * with it). GNN_ERR_INVALID_ARG for a NULL plan or an unknown norm.
  */
 int gnn_spmm_prepare(gnn_plan_t plan, gnn_norm_t norm, hipStream_t stream);
 

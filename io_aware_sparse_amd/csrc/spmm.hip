@@ -295,12 +295,15 @@ int gnn_spmm_prepare(gnn_plan_t plan, gnn_norm_t norm, hipStream_t stream) {
     if (norm != GNN_NORM_SUM && norm != GNN_NORM_MEAN && norm != GNN_NORM_GCN) return GNN_ERR_INVALID_ARG;
     const int32_t n = plan->n_nodes;
     const int64_t e = plan->n_edges;
-    GNN_TRY(dev_alloc(plan->spmm_w, (size_t)std::max<int64_t>(e, 1) * 4));
+    const size_t bytes = (size_t)std::max<int64_t>(e, 1) * 4;
+    // a later call rewrites the cached weights in place (stream-ordered after
+    // earlier products on the same stream), never freeing a buffer in use
+    if (plan->spmm_w.bytes != bytes) GNN_TRY(dev_alloc(plan->spmm_w, bytes));
     if (n > 0)
         hipLaunchKernelGGL(k_spmm_w_rows, grid1d((int64_t)n * kWave), dim3(256), 0, stream, plan->indptr,
                            plan->indices, n, (int)norm, as<float>(plan->spmm_w));
     if (plan->has_csc) {
-        GNN_TRY(dev_alloc(plan->spmm_cw, (size_t)std::max<int64_t>(e, 1) * 4));
+        if (plan->spmm_cw.bytes != bytes) GNN_TRY(dev_alloc(plan->spmm_cw, bytes));
         if (n > 0)
             hipLaunchKernelGGL(k_spmm_w_cols, grid1d((int64_t)n * kWave), dim3(256), 0, stream, plan->indptr,
                                as<int32_t>(plan->cindptr), as<int32_t>(plan->cindices), n, (int)norm,
