@@ -505,6 +505,20 @@ def make_step(g, wl, indptr, indices, plan, T, op="max", msg="src"):
     return step
 
 
+def host_cpu() -> str:
+    """CPU model and the logical CPUs this process may run on."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {len(os.sched_getaffinity(0))} of {os.cpu_count()} logical CPUs in this process's affinity"
+
+
 def cpu_baseline(wl, rp, rx, target_s, threads=None, op="max", msg="src", norm="gcn"):
     """fp64 oracle on a seeded sample of destination rows (and the same nodes
     as sources for the gradient), sized to about target_s seconds."""
@@ -576,7 +590,7 @@ def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg, norm):
         reps += 1
     t = tt / reps
     cores = 1 if wl.kind == "spmm" else oracle.num_threads()      # scipy's sparse product runs on one thread
-    return dict(value=round(e / t / 1e9, 6), unit="GEdges/s", cores=cores, kind="oracle",
+    return dict(value=round(e / t / 1e9, 6), unit="GEdges/s", cores=cores, kind="oracle", host=host_cpu(),
                 sample=f"{r} destination rows drawn uniformly (seed 12345) covering {e} of {int(csum[-1])} edges"
                        + (" (forward + backward, the same nodes as sources)" if wl.backward else " (forward)")
                        + f", {t:.2f} s per pass, mean of {reps}")
