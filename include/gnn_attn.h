@@ -33,7 +33,7 @@
  *     dtype (fp32 or bf16). Arithmetic is fp32; bf16 results are rounded to
  *     nearest-even. LSE is fp32 [N, H] in natural-log units.
  *   - D must be 16, 32, 64 or 128; H >= 1. Feature pointers must be 16-byte
- *     aligned. E < 2^31.
+ *     aligned. E <= 2^31 - 2^21 (2,145,386,496; GNN_ERR_INVALID_ARG above).
  *   - A node with no in-edges gets O = 0, LSE = -inf and zero gradients.
  *   - Attention calls are asynchronous on `stream` and do not synchronise
  *     the host, with one exception: a call on a plan whose workspace is
@@ -76,7 +76,8 @@ typedef struct gnn_plan_s *gnn_plan_t;   /* opaque; owns its device arrays */
  */
 typedef struct {
     int32_t light_threshold; /* T: in-degree <= T is light (one wave per node); default 512   */
-    int32_t chunk;           /* C: edges per wave on a heavy row; default 512, >= 1             */
+    int32_t chunk;           /* C: edges per wave on a heavy row; default 512, >= 1,
+                                C * waves_per_group <= 2^20                                        */
     int32_t waves_per_group; /* W: waves per heavy workgroup, merged in LDS; 1, 2, 4 or 8; default 4 */
     float tile_density;      /* tau: a 16x16 block with >= tau*256 edges becomes a dense tile;
                                 <= 0 disables the tile path; default 0                         */

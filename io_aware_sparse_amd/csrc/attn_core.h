@@ -431,7 +431,7 @@ static inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; 
 
 static inline int check_common(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
                         int32_t H, int32_t D, gnn_dtype_t dtype) {
-    if (N < 0 || E < 0 || E >= (1ll << 31) || H < 1 || !indptr) return GNN_ERR_INVALID_ARG;
+    if (N < 0 || E < 0 || E > kMaxEdges || H < 1 || !indptr) return GNN_ERR_INVALID_ARG;
     if (E > 0 && !indices) return GNN_ERR_INVALID_ARG;
     if (dtype != GNN_F32 && dtype != GNN_BF16) return GNN_ERR_UNSUPPORTED;
     if (!lanes_per_head(dtype, D)) return GNN_ERR_UNSUPPORTED;

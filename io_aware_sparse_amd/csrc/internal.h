@@ -10,6 +10,12 @@
 
 namespace gnn {
 
+// Size limits. Edge positions are int32 in the kernels, which add up to one
+// chunk group (C * W entries) and two steps of 64 entries to a position inside
+// a row; the headroom below keeps every such sum below 2^31.
+constexpr int64_t kMaxGroupSpan = 1ll << 20;                 // C * W
+constexpr int64_t kMaxEdges = (1ll << 31) - (1ll << 21);     // E
+
 // Remember the last HIP failure for gnn_status_string.
 void set_hip_error(hipError_t e, const char *what);
 

@@ -701,7 +701,7 @@ int gnn_csr_build(const int32_t *src, const int32_t *dst, int64_t n_edges_in, in
     if (n_edges_in > 0 && (!src || !dst)) return GNN_ERR_INVALID_ARG;
     if (cap > 0 && !indices) return GNN_ERR_INVALID_ARG;
     const int64_t m = n_edges_in + (add_self_loops ? n_nodes : 0);
-    if (m >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
+    if (m > kMaxEdges) return GNN_ERR_INVALID_ARG;
     if (n_nodes == 0 && n_edges_in > 0) return GNN_ERR_BAD_GRAPH;
     const int nb = bits_for(std::max<int64_t>(2, n_nodes));
     // scratch: keys, tmp keys (8 B each), flags, pos (4 B each), sort/scan scratch
@@ -741,7 +741,7 @@ done:
 
 int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nodes, int64_t n_edges,
                     const gnn_plan_opts *opts, hipStream_t stream, gnn_plan_t *plan_out) {
-    if (!plan_out || !indptr || n_nodes < 0 || n_edges < 0 || n_edges >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
+    if (!plan_out || !indptr || n_nodes < 0 || n_edges < 0 || n_edges > kMaxEdges) return GNN_ERR_INVALID_ARG;
     if (n_edges > 0 && !indices) return GNN_ERR_INVALID_ARG;
     gnn_plan_opts o;
     gnn_plan_opts_default(&o);
@@ -750,7 +750,7 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
         !(o.waves_per_group == 1 || o.waves_per_group == 2 || o.waves_per_group == 4 || o.waves_per_group == 8))
         return GNN_ERR_INVALID_ARG;
     if (o.tile_density > 1.0f || o.sched_order < 0 || o.sched_order > 2) return GNN_ERR_INVALID_ARG;
-    if ((int64_t)o.chunk * o.waves_per_group >= (1ll << 30)) return GNN_ERR_INVALID_ARG;
+    if ((int64_t)o.chunk * o.waves_per_group > kMaxGroupSpan) return GNN_ERR_INVALID_ARG;
 
     gnn_plan_s *p = new (std::nothrow) gnn_plan_s();
     if (!p) return GNN_ERR_OOM;

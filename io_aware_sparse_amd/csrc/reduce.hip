@@ -502,7 +502,7 @@ static RedGeom red_geom(int32_t N, int32_t F, gnn_dtype_t dt) {
 
 static int red_check(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
                      gnn_dtype_t dtype) {
-    if (N < 0 || E < 0 || E >= (1ll << 31) || F < 1 || !indptr) return GNN_ERR_INVALID_ARG;
+    if (N < 0 || E < 0 || E > kMaxEdges || F < 1 || !indptr) return GNN_ERR_INVALID_ARG;
     if (E > 0 && !indices) return GNN_ERR_INVALID_ARG;
     if (dtype != GNN_F32 && dtype != GNN_BF16) return GNN_ERR_UNSUPPORTED;
     const int s = dtype == GNN_BF16 ? 2 : 4;

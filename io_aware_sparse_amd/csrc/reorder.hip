@@ -384,7 +384,7 @@ extern "C" {
 
 int gnn_reorder(const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, gnn_order_t method,
                 int32_t *perm, hipStream_t stream) {
-    if (N < 0 || E < 0 || E >= (1ll << 31) || !indptr || (E > 0 && !indices) || (N > 0 && !perm))
+    if (N < 0 || E < 0 || E > kMaxEdges || !indptr || (E > 0 && !indices) || (N > 0 && !perm))
         return GNN_ERR_INVALID_ARG;
     if (method != GNN_ORDER_DEGREE && method != GNN_ORDER_RCM) return GNN_ERR_INVALID_ARG;
     if (N == 0) return GNN_OK;
@@ -401,7 +401,7 @@ int gnn_reorder(const int32_t *indptr, const int32_t *indices, int32_t N, int64_
 
 int gnn_permute_graph(const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, const int32_t *perm,
                       int32_t *new_indptr, int32_t *new_indices, hipStream_t stream) {
-    if (N < 0 || E < 0 || E >= (1ll << 31) || !indptr || !new_indptr || (E > 0 && (!indices || !new_indices)) ||
+    if (N < 0 || E < 0 || E > kMaxEdges || !indptr || !new_indptr || (E > 0 && (!indices || !new_indices)) ||
         (N > 0 && !perm))
         return GNN_ERR_INVALID_ARG;
     if (N == 0) {

@@ -57,6 +57,7 @@ def test_host_validation(g):
     assert fwd(D=24) == -2 and fwd(D=0) == -2 and fwd(D=256) == -2
     assert fwd(dt=7) == -2
     assert fwd(N=-1) == -1 and fwd(E=-1) == -1 and fwd(H=0) == -1 and fwd(E=1 << 31) == -1
+    assert fwd(E=(1 << 31) - (1 << 21) + 1) == -1          # edge limit: headroom for int32 positions
     assert fwd(q=A + 4) == -3
     assert fwd(ip=None) == -1
     assert L.gnn_attn_fwd(None, A, A, 10, 20, 2, 32, None, A, A, A, None, 0.0, 0, None) == -1
@@ -93,6 +94,7 @@ def test_host_validation(g):
     assert L.gnn_csr_build(None, A, 5, 3, 1, A, A, 10, C.byref(e), None) == -1
     assert L.gnn_csr_build(A, A, 5, 3, 1, A, A, 10, None, None) == -1
     assert L.gnn_csr_build(A, A, 1 << 31, 3, 1, A, A, 10, C.byref(e), None) == -1
+    assert L.gnn_csr_build(A, A, (1 << 31) - (1 << 21) - 2, 3, 1, A, A, 10, C.byref(e), None) == -1  # with self-loops
     # plans
     h = C.c_void_p()
     o = g.PlanOpts()
@@ -100,7 +102,10 @@ def test_host_validation(g):
     assert L.gnn_plan_opts_default(None) == -1
     assert L.gnn_plan_create(None, A, 10, 20, None, None, C.byref(h)) == -1
     assert L.gnn_plan_create(A, A, 10, 20, None, None, None) == -1
-    for field, bad in (("waves_per_group", 3), ("chunk", 0), ("light_threshold", -1)):
+    assert L.gnn_plan_create(A, A, 10, (1 << 31) - (1 << 21) + 1, None, None, C.byref(h)) == -1
+    assert L.gnn_reduce_fwd(None, A, A, 10, (1 << 31) - (1 << 21) + 1, 8, A, A, A, 0, 0, 0, None) == -1
+    assert L.gnn_reorder(A, A, 10, (1 << 31) - (1 << 21) + 1, 0, A, None) == -1
+    for field, bad in (("waves_per_group", 3), ("chunk", 0), ("light_threshold", -1), ("chunk", (1 << 18) + 1)):
         L.gnn_plan_opts_default(C.byref(o))
         setattr(o, field, bad)
         assert L.gnn_plan_create(A, A, 10, 20, C.byref(o), None, C.byref(h)) == -1, field
