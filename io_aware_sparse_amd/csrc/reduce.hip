@@ -513,9 +513,8 @@ static int red_check(gnn_plan_t plan, const int32_t *indptr, const int32_t *indi
     return GNN_OK;
 }
 
-template <class T, int OP, int MSG, bool SORTED, int RPW>
+template <class T, int OP, int MSG, bool SORTED, int RPW, int U = 4>
 static int launch_red_main(gnn_plan_t plan, const RedParams &P, hipStream_t s) {
-    constexpr int U = 4;
     const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NFG : ((int64_t)P.n_light + RPW - 1) / RPW;
     const int64_t blocks = (int64_t)P.n_groups * P.g.NFG + (light_waves + P.W - 1) / P.W;
     if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
@@ -523,20 +522,22 @@ static int launch_red_main(gnn_plan_t plan, const RedParams &P, hipStream_t s) {
                   0, s, P);
 }
 
-// Sorted rows on a plan, rows of up to 16 lanes (256 bytes): the light rows
-// run from the descending-degree list, 4 per wave, so rows of similar length
-// share a wave and each row merges only its own edge groups. Otherwise (wider
-// rows, where one row already fills the wave's edge groups and packing was
-// measured slower, or unsorted rows) one row per wave.
+// Sorted rows on a plan, rows of up to 32 lanes (512 bytes): the light rows
+// run from the descending-degree list, 4 per wave (rows of up to 256 bytes)
+// or 2 per wave with 8 edges per step (up to 512 bytes, so a row keeps the
+// 8 edges per step it has alone), so rows of similar length share a wave and
+// each row merges only its own edge groups. Otherwise (wider rows, or
+// unsorted rows) one row per wave.
 template <class T, int OP, int MSG>
 static int run_red_fwd(gnn_plan_t plan, RedParams &P, hipStream_t s) {
     const int64_t nk = (int64_t)P.n_heavy * P.g.F;
     if (nk) GNN_TRY(launch(plan, K_RED_INIT, k_red_init<OP>, grid1d(nk), dim3(256), 0, s, P.keys, nk));
     if (plan && plan->rows_sorted) {
-        if (P.g.NFG == 1 && P.g.G >= 4) {
+        if (P.g.NFG == 1 && P.g.G >= 2) {
             RedParams Q = P;
             Q.light = as<int32_t>(plan->fwd.by_degree);
-            GNN_TRY((launch_red_main<T, OP, MSG, true, 4>(plan, Q, s)));
+            if (P.g.G >= 4) GNN_TRY((launch_red_main<T, OP, MSG, true, 4>(plan, Q, s)));
+            else GNN_TRY((launch_red_main<T, OP, MSG, true, 2, 8>(plan, Q, s)));
         } else {
             GNN_TRY((launch_red_main<T, OP, MSG, true, 1>(plan, P, s)));
         }

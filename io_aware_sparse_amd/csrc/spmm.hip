@@ -14,9 +14,10 @@
 // has the transposed adjacency, in its order too.
 //
 // The product uses the degree-aware layout of the other kernels: a lane holds
-// one 16-byte slice of a feature row; light rows run one per wave, or 4 per
-// wave from the descending-degree list when a row spans at most 16 lanes
-// (256 bytes); heavy rows run as the plan's chunk groups, their W waves
+// one 16-byte slice of a feature row; light rows run from the
+// descending-degree list 4 per wave when a row spans at most 16 lanes
+// (256 bytes), 2 per wave with 8 edges per step when it spans 17-32 lanes
+// (512 bytes), else one per wave; heavy rows run as the plan's chunk groups, their W waves
 // summed in LDS and the groups summed in ascending order by a second pass.
 // fp32 accumulation, output rounded to the storage type; no atomics, so the
 // result is bitwise reproducible. The transposed product (dX = A_w^T dY) is
@@ -258,9 +259,8 @@ static SpGeom sp_geom(int32_t N, int32_t F, gnn_dtype_t dt) {
     return g;
 }
 
-template <class T, int RPW, bool TR>
+template <class T, int RPW, bool TR, int U = 4>
 static int launch_spmm_main(gnn_plan_t plan, const SpParams &P, int kind, hipStream_t s) {
-    constexpr int U = 4;
     constexpr int NV = Vec<T>::N;
     const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NFG : ((int64_t)P.n_light + RPW - 1) / RPW;
     const int64_t blocks = (int64_t)P.n_groups * P.g.NFG + (light_waves + P.W - 1) / P.W;
@@ -272,10 +272,11 @@ static int launch_spmm_main(gnn_plan_t plan, const SpParams &P, int kind, hipStr
 template <class T, bool TR>
 static int run_spmm(gnn_plan_t plan, SpParams &P, const int32_t *by_degree, hipStream_t s) {
     const int k_main = TR ? K_SPMM_T_MAIN : K_SPMM_MAIN, k_merge = TR ? K_SPMM_T_MERGE : K_SPMM_MERGE;
-    if (by_degree && P.g.NFG == 1 && P.g.G >= 4) {
+    if (by_degree && P.g.NFG == 1 && P.g.G >= 2) {
         SpParams Q = P;
         Q.light = by_degree;
-        GNN_TRY((launch_spmm_main<T, 4, TR>(plan, Q, k_main, s)));
+        if (P.g.G >= 4) GNN_TRY((launch_spmm_main<T, 4, TR>(plan, Q, k_main, s)));
+        else GNN_TRY((launch_spmm_main<T, 2, TR, 8>(plan, Q, k_main, s)));
     } else {
         GNN_TRY((launch_spmm_main<T, 1, TR>(plan, P, k_main, s)));
     }
