@@ -7,7 +7,8 @@
 // registers (online softmax) so no edge logit is written; the backward reads
 // a cached per-node log-sum-exp and recomputes every weight on the fly.
 // Degree-aware tiling (same section): light nodes (in-degree <= T) take one
-// wavefront each; heavy nodes are cut into chunk groups whose waves each
+// wavefront each (two per wavefront for rows of 257-512 bytes in the
+// forward); heavy nodes are cut into chunk groups whose waves each
 // stream <= C edges, merge their partial (m, l, acc) states in LDS, write one
 // partial per group, and a second pass merges a node's partials.
 //
@@ -29,7 +30,8 @@
 
 namespace gnn {
 
-template <class T, int LH, int MODE, int U>
+// RPW > 1: the light rows run RPW per wave (rows of at most 64/RPW lanes).
+template <class T, int LH, int MODE, int U, int RPW>
 __global__ __launch_bounds__(512) void k_fwd_main(FwdParams P) {
     using VT = Vec<T>;
     constexpr int NV = VT::N;
@@ -72,6 +74,18 @@ __global__ __launch_bounds__(512) void k_fwd_main(FwdParams P) {
         return;
     }
     const int64_t item = (int64_t)(blockIdx.x - heavy_blocks) * P.W + w;
+    if (RPW > 1) {                        // RPW rows of the light list per wave (NHG == 1)
+        const int64_t ni0 = item * RPW;
+        if (ni0 >= P.n_light) return;
+        const int64_t ni = ni0 + lane_id() / (kWave / RPW);
+        const int node = ni < P.n_light ? P.light[ni] : -1;
+        const int e0 = node >= 0 ? P.indptr[node] : 0, e1 = node >= 0 ? P.indptr[node + 1] : 0;
+        const LanePos lp = lane_pos<LH, NV, RPW>(P.g, 0);
+        SoftState<NV> st;
+        fwd_stream<T, LH, MODE, U, RPW>(P, lp, node < 0 ? 0 : node, e0, e1, st);
+        if (node >= 0) write_out<T, NV>(P, lp, node, st);
+        return;
+    }
     const int64_t ni = item / P.g.NHG;
     if (ni >= P.n_light) return;
     const int hg = (int)(item % P.g.NHG);
@@ -277,17 +291,33 @@ __global__ __launch_bounds__(256) void k_bwd_src_merge(BwdParams P) {
 // host side
 // ======================================================================
 
-template <class T, int LH, int MODE>
-static int run_fwd(gnn_plan_t plan, FwdParams &P, hipStream_t s) {
-    constexpr int U = 4;
+template <class T, int LH, int MODE, int U, int RPW>
+static int launch_fwd_main(gnn_plan_t plan, const FwdParams &P, hipStream_t s) {
     constexpr int NV = Vec<T>::N;
     const int kind_main = MODE == M_GT ? K_FWD_MAIN : K_GAT_MAIN;
-    const int kind_merge = MODE == M_GT ? K_FWD_MERGE : K_GAT_MERGE;
-    const int64_t light_blocks = ((int64_t)P.n_light * P.g.NHG + P.W - 1) / P.W;
-    const int64_t blocks = (int64_t)P.n_groups * P.g.NHG + light_blocks;
+    const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NHG : ((int64_t)P.n_light + RPW - 1) / RPW;
+    const int64_t blocks = (int64_t)P.n_groups * P.g.NHG + (light_waves + P.W - 1) / P.W;
     if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
     const size_t lds = P.n_groups ? (size_t)P.W * (1 << P.g.lr_shift) * (NV + 2) * sizeof(float) : 0;
-    GNN_TRY(launch(plan, kind_main, k_fwd_main<T, LH, MODE, U>, dim3((unsigned)blocks), dim3(64 * P.W), lds, s, P));
+    return launch(plan, kind_main, k_fwd_main<T, LH, MODE, U, RPW>, dim3((unsigned)blocks), dim3(64 * P.W), lds, s,
+                  P);
+}
+
+// Light rows of 257-512 bytes (two edge groups per wave) on a plan run from
+// the descending-degree list, 2 per wave with 8 edges per step, so each row
+// keeps the edges per step it would have alone and a wave has twice the
+// rows in flight; otherwise one (row, head group) per wave, 4 edges per
+// group and step.
+template <class T, int LH, int MODE>
+static int run_fwd(gnn_plan_t plan, FwdParams &P, const int32_t *by_degree, hipStream_t s) {
+    const int kind_merge = MODE == M_GT ? K_FWD_MERGE : K_GAT_MERGE;
+    if (by_degree && P.g.NHG == 1 && P.g.G == 2) {
+        FwdParams Q = P;
+        Q.light = by_degree;
+        GNN_TRY((launch_fwd_main<T, LH, MODE, 8, 2>(plan, Q, s)));
+    } else {
+        GNN_TRY((launch_fwd_main<T, LH, MODE, 4, 1>(plan, P, s)));
+    }
     if (P.n_heavy) {
         const int64_t mb = (int64_t)P.n_heavy * P.g.NHG;
         GNN_TRY(launch(plan, kind_merge, k_fwd_merge<T, LH>, dim3((unsigned)mb), dim3(64 * kMergeWaves), 0, s, P));
@@ -296,20 +326,21 @@ static int run_fwd(gnn_plan_t plan, FwdParams &P, hipStream_t s) {
 }
 
 template <int MODE>
-static int dispatch_fwd(gnn_plan_t plan, FwdParams &P, gnn_dtype_t dt, int D, hipStream_t s) {
+static int dispatch_fwd(gnn_plan_t plan, FwdParams &P, const int32_t *by_degree, gnn_dtype_t dt, int D,
+                        hipStream_t s) {
     if (dt == GNN_F32) {
         switch (D) {
-            case 16: return run_fwd<float, 4, MODE>(plan, P, s);
-            case 32: return run_fwd<float, 8, MODE>(plan, P, s);
-            case 64: return run_fwd<float, 16, MODE>(plan, P, s);
-            case 128: return run_fwd<float, 32, MODE>(plan, P, s);
+            case 16: return run_fwd<float, 4, MODE>(plan, P, by_degree, s);
+            case 32: return run_fwd<float, 8, MODE>(plan, P, by_degree, s);
+            case 64: return run_fwd<float, 16, MODE>(plan, P, by_degree, s);
+            case 128: return run_fwd<float, 32, MODE>(plan, P, by_degree, s);
         }
     } else {
         switch (D) {
-            case 16: return run_fwd<bf16_tag, 2, MODE>(plan, P, s);
-            case 32: return run_fwd<bf16_tag, 4, MODE>(plan, P, s);
-            case 64: return run_fwd<bf16_tag, 8, MODE>(plan, P, s);
-            case 128: return run_fwd<bf16_tag, 16, MODE>(plan, P, s);
+            case 16: return run_fwd<bf16_tag, 2, MODE>(plan, P, by_degree, s);
+            case 32: return run_fwd<bf16_tag, 4, MODE>(plan, P, by_degree, s);
+            case 64: return run_fwd<bf16_tag, 8, MODE>(plan, P, by_degree, s);
+            case 128: return run_fwd<bf16_tag, 16, MODE>(plan, P, by_degree, s);
         }
     }
     return GNN_ERR_UNSUPPORTED;
@@ -366,12 +397,13 @@ static int fwd_common(gnn_plan_t plan, const int32_t *indptr, const int32_t *ind
     if (tiles) {
         P.light = as<int32_t>(plan->light_nt);
         P.n_light = plan->n_light_nt;
-        GNN_TRY(dispatch_fwd<M_GT>(plan, P, dtype, D, s));
+        GNN_TRY(dispatch_fwd<M_GT>(plan, P, nullptr, dtype, D, s));   // light rows outside tiled blocks: one per wave
         return launch_tile_fwd(plan, P, D, s);
     }
-    if (mode == M_GT) return dispatch_fwd<M_GT>(plan, P, dtype, D, s);
-    if (mode == M_GAT_ALIAS) return dispatch_fwd<M_GAT_ALIAS>(plan, P, dtype, D, s);
-    return dispatch_fwd<M_GAT_SEPV>(plan, P, dtype, D, s);
+    const int32_t *by_degree = plan ? as<int32_t>(plan->fwd.by_degree) : nullptr;
+    if (mode == M_GT) return dispatch_fwd<M_GT>(plan, P, by_degree, dtype, D, s);
+    if (mode == M_GAT_ALIAS) return dispatch_fwd<M_GAT_ALIAS>(plan, P, by_degree, dtype, D, s);
+    return dispatch_fwd<M_GAT_SEPV>(plan, P, by_degree, dtype, D, s);
 }
 
 template <class T, int LH>

@@ -45,16 +45,21 @@ struct FwdParams {
 // per-lane position inside the wave's (node, head group) slice
 struct LanePos {
     int lane, g, r, hh, dv, h;
+    int rg0;       // first lane of this lane's row group (RPW rows per wave), else 0
     bool act;
     int64_t col;   // element offset inside the node's H*D row
 };
 
-template <int LH, int NV>
+// RPW > 1 (rows of at most 64/RPW lanes, one head group): the wave's lanes
+// split into RPW row groups of 64/RPW lanes, each streaming its own row with
+// the edge groups g = 0 .. G/RPW - 1 inside it.
+template <int LH, int NV, int RPW = 1>
 __device__ __forceinline__ LanePos lane_pos(const Geom &G, int hg) {
     LanePos p;
     p.lane = lane_id();
     const int LR = 1 << G.lr_shift;
-    p.g = p.lane >> G.lr_shift;
+    p.rg0 = p.lane & ~(kWave / RPW - 1);
+    p.g = (p.lane - p.rg0) >> G.lr_shift;
     p.r = p.lane & (LR - 1);
     p.hh = p.r / LH;
     p.dv = p.r % LH;
@@ -80,9 +85,9 @@ __device__ __forceinline__ void merge_state(SoftState<NV> &a, float m2, float l2
     a.m = mn;
 }
 
-template <int NV>
+template <int NV, int RPW = 1>
 __device__ __forceinline__ void merge_groups(SoftState<NV> &st, int lr_shift) {
-    for (int off = 1 << lr_shift; off < kWave; off <<= 1) {
+    for (int off = 1 << lr_shift; off < kWave / RPW; off <<= 1) {
         const float m2 = xor_lane(st.m, off), l2 = xor_lane(st.l, off);
         float a2[NV];
 #pragma unroll
@@ -95,7 +100,7 @@ __device__ __forceinline__ void merge_groups(SoftState<NV> &st, int lr_shift) {
 // wave-merged online-softmax state (valid in every lane). With reset false
 // the caller's state is continued (only edge group 0 may carry a non-empty
 // state, the other groups must start empty).
-template <class T, int LH, int MODE, int U>
+template <class T, int LH, int MODE, int U, int RPW = 1>
 __device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp, int node, int e0, int e1,
                                            SoftState<Vec<T>::N> &st, bool reset = true) {
     using VT = Vec<T>;
@@ -120,15 +125,22 @@ __device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp
         for (int k = 0; k < NV; ++k) st.acc[k] = 0.f;
     }
 
-    const int S = min(kWave, G.G * U);   // edges per step
-    const int UE = S / G.G;               // steps per group actually used
-    int jn = (lp.lane < S && e0 + lp.lane < e1) ? P.indices[e0 + lp.lane] : -1;
-    for (int base = e0; base < e1; base += S) {
+    const int GR = G.G / RPW;                       // edge groups of this row
+    const int S = min(kWave / RPW, GR * U);         // edges per step of this row
+    const int UE = S / GR;                          // steps per group actually used
+    const int li = lp.lane - lp.rg0;
+    int jn = (li < S && e0 + li < e1) ? P.indices[e0 + li] : -1;
+    // steps until every row of the wave has used up its edges (one row: until base >= e1)
+    for (int base = e0; RPW == 1 ? base < e1 : __any(base < e1); base += S) {
         const int jc = jn;
-        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? P.indices[base + S + lp.lane] : -1;
+        if (RPW == 1) {
+            if (base + S < e1) jn = (li < S && base + S + li < e1) ? P.indices[base + S + li] : -1;
+        } else {
+            jn = (li < S && base + S + li < e1) ? P.indices[base + S + li] : -1;
+        }
         int j[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) j[u] = (u < UE) ? __shfl(jc, u * G.G + lp.g, kWave) : -1;
+        for (int u = 0; u < U; ++u) j[u] = (u < UE) ? __shfl(jc, lp.rg0 + u * GR + lp.g, kWave) : -1;
         typename VT::raw kr[U], vr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -175,7 +187,7 @@ __device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp
         }
         st.m = mn;
     }
-    merge_groups(st, G.lr_shift);
+    merge_groups<NV, RPW>(st, G.lr_shift);
 }
 
 template <class T, int NV>
