@@ -94,6 +94,36 @@ def test_gt_fwd_empty_rows_and_scale(g, plan, dtype):
     assert np.all(host(O)[empty] == 0) and np.all(np.isneginf(host(L)[empty]))
 
 
+@pytest.mark.parametrize("dtype,D,H", [("f32", 32, 4), ("f32", 16, 8), ("bf16", 64, 4)])
+@pytest.mark.parametrize("plan", ["heavy_w1", "mixed", "mixed_w8"])
+def test_packed_light_rows_with_empty_rows(g, dtype, D, H, plan):
+    """Rows of 257-512 bytes run two per wave from the descending-degree list:
+    empty rows, an odd number of light rows (the last wave holds one row) and
+    both attention modes against the oracle."""
+    import torch
+    n = 2501
+    say("packed light rows", dtype, D, H, plan)
+    ip, ix, rp, rx = _graph(g, 4, n, self_loops=False)
+    empty = np.diff(rp) == 0
+    assert empty.any()
+    pl = _plan(g, ip, ix, plan)
+    n_light = g.gnn_plan_export(pl)["n_light"]
+    say(f"  light rows {n_light}, empty rows {int(empty.sum())}")
+    rng = np.random.default_rng(5)
+    Q, K, V = rand_feats(rng, n, H, D, dtype)
+    q, k, v = (dev_feat(x, dtype) for x in (Q, K, V))
+    O, L = g.gnn_attn_fwd(pl, ip, ix, q, k, v)
+    ref = oracle.gt_fwd(rp, rx, Q, K, V)
+    _check("O", host(O), ref["O"], ref["SO"], dtype)
+    _check("LSE", host(L), ref["LSE"], ref["SL"], "f32")
+    assert np.all(host(O)[empty] == 0) and np.all(np.isneginf(host(L)[empty]))
+    att = (rng.standard_normal((H, D)) / np.sqrt(D)).astype(np.float32)
+    Og, Lg = g.gatv2_attn_fwd(pl, ip, ix, q, k, torch.from_numpy(att).cuda())
+    rg = oracle.gatv2_fwd(rp, rx, Q, K, att)
+    _check("GATv2 O", host(Og), rg["O"], rg["SO"], dtype)
+    _check("GATv2 LSE", host(Lg), rg["LSE"], rg["SL"], "f32")
+
+
 @pytest.mark.parametrize("dtype,D,H", [("f32", 16, 8), ("f32", 32, 2), ("bf16", 16, 8), ("bf16", 64, 4),
                                        ("f32", 128, 1)])
 @pytest.mark.parametrize("plan", ["none", "heavy", "mixed"])
