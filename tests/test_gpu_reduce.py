@@ -76,8 +76,8 @@ def _plan(g, ip_d, ix_d, kind, csc=False):
     return g.gnn_plan_create(ip_d, ix_d, want_csc=csc)
 
 
-CASES = [("f32", 4), ("f32", 32), ("f32", 128), ("f32", 256), ("f32", 320), ("bf16", 8), ("bf16", 64),
-         ("bf16", 128), ("bf16", 1032)]
+CASES = [("f32", 4), ("f32", 32), ("f32", 96), ("f32", 128), ("f32", 256), ("f32", 320), ("bf16", 8), ("bf16", 64),
+         ("bf16", 128), ("bf16", 200), ("bf16", 1032)]
 
 
 @pytest.mark.parametrize("dtype,F", CASES)
