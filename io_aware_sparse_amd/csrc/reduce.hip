@@ -15,7 +15,9 @@
 // Lane geometry: a lane holds one 16-byte slice of a feature row (4 fp32 or
 // 8 bf16). A row of L = F*s/16 slices takes LR = next_pow2(L) lanes when
 // L <= 64 (64/LR edge groups per wave), else whole waves over NFG = ceil(L/64)
-// feature groups. Light rows: one wave per (row, feature group), the best
+// feature groups. Light rows: one wave per (row, feature group), or on a
+// plan with sorted rows 4 or 2 rows per wave for rows of at most 256 or 512
+// bytes (see run_red_fwd), the best
 // (value, source) pair of each feature kept in registers, edge groups merged
 // by a xor tree with the same ordering rule. Heavy rows: the plan's chunk
 // groups (C edges per wave, W waves); each wave reduces its chunk and merges
