@@ -732,6 +732,7 @@ def bench(args) -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
             "traffic": traffic,
+            "traffic_GBps": round(traffic / (dk["avg_us"] * 1e-6) / 1e9, 1) if traffic and dk["avg_us"] else None,
             "traffic_source": f"profiles/{dom}__{tag}__counters.txt" if traffic is not None else None,
             "alg_bytes_per_launch": dk["alg_bytes"],
             "avg_launch_us": dk["avg_us"],
