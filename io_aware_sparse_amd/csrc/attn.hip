@@ -73,7 +73,11 @@ __global__ __launch_bounds__(512) void k_fwd_main(FwdParams P) {
         }
         return;
     }
-    const int64_t item = (int64_t)(blockIdx.x - heavy_blocks) * P.W + w;
+    // the packed rows come from the descending-degree list, which has no id
+    // locality for an XCD-aware order to keep; one-row waves follow the plan's
+    // launch order, mostly id order, and take the XCD-aware block order
+    const int64_t lblock = blockIdx.x - heavy_blocks;
+    const int64_t item = (RPW > 1 ? lblock : xcd_block(lblock, gridDim.x - heavy_blocks)) * P.W + w;
     if (RPW > 1) {                        // RPW rows of the light list per wave (NHG == 1)
         const int64_t ni0 = item * RPW;
         if (ni0 >= P.n_light) return;
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(512) void k_bwd_dst_main(BwdParams P) {
         if (lp.dv == 0) slot[2 * rowlen + lp.h] = x[2][0];
         return;
     }
-    const int64_t item = (int64_t)(blockIdx.x - heavy_blocks) * P.W + w;
+    const int64_t item = xcd_block(blockIdx.x - heavy_blocks, gridDim.x - heavy_blocks) * P.W + w;
     const int64_t ni = item / P.g.NHG;
     if (ni >= P.a_n_light) return;
     const int hg = (int)(item % P.g.NHG);
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(512) void k_bwd_src_main(BwdParams P) {
         }
         return;
     }
-    const int64_t item = (int64_t)(blockIdx.x - heavy_blocks) * P.W + w;
+    const int64_t item = xcd_block(blockIdx.x - heavy_blocks, gridDim.x - heavy_blocks) * P.W + w;
     const int64_t ni = item / P.g.NHG;
     if (ni >= P.b_n_light) return;
     const int hg = (int)(item % P.g.NHG);

@@ -37,6 +37,22 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// XCD-aware order of a kernel's row blocks. Workgroups go to the 8 XCDs (each
+// with its own L2) round-robin by block id, so consecutive blocks land on
+// different L2s. Physical block p (of nb) runs logical block
+// ((s / K) * 8 + p % 8) * K + s % K with s = p / 8: each XCD takes runs of
+// K = 4 consecutive logical blocks (16 consecutive rows at 4 waves per block),
+// so rows that share sources (a community) share one L2, while the runs of
+// an XCD stay spread over the whole launch order. Blocks past the last full
+// group of 8 K keep their own index; the map is a bijection on [0, nb).
+__device__ __forceinline__ int64_t xcd_block(int64_t p, int64_t nb) {
+    constexpr int64_t kX = 8, kK = 4;
+    const int64_t full = nb / (kX * kK) * (kX * kK);
+    if (p >= full) return p;
+    const int64_t s = p / kX;
+    return ((s / kK) * kX + p % kX) * kK + s % kK;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
