@@ -99,7 +99,9 @@ __device__ __forceinline__ void merge_groups(SoftState<NV> &st, int lr_shift) {
 // Stream edges [e0, e1) of `node` for this lane's head group; returns the
 // wave-merged online-softmax state (valid in every lane). With reset false
 // the caller's state is continued (only edge group 0 may carry a non-empty
-// state, the other groups must start empty).
+// state, the other groups must start empty). With RPW > 1 each row group of
+// the wave streams its own node and range (lane_pos<..., RPW>) and the merge
+// stays inside the row group; the wave steps until every row is done.
 template <class T, int LH, int MODE, int U, int RPW = 1>
 __device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp, int node, int e0, int e1,
                                            SoftState<Vec<T>::N> &st, bool reset = true) {
