@@ -53,13 +53,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines, so that a comment edit
+    does not mark a counter summary as stale."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(kernel: str = "") -> str:
-    """Hash of the sources of `kernel`'s family (reduce_*, spmm_*, else attention)."""
+    """Hash of the code (comments stripped) of `kernel`'s family's sources
+    (reduce_*, spmm_*, else attention)."""
     h = hashlib.sha256()
     for f in (REDUCE_SOURCES if kernel.startswith("reduce_") else SPMM_SOURCES if kernel.startswith("spmm_")
               else KERNEL_SOURCES):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -117,3 +117,11 @@ def test_kernel_stats_summary_sorts_by_total_time(tmp_path):
     rows = [line.split() for line in out.read_text().splitlines() if line.strip().endswith(("big", "small"))]
     assert [r[-1] for r in rows] == ["big", "small"]
     assert float(rows[0][1]) == 6.0 and float(rows[1][1]) == 1.0      # average in microseconds
+
+
+def test_source_hash_ignores_comments():
+    code = "int f(int x) {\n    return x + 1;   // add one\n}\n"
+    commented = "/* a block\n   comment */\n// header\nint f(int x) {\n    return x + 1;   // plus one\n\n}\n"
+    changed = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench._code_only(code) == bench._code_only(commented)
+    assert bench._code_only(code) != bench._code_only(changed)
