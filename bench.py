@@ -766,24 +766,6 @@ def bench(args) -> int:
     return 0
 
 
-def bw_probe(args) -> int:
-    """Run the bandwidth-reference executable (streaming read, copy, random
-    row gathers) and record its output with the command that made it."""
-    import subprocess
-    exe = os.path.join(ROOT, "io_aware_sparse_amd", "bw_probe")
-    if not os.path.exists(exe):
-        raise SystemExit("io_aware_sparse_amd/bw_probe is not built (python -m io_aware_sparse_amd.build)")
-    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
-    text = ("# achievable bandwidth on one GPU (hipEvent timing, 5 launches per line)\n"
-            "# command: python3 bench.py --bw-probe  (runs io_aware_sparse_amd/bw_probe, "
-            "source io_aware_sparse_amd/csrc/bw_probe.hip)\n" + r.stdout)
-    if args.out:
-        with open(args.out, "w") as f:
-            f.write(text)
-    print(text, end="")
-    return r.returncode
-
-
 def copy_probe(args) -> int:
     import torch
     nbytes = args.copy_mib << 20
@@ -829,8 +811,6 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=1024)
-    ap.add_argument("--bw-probe", action="store_true",
-                    help="run the achievable-bandwidth reference (read, copy, random row gathers)")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--out", help="summary output file")
@@ -848,8 +828,6 @@ def main():
         return units_summary(args)
     if args.copy_probe:
         return copy_probe(args)
-    if args.bw_probe:
-        return bw_probe(args)
     return bench(args)
 
 
