@@ -313,6 +313,52 @@ def gatv2_fwd(indptr, indices, XD, XS, att, V=None, slope: float = 0.2, rows=Non
     return dict(O=O, LSE=LSE, SO=SO, SL=SL)
 
 
+def gt_bwd_dst(indptr, indices, Q, K, V, dO, scale: Optional[float] = None, rows=None):
+    """Destination side of the Graph-Transformer backward in fp64, from the
+    definition, for the rows `rows` (None = all): dQ, Delta (from the
+    weights), the scale SdQ, and the row statistics M (max logit) and Z (sum
+    of exp(s - M)) that the source side needs. Returns a dict of those."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    N, H, D = Q.shape
+    ip, ix = _graph(indptr, indices)
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    r, nr = _rows(rows, N)
+    dQ = np.empty((nr, H, D)); Dl = np.empty((nr, H)); M = np.empty((nr, H)); Z = np.empty((nr, H))
+    SdQ = np.empty((nr, H, D))
+    rc = _load().orc_gt_bwd_rows(N, _p(ip), _p(ix), H, D, _p(Q), _p(K), _p(V), _p(dO), sc, nr, _p(r),
+                                 _p(dQ), _p(Dl), _p(M), _p(Z), _p(SdQ))
+    if rc:
+        raise MemoryError("oracle row buffer")
+    return dict(dQ=dQ, Delta=Dl, SdQ=SdQ, M=M, Z=Z)
+
+
+def gt_bwd_src(cindptr, cindices, Q, K, V, dO, M, Z, Delta, scale: Optional[float] = None, srcs=None,
+               need=None):
+    """Source side of the Graph-Transformer backward in fp64 over the
+    transposed adjacency (cindptr/cindices list each source's destinations):
+    dK, dV and their scales SdK, SdV for the sources `srcs` (None = all).
+    M, Z, Delta are the destination statistics of gt_bwd_dst, for every row
+    (need None) or for the rows listed in `need` (in that order)."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    N, H, D = Q.shape
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    cip = np.ascontiguousarray(cindptr, np.int64)
+    cix = np.ascontiguousarray(cindices, np.int32)
+    s, ns = _rows(srcs, N)
+    if need is None:
+        slot = np.arange(N, dtype=np.int64)
+    else:
+        slot = np.full(N, -1, np.int64)
+        slot[np.asarray(need, np.int64)] = np.arange(len(need))
+    M, Z, Dl = (np.ascontiguousarray(a, np.float64) for a in (M, Z, Delta))
+    dK = np.empty((ns, H, D)); dV = np.empty((ns, H, D)); SdK = np.empty((ns, H, D)); SdV = np.empty((ns, H, D))
+    rc = _load().orc_gt_bwd_srcs(N, _p(cip), _p(cix), H, D, _p(Q), _p(K), _p(V), _p(dO), sc, _p(slot),
+                                 _p(M), _p(Z), _p(Dl), ns, _p(s), _p(dK), _p(dV), _p(SdK), _p(SdV))
+    if rc:
+        raise RuntimeError("oracle source pass: missing destination statistics")
+    return dict(dK=dK, dV=dV, SdK=SdK, SdV=SdV)
+
+
 def gt_bwd(indptr, indices, Q, K, V, dO, scale: Optional[float] = None, rows=None, srcs=None,
            csc_arrays=None, want_src: bool = True):
     """Graph-Transformer backward in fp64, from the definition.
@@ -323,48 +369,27 @@ def gt_bwd(indptr, indices, Q, K, V, dO, scale: Optional[float] = None, rows=Non
     rows it touches. Returns dict dQ, Delta, SdQ [rows] and dK, dV, SdK, SdV
     [srcs]."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
-    N, H, D = Q.shape
+    N = Q.shape[0]
     ip, ix = _graph(indptr, indices)
-    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
-    lib = _load()
-    out = {}
-    r, nr = _rows(rows, N)
-    dQ = np.empty((nr, H, D)); Dl = np.empty((nr, H)); M = np.empty((nr, H)); Z = np.empty((nr, H))
-    SdQ = np.empty((nr, H, D))
-    rc = lib.orc_gt_bwd_rows(N, _p(ip), _p(ix), H, D, _p(Q), _p(K), _p(V), _p(dO), sc, nr, _p(r),
-                             _p(dQ), _p(Dl), _p(M), _p(Z), _p(SdQ))
-    if rc:
-        raise MemoryError("oracle row buffer")
-    out.update(dQ=dQ, Delta=Dl, SdQ=SdQ)
+    d = gt_bwd_dst(ip, ix, Q, K, V, dO, scale, rows)
+    out = dict(dQ=d["dQ"], Delta=d["Delta"], SdQ=d["SdQ"])
     if not want_src:
         return out
     cip, cix = csc(ip, ix, N) if csc_arrays is None else csc_arrays
     cip = np.ascontiguousarray(cip, np.int64)
     cix = np.ascontiguousarray(cix, np.int32)
-    s, ns = _rows(srcs, N)
-    # destination rows touched by the listed sources
-    if s is None:
-        need = np.arange(N, dtype=np.int64)
+    s, _ = _rows(srcs, N)
+    if rows is None:
+        stats, need = d, None
     else:
-        parts = [cix[cip[j]:cip[j + 1]] for j in s]
-        need = np.unique(np.concatenate(parts).astype(np.int64)) if parts else np.zeros(0, np.int64)
-    if r is None and s is None:
-        M2, Z2, D2 = M, Z, Dl
-    else:
-        n2 = need.size
-        tmp_dq = np.empty((n2, H, D)); D2 = np.empty((n2, H)); M2 = np.empty((n2, H)); Z2 = np.empty((n2, H))
-        rc = lib.orc_gt_bwd_rows(N, _p(ip), _p(ix), H, D, _p(Q), _p(K), _p(V), _p(dO), sc, n2, _p(need),
-                                 _p(tmp_dq), _p(D2), _p(M2), _p(Z2), None)
-        if rc:
-            raise MemoryError("oracle row buffer")
-    slot = np.full(N, -1, np.int64)
-    slot[need] = np.arange(need.size)
-    dK = np.empty((ns, H, D)); dV = np.empty((ns, H, D)); SdK = np.empty((ns, H, D)); SdV = np.empty((ns, H, D))
-    rc = lib.orc_gt_bwd_srcs(N, _p(cip), _p(cix), H, D, _p(Q), _p(K), _p(V), _p(dO), sc, _p(slot),
-                             _p(M2), _p(Z2), _p(D2), ns, _p(s), _p(dK), _p(dV), _p(SdK), _p(SdV))
-    if rc:
-        raise RuntimeError("oracle source pass: missing destination statistics")
-    out.update(dK=dK, dV=dV, SdK=SdK, SdV=SdV)
+        # destination rows touched by the listed sources
+        if s is None:
+            need = np.arange(N, dtype=np.int64)
+        else:
+            parts = [cix[cip[j]:cip[j + 1]] for j in s]
+            need = np.unique(np.concatenate(parts).astype(np.int64)) if parts else np.zeros(0, np.int64)
+        stats = gt_bwd_dst(ip, ix, Q, K, V, dO, scale, need)
+    out.update(gt_bwd_src(cip, cix, Q, K, V, dO, stats["M"], stats["Z"], stats["Delta"], scale, s, need))
     return out
 
 
@@ -637,18 +662,36 @@ def round_bf16(x) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def scaled_error(x, ref, scale) -> float:
-    """max_e |x_e - r_e| / max(|r_e|, S_e), S_e the oracle's summation scale.
-
-    Entries where both are -inf (empty rows' LSE) count as exact."""
+def normwise_error(x, ref) -> float:
+    """Plain normwise relative error max_e |x_e - r_e| / max_e |r_e| over
+    the finite entries of ref (reported beside the scaled error; 0 when ref
+    has no non-zero finite entry and x equals it there)."""
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)
-    s = np.maximum(np.abs(ref), np.asarray(scale, np.float64))
-    both_inf = np.isinf(x) & np.isinf(ref) & (np.sign(x) == np.sign(ref))
-    with np.errstate(invalid="ignore"):
-        diff = np.where(both_inf, 0.0, np.abs(x - ref))
-    den = np.where(both_inf, 1.0, np.where(s > 0, s, 1.0))
-    e = diff / den
-    if e.size == 0:
+    fin = np.isfinite(ref)
+    if not np.any(fin):
         return 0.0
+    num = float(np.max(np.abs(x[fin] - ref[fin])))
+    den = float(np.max(np.abs(ref[fin])))
+    return num / den if den > 0 else (0.0 if num == 0 else float("inf"))
+
+
+def scaled_error(x, ref, scale) -> float:
+    """max_e |x_e - r_e| / max(|r_e|, S_e), S_e the oracle's summation scale
+    (where both |r_e| and S_e are 0 the absolute difference is taken).
+
+    Entries where both are infinite with the same sign (empty rows' LSE)
+    count as exact; an infinity on one side only, infinities of opposite
+    signs and NaN on either side give an infinite error."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    s = np.maximum(np.abs(ref), np.asarray(scale, np.float64))
+    same_inf = np.isinf(x) & np.isinf(ref) & (np.sign(x) == np.sign(ref))
+    bad = ~same_inf & ~(np.isfinite(x) & np.isfinite(ref) & np.isfinite(s))
+    ok = ~(same_inf | bad)
+    diff = np.where(ok, np.abs(np.where(ok, x, 0.0) - np.where(ok, ref, 0.0)), 0.0)
+    den = np.where(ok & (s > 0), s, 1.0)
+    e = np.where(bad, np.inf, diff / den)
     return float(np.max(e))

@@ -15,6 +15,18 @@ def say(*a):
     sys.stdout.flush()
 
 
+def check(name, x, ref, scale, dtype, extra=""):
+    """Assert the condition-scaled error of x against the oracle's ref is
+    within the tolerance of dtype; print it with the plain normwise error
+    max|x - r| / max|r| beside it. Returns the scaled error."""
+    import oracle
+    err = oracle.scaled_error(x, ref, scale)
+    nw = oracle.normwise_error(x, ref)
+    say(f"  {name}: scaled err {err:.3e}, normwise {nw:.3e}{extra} (tol {TOL[dtype]:.0e})")
+    assert err <= TOL[dtype], (name, err)
+    return err
+
+
 def torch():
     import torch as t
     return t

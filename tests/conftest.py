@@ -18,3 +18,18 @@ def orc():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture
+def live(pytestconfig):
+    """print() that bypasses pytest's output capture, for progress lines of
+    long tests (each line is flushed as it is written)."""
+    cm = pytestconfig.pluginmanager.getplugin("capturemanager")
+
+    def out(*a):
+        if cm is None:
+            print(*a, flush=True)
+            return
+        with cm.global_and_fixture_disabled():
+            print(*a, flush=True)
+    return out

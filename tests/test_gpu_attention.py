@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads
-from _gpu import TOL, dev_feat, dev_i32, host, rand_feats, say
+from _gpu import TOL, check, dev_feat, dev_i32, host, rand_feats, say
 
 pytestmark = pytest.mark.gpu
 
@@ -52,9 +52,7 @@ def _plan(g, ip, ix, name, want_csc=False):
 
 
 def _check(name, x, ref, scale, dtype):
-    err = oracle.scaled_error(x, ref, scale)
-    say(f"  {name}: scaled err {err:.3e} (tol {TOL[dtype]:.0e})")
-    assert err <= TOL[dtype], (name, err)
+    check(name, x, ref, scale, dtype)
 
 
 CASES = [("f32", 16, 1), ("f32", 32, 4), ("f32", 64, 2), ("f32", 128, 3), ("f32", 16, 8),

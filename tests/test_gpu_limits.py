@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from _gpu import TOL, dev_feat, dev_i32, host, rand_feats, say
+from _gpu import TOL, check, dev_feat, dev_i32, host, rand_feats, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -35,9 +35,7 @@ def _hub_graph(m):
 
 
 def _check(name, x, ref, scale, dtype):
-    err = oracle.scaled_error(x, ref, scale)
-    say(f"  {name}: scaled err {err:.3e} over {np.asarray(ref).shape[0]} rows (tol {TOL[dtype]:.0e})")
-    assert err <= TOL[dtype], (name, err)
+    check(name, x, ref, scale, dtype, f" over {np.asarray(ref).shape[0]} rows")
 
 
 def _setup(g, m, seed):

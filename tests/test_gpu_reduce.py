@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from _gpu import TOL, dev_feat, dev_i32, host, say
+from _gpu import TOL, check, dev_feat, dev_i32, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -173,9 +173,7 @@ def test_reduce_bwd(g, dtype, F, plan_kind):
             dX = g.gnn_reduce_bwd(plan, ip_d, ix_d, gd, arg, msg)
             ra = oracle.segment_reduce(ip, ix, X, op, msg)["arg"]
             ref, S = oracle.segment_reduce_bwd(ip, ix, dOut, ra, msg, want_scale=True)
-            err = oracle.scaled_error(host(dX), ref, S)
-            say(f"  {op} {msg}: scaled err {err:.2e}")
-            assert err <= TOL[dtype], (op, msg, err)
+            check(f"{op} {msg} dX", host(dX), ref, S, dtype)
             dX2 = g.gnn_reduce_bwd(plan, ip_d, ix_d, gd, arg, msg)
             assert np.array_equal(host(dX2), host(dX)), "not reproducible"
 

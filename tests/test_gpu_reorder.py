@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads
-from _gpu import TOL, dev_feat, dev_i32, host, say
+from _gpu import TOL, check, dev_feat, dev_i32, host, say
 from _helpers import read_golden
 
 pytestmark = pytest.mark.gpu
@@ -112,9 +112,7 @@ def test_attention_on_relabelled_graph(g, method):
     O, L = g.gnn_attn_fwd(plan, nip, nix, qp, kp, vp)
     Ob = g.gnn_permute_rows(O, perm, back=True)
     ref = oracle.gt_fwd(ip, ix, wl.feats["Q"], wl.feats["K"], wl.feats["V"])
-    err = oracle.scaled_error(host(Ob), ref["O"], ref["SO"])
-    say(f"  {method}: relabelled GT forward, scaled err {err:.2e}")
-    assert err <= TOL["f32"]
+    check(f"{method}: relabelled GT forward O", host(Ob), ref["O"], ref["SO"], "f32")
 
 
 @pytest.mark.slow

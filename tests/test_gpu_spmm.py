@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from _gpu import TOL, dev_feat, dev_i32, host, say
+from _gpu import TOL, check, dev_feat, dev_i32, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -81,9 +81,7 @@ def test_spmm_parity(g, dtype, F, plan_kind):
         for tr in (False, True):
             Y = g.gnn_spmm(plan, ip_d, ix_d, Xd, transpose=tr)
             ref = oracle.spmm(ip, ix, X, norm, transpose=tr)
-            err = oracle.scaled_error(host(Y), ref["Y"], ref["S"])
-            say(f"spmm {dtype} F={F} {plan_kind} {norm} transpose={tr}: scaled err {err:.2e}")
-            assert err <= TOL[dtype], (norm, tr, err)
+            check(f"spmm {dtype} F={F} {plan_kind} {norm} transpose={tr}", host(Y), ref["Y"], ref["S"], dtype)
             Y2 = g.gnn_spmm(plan, ip_d, ix_d, Xd, transpose=tr)
             assert np.array_equal(host(Y2), host(Y)), "not reproducible"
 

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import workloads
-from _gpu import TOL, dev_feat, dev_i32, host, rand_feats, say
+from _gpu import TOL, check, dev_feat, dev_i32, host, rand_feats, say
 
 pytestmark = pytest.mark.gpu
 
@@ -46,9 +46,7 @@ def _graph(g, kind):
 
 
 def _check(name, x, ref, scale, dtype):
-    err = oracle.scaled_error(x, ref, scale)
-    say(f"  {name}: scaled err {err:.3e} (tol {TOL[dtype]:.0e})")
-    assert err <= TOL[dtype], (name, err)
+    check(name, x, ref, scale, dtype)
 
 
 CASES = [(64, 8), (32, 16), (32, 4), (128, 2), (128, 5), (64, 3), (64, 1)]
