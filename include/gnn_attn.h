@@ -65,7 +65,8 @@ typedef enum {
     GNN_ERR_ALIGNMENT = -3,    /* feature pointer not 16-byte aligned                 */
     GNN_ERR_OOM = -4,          /* device allocation failed                            */
     GNN_ERR_HIP = -5,          /* a HIP runtime call failed (see gnn_status_string)   */
-    GNN_ERR_BAD_GRAPH = -6     /* indptr/indices inconsistent or out of range         */
+    GNN_ERR_BAD_GRAPH = -6,    /* indptr/indices inconsistent or out of range         */
+    GNN_ERR_SCRATCH = -7       /* gnn_attn_fwd_noalloc: problem exceeds its fixed scratch */
 } gnn_status_t;
 
 typedef struct gnn_plan_s *gnn_plan_t;   /* opaque; owns its device arrays */
@@ -194,6 +195,33 @@ int gnn_plan_destroy(gnn_plan_t plan);
 int gnn_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
                  int32_t H, int32_t D, const void *Q, const void *K, const void *V, void *O,
                  float *LSE /*nullable*/, float scale, gnn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Graph-Transformer attention forward that allocates no device memory, for
+ * callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, operation and
+ * results as gnn_attn_fwd (bitwise identical outputs for the same inputs and
+ * plan); the caller passes O (and LSE, nullable) already allocated.
+ *   Scratch: the heavy rows' partial states go to a fixed device buffer of
+ *   GNN_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on each GPU it
+ *   runs on until the process ends, instead of the plan workspace, which this
+ *   call never grows. A call needs n_groups * (H*D + 2*H) * 4 bytes of it
+ *   (n_groups: the plan's heavy chunk groups; 0 without a plan, without heavy
+ *   rows, or on the tile path's tiled rows); a larger need returns
+ *   GNN_ERR_SCRATCH before anything is launched.
+ *   Sharing: every call on one GPU uses that GPU's buffer, which keeps the
+ *   last call's contents. Calls that overlap in time on one GPU (two streams,
+ *   or two host threads) race and give undefined results: serialise them.
+ *   Nothing in the buffer needs to start at zero (every partial a call reads
+ *   is written earlier in the same call).
+ *   Per-kernel timing must be off on the plan (GNN_ERR_UNSUPPORTED otherwise).
+ *   The first call on a device looks up the buffer's device address with the
+ *   device current (hipGetSymbolAddress); later calls make no such lookup.
+ */
+#define GNN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int gnn_attn_fwd_noalloc(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
+                         int32_t H, int32_t D, const void *Q, const void *K, const void *V, void *O,
+                         float *LSE /*nullable*/, float scale, gnn_dtype_t dtype, hipStream_t stream);
 
 /*
  * Graph-Transformer attention backward from the cached LSE (the forward's

@@ -9,7 +9,7 @@ pointers and torch's current HIP stream, and turns a non-zero status into
 fallback path, and calls fail loudly when the library is missing.
 
 Function names match the C ABI: gnn_csr_build, gnn_plan_create,
-gnn_plan_export, gnn_plan_destroy, gnn_attn_fwd, gnn_attn_bwd,
+gnn_plan_export, gnn_plan_destroy, gnn_attn_fwd, gnn_attn_fwd_noalloc, gnn_attn_bwd,
 gatv2_attn_fwd, gatv2_attn_bwd, gnn_plan_set_timing, gnn_plan_timing_read,
 gnn_status_string.
 """
@@ -25,11 +25,11 @@ LIB_PATH = os.path.join(_PKG, "libgnn_attn.so")
 GNN_F32, GNN_BF16 = 0, 1
 GNN_OK = 0
 STATUS = {0: "GNN_OK", -1: "GNN_ERR_INVALID_ARG", -2: "GNN_ERR_UNSUPPORTED", -3: "GNN_ERR_ALIGNMENT",
-          -4: "GNN_ERR_OOM", -5: "GNN_ERR_HIP", -6: "GNN_ERR_BAD_GRAPH"}
+          -4: "GNN_ERR_OOM", -5: "GNN_ERR_HIP", -6: "GNN_ERR_BAD_GRAPH", -7: "GNN_ERR_SCRATCH"}
 
 # exported symbols, in the order include/gnn_attn.h declares them
 EXPORTS = ["gnn_plan_opts_default", "gnn_csr_build", "gnn_plan_create", "gnn_plan_export", "gnn_plan_destroy",
-           "gnn_attn_fwd", "gnn_attn_bwd", "gatv2_attn_fwd", "gatv2_attn_bwd", "gnn_plan_set_timing",
+           "gnn_attn_fwd", "gnn_attn_fwd_noalloc", "gnn_attn_bwd", "gatv2_attn_fwd", "gatv2_attn_bwd", "gnn_plan_set_timing",
            "gnn_plan_timing_read", "gnn_status_string", "gnn_reduce_fwd", "gnn_reduce_bwd", "gnn_reorder",
            "gnn_permute_graph", "gnn_permute_rows", "gnn_spmm_prepare", "gnn_spmm"]
 ORDERS = {"degree": 0, "rcm": 1}      # gnn_order_t
@@ -96,6 +96,7 @@ def lib():
         L.gnn_plan_export.argtypes = [V, C.POINTER(PlanInfo)]
         L.gnn_plan_destroy.argtypes = [V]
         L.gnn_attn_fwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, V, F, C.c_int, V]
+        L.gnn_attn_fwd_noalloc.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, V, F, C.c_int, V]
         L.gnn_attn_bwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, V, V, V, V, V, F, C.c_int, V]
         L.gatv2_attn_fwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, F, V, V, C.c_int, V]
         L.gatv2_attn_bwd.argtypes = [V, V, V, I32, I64, I32, I32, V, V, V, V, F, V, V, V, V, V, V, C.c_int, V]
@@ -314,6 +315,29 @@ def gnn_attn_fwd(plan: Optional[Plan], indptr, indices, Q, K, V, O=None, LSE=Non
     _check(lib().gnn_attn_fwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
                               _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), float(scale), _dtype_code(Q),
                               _stream(stream)), "gnn_attn_fwd")
+    return O, LSE
+
+
+def gnn_attn_fwd_noalloc(plan: Optional[Plan], indptr, indices, Q, K, V, O, LSE=None, scale: float = 0.0,
+                         stream=None):
+    """Graph-Transformer attention forward through the entry point that
+    allocates no device memory: O (and LSE, optional) must be given, and
+    nothing is allocated here either. Returns (O, LSE)."""
+    n, e = _graph(indptr, indices)
+    _feat(Q, "Q")
+    N, H, D = Q.shape
+    if N != n:
+        raise ValueError("Q rows differ from the graph's node count")
+    _feat(K, "K", Q.shape, Q.dtype)
+    _feat(V, "V", Q.shape, Q.dtype)
+    _feat(O, "O", Q.shape, Q.dtype)
+    if LSE is not None:
+        torch = _torch()
+        if not (LSE.is_cuda and LSE.dtype == torch.float32 and LSE.is_contiguous() and tuple(LSE.shape) == (N, H)):
+            raise TypeError("LSE must be a contiguous float32 [N, H] device tensor")
+    _check(lib().gnn_attn_fwd_noalloc(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
+                                      _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), float(scale), _dtype_code(Q),
+                                      _stream(stream)), "gnn_attn_fwd_noalloc")
     return O, LSE
 
 

@@ -25,6 +25,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "attn_core.h"
 
@@ -350,9 +351,12 @@ static int dispatch_fwd(gnn_plan_t plan, FwdParams &P, const int32_t *by_degree,
     return GNN_ERR_UNSUPPORTED;
 }
 
+// fixed_ws: when non-null, the heavy partials go there (at most fixed_bytes)
+// instead of the plan workspace, and nothing is allocated.
 static int fwd_common(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
                       int32_t H, int32_t D, const void *Q, const void *K, const void *V, void *O, float *LSE,
-                      const float *att, float slope, float mul, int mode, gnn_dtype_t dtype, hipStream_t s) {
+                      const float *att, float slope, float mul, int mode, gnn_dtype_t dtype, hipStream_t s,
+                      float *fixed_ws = nullptr, size_t fixed_bytes = 0) {
     GNN_TRY(check_common(plan, indptr, indices, N, E, H, D, dtype));
     if (N > 0 && (!Q || !K || !V || !O)) return GNN_ERR_INVALID_ARG;
     if (mode != M_GT && N > 0 && !att) return GNN_ERR_INVALID_ARG;
@@ -384,8 +388,13 @@ static int fwd_common(gnn_plan_t plan, const int32_t *indptr, const int32_t *ind
         P.W = plan->opts.waves_per_group;
         if (P.n_groups) {
             const size_t rowlen = (size_t)H * D;
-            void *ws = nullptr;
-            GNN_TRY(plan_workspace(plan, (size_t)P.n_groups * (rowlen + 2 * H) * sizeof(float), s, &ws));
+            const size_t bytes = (size_t)P.n_groups * (rowlen + 2 * H) * sizeof(float);
+            void *ws = fixed_ws;
+            if (fixed_ws) {
+                if (bytes > fixed_bytes) return GNN_ERR_SCRATCH;
+            } else {
+                GNN_TRY(plan_workspace(plan, bytes, s, &ws));
+            }
             P.ws_acc = (float *)ws;
             P.ws_ml = P.ws_acc + (size_t)P.n_groups * rowlen;
         }
@@ -442,6 +451,36 @@ static int run_bwd(gnn_plan_t plan, BwdParams &P, hipStream_t s, bool tiles) {
     return GNN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free forward. The heavy rows' partial states live in this
+// file-scope device array instead of the plan workspace. In host code the
+// name `scratch` is only a host-side stand-in for the symbol: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is passed to kernels. Every call on a GPU
+// shares that GPU's copy.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[GNN_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static float *g_scratch_dev[kMaxDevices] = {};
+
+// device address of the current device's copy of `scratch`
+static int scratch_on_current_device(float **out) {
+    int dev = 0;
+    GNN_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return GNN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        GNN_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return GNN_ERR_HIP;
+        g_scratch_dev[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return GNN_OK;
+}
+
 }  // namespace gnn
 
 using namespace gnn;
@@ -454,6 +493,22 @@ int gnn_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices,
     const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)std::max(D, 1)));
     return fwd_common(plan, indptr, indices, N, E, H, D, Q, K, V, O, LSE, nullptr, 0.f, sc * kLog2e, M_GT, dtype,
                       stream);
+}
+
+int gnn_attn_fwd_noalloc(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
+                         int32_t H, int32_t D, const void *Q, const void *K, const void *V, void *O, float *LSE,
+                         float scale, gnn_dtype_t dtype, hipStream_t stream) {
+    // argument checks first, so that a rejected call never touches the device
+    GNN_TRY(check_common(plan, indptr, indices, N, E, H, D, dtype));
+    if (N > 0 && (!Q || !K || !V || !O)) return GNN_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return GNN_ERR_ALIGNMENT;
+    if (plan && plan->timer.enabled) return GNN_ERR_UNSUPPORTED;   // event records are not allocation-free
+    if (N == 0) return GNN_OK;
+    float *buf = nullptr;
+    GNN_TRY(scratch_on_current_device(&buf));
+    const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)std::max(D, 1)));
+    return fwd_common(plan, indptr, indices, N, E, H, D, Q, K, V, O, LSE, nullptr, 0.f, sc * kLog2e, M_GT, dtype,
+                      stream, buf, GNN_NOALLOC_SCRATCH_BYTES);
 }
 
 int gatv2_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,

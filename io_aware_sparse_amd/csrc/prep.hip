@@ -679,6 +679,8 @@ const char *gnn_status_string(int status) {
         case GNN_ERR_OOM: return g_hip_msg[0] ? g_hip_msg : "device allocation failed";
         case GNN_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP runtime error";
         case GNN_ERR_BAD_GRAPH: return "graph arrays inconsistent or out of range";
+        case GNN_ERR_SCRATCH:
+            return "the call needs more scratch than the allocation-free entry point's fixed buffer holds";
         default: return "unknown status";
     }
 }

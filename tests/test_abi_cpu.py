@@ -43,9 +43,10 @@ def test_exports_every_declared_function(g):
 
 
 def test_status_strings(g):
-    for code in (0, -1, -2, -3, -4, -5, -6, 99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 99):
         assert isinstance(g.gnn_status_string(code), str)
     assert g.gnn_status_string(-3).startswith("feature pointer")
+    assert "allocation-free" in g.gnn_status_string(-7)
 
 
 def test_host_validation(g):
@@ -62,6 +63,12 @@ def test_host_validation(g):
     assert fwd(ip=None) == -1
     assert L.gnn_attn_fwd(None, A, A, 10, 20, 2, 32, None, A, A, A, None, 0.0, 0, None) == -1
     assert L.gnn_attn_fwd(None, A, A, 0, 0, 2, 32, A, A, A, A, None, 0.0, 0, None) == 0   # empty graph: no-op
+    # the allocation-free forward validates like gnn_attn_fwd, before any HIP call
+    nfwd = lambda N=10, E=20, H=2, D=32, q=A, o=A, dt=0: L.gnn_attn_fwd_noalloc(None, A, A, N, E, H, D, q, A, A, o,
+                                                                                None, 0.0, dt, None)
+    assert nfwd(D=24) == -2 and nfwd(dt=7) == -2 and nfwd(N=-1) == -1 and nfwd(H=0) == -1
+    assert nfwd(q=None) == -1 and nfwd(o=None) == -1 and nfwd(q=A + 4) == -3 and nfwd(o=A + 8) == -3
+    assert nfwd(N=0, E=0) == 0                                                            # empty graph: no-op
     # GATv2 needs att
     assert L.gatv2_attn_fwd(None, A, A, 10, 20, 2, 32, A, A, A, None, 0.2, A, None, 0, None) == -1
     # backward needs a plan
@@ -122,3 +129,4 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(g, "_lib", None)
     with pytest.raises(RuntimeError, match="HIP library missing"):
         g.lib()
+
