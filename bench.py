@@ -181,6 +181,93 @@ def kernel_bytes(kind, c, H, D, s, v_alias=True):
     return 0
 
 
+# ------------------------------------------------------ what the rate means
+
+INFINITY_CACHE_BYTES = 256 << 20      # MI355X last-level (Infinity) cache
+# Random-gather rate (GB/s) of 64 row gathers per destination from one table,
+# by row bytes and table MiB, quoted from profiles/bw_probe__read_copy_gather.txt.
+GATHER_CEILING_GBPS = {
+    256: [(64, 8107.5), (256, 7692.6), (1024, 7245.8), (4096, 6376.6)],
+    512: [(64, 8067.2), (256, 7580.3), (1024, 7153.9), (4096, 6311.5)],
+    1024: [(64, 8073.7), (256, 7630.7), (1024, 7197.6), (4096, 6290.9)],
+}
+
+
+def gathered_tables(kind, H, D, s, N, v_alias=True):
+    """(bytes of the node tables kernel `kind` gathers rows from per edge,
+    bytes of one gathered row)."""
+    R = H * D * s
+    F4 = 4 * H * D
+    two = {"gt_fwd_main", "gt_bwd_dst_main", "gt_bwd_src_main", "gatv2_bwd_src_main", "gt_tile_fwd",
+           "gt_tile_bwd_dst", "gt_tile_bwd_src"}
+    if kind in two:
+        return 2 * R * N, R
+    if kind in ("gatv2_fwd_main", "gatv2_bwd_dst_main"):
+        return (1 if v_alias else 2) * R * N, R
+    if kind in ("reduce_fwd_main", "spmm_main", "spmm_t_main"):
+        return R * N, R
+    if kind == "reduce_bwd_main":                 # dOut rows and winner rows (int32 per feature)
+        return (R + F4) * N, R
+    return 0, R
+
+
+def gather_ceiling(table_bytes, row_bytes):
+    """Measured gather ceiling (GB/s) for a gathered working set of
+    table_bytes in rows of row_bytes: the nearest row size, interpolated in
+    log(table size) between the measured sizes and held at the ends."""
+    import math
+    rows = min(GATHER_CEILING_GBPS, key=lambda r: abs(math.log(max(row_bytes, 1) / r)))
+    pts = GATHER_CEILING_GBPS[rows]
+    mib = max(table_bytes, 1) / (1 << 20)
+    if mib <= pts[0][0]:
+        return pts[0][1]
+    if mib >= pts[-1][0]:
+        return pts[-1][1]
+    for (m0, c0), (m1, c1) in zip(pts, pts[1:]):
+        if m0 <= mib <= m1:
+            t = math.log(mib / m0) / math.log(m1 / m0)
+            return c0 + t * (c1 - c0)
+    return pts[-1][1]
+
+
+def roofline_context(kind, H, D, s, N, achieved, traffic, avg_us, v_alias=True):
+    """Fields that say what the model fraction measures for this kernel: the
+    gathered working set, whether it fits the Infinity Cache (then the rate is
+    mostly cache bandwidth and the bound is labelled "infinity-cache", else
+    "hbm"), the counter rate against the measured gather ceiling for that
+    working set, and whether the model is a bound at all (a model fraction
+    above 1 means caches served repeated rows)."""
+    tb, row = gathered_tables(kind, H, D, s, N, v_alias)
+    resident = tb <= INFINITY_CACHE_BYTES
+    ceil = gather_ceiling(tb, row)
+    out = {
+        "bound": "infinity-cache" if resident else "hbm",
+        "gathered_table_bytes": int(tb),
+        "gathered_row_bytes": int(row),
+        "cache_resident": bool(resident),
+        "gather_ceiling_GBps": round(ceil, 1),
+        "gather_ceiling_source": f"profiles/bw_probe__read_copy_gather.txt ({row}-byte rows, "
+                                 f"{tb / (1 << 20):.0f} MiB working set)",
+    }
+    frac = achieved / HBM_PEAK_GBPS if achieved else None
+    out["model_is_bound"] = bool(frac is not None and frac <= 1.0)
+    if traffic and avg_us:
+        rate = traffic / (avg_us * 1e-6) / 1e9
+        out["traffic_frac_of_gather_ceiling"] = round(rate / ceil, 4)
+    else:
+        out["traffic_frac_of_gather_ceiling"] = None
+    notes = []
+    if resident:
+        notes.append(f"the gathered tables ({tb / 1e6:.0f} MB) fit in the 256 MB Infinity Cache, so the "
+                     "gathers are served mostly from it: frac is model bytes over the 8 TB/s HBM peak, not HBM "
+                     "utilisation")
+    if frac is not None and frac > 1.0:
+        notes.append("model fraction above 1: the per-edge model is not a bound here (caches served "
+                     "repeated rows)")
+    out["note"] = "; ".join(notes) if notes else "gathered tables exceed the Infinity Cache: the gathers reach HBM"
+    return out
+
+
 # ---------------------------------------------------------------- profiles
 
 def profile_tag(workload: str, tiles: bool, extra_backward: bool, reorder: str) -> str:
@@ -695,6 +782,10 @@ def bench(args) -> int:
     tag = profile_tag(args.workload, int(info["n_tiles"]) > 0,
                       wl.backward and not workloads.SPECS[args.workload]["backward"], args.reorder)
     traffic = read_traffic(dom, tag)
+    ctx = roofline_context(dom, H, D, s, N, achieved, traffic, dk["avg_us"], v_alias=v_alias)
+    for name, k in kernels.items():
+        if k["GBps"] and k["GBps"] > HBM_PEAK_GBPS:
+            k["note"] = "above 8 TB/s: the per-edge model is not a bound (caches served repeated rows)"
     step_bytes = sum(kernel_bytes(k, counts, H, D, s, v_alias=v_alias) for k in kernels)
     rec = {
         "metric": METRIC,
@@ -736,7 +827,7 @@ def bench(args) -> int:
         "step_model_frac_of_8TBps": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {
             "kernel": dom,
-            "bound": "hbm",
+            "bound": ctx.pop("bound"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -746,6 +837,7 @@ def bench(args) -> int:
             "traffic_source": f"profiles/{dom}__{tag}__counters.txt" if traffic is not None else None,
             "alg_bytes_per_launch": dk["alg_bytes"],
             "avg_launch_us": dk["avg_us"],
+            **ctx,
         },
         "kernels": kernels,
         "kernel_source_sha256": kernel_source_hash(dom),

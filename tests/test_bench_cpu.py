@@ -125,3 +125,38 @@ def test_source_hash_ignores_comments():
     changed = "int f(int x) {\n    return x + 2;\n}\n"
     assert bench._code_only(code) == bench._code_only(commented)
     assert bench._code_only(code) != bench._code_only(changed)
+
+
+def test_gather_ceiling_follows_the_quoted_probe_lines():
+    """The ceiling table is the probe note's gather lines, and the lookup
+    interpolates between them in log(table size), held at the ends."""
+    import re
+    quoted = {}
+    with open(os.path.join(ROOT, "profiles", "bw_probe__read_copy_gather.txt")) as f:
+        for line in f:
+            m = re.match(r"gather (\d+)-byte rows from a (\d+) MiB table.*: ([\d.]+) GB/s", line)
+            if m:
+                quoted.setdefault(int(m.group(1)), []).append((int(m.group(2)), float(m.group(3))))
+    assert quoted == bench.GATHER_CEILING_GBPS
+    mib = 1 << 20
+    assert bench.gather_ceiling(51 * mib, 512) == 8067.2             # below the smallest table: held
+    assert bench.gather_ceiling(8192 * mib, 1024) == 6290.9          # above the largest: held
+    assert bench.gather_ceiling(256 * mib, 300) == 7692.6            # nearest row size (256 B)
+    mid = bench.gather_ceiling(512 * mib, 512)                       # halfway in log size between 256 and 1024 MiB
+    assert mid == pytest.approx((7580.3 + 7153.9) / 2)
+
+
+def test_roofline_context_labels_the_cache_state():
+    # GATv2 forward, 100k nodes, H = 8, D = 16, fp32, V = XS: one 51 MB table -> Infinity Cache
+    c = bench.roofline_context("gatv2_fwd_main", 8, 16, 4, 100_000, 7926.3, 2.527e9, 345.3)
+    assert c["bound"] == "infinity-cache" and c["cache_resident"] and c["gathered_table_bytes"] == 51_200_000
+    assert c["model_is_bound"] and c["traffic_frac_of_gather_ceiling"] == pytest.approx(
+        2.527e9 / 345.3e-6 / 1e9 / 8067.2, rel=1e-3)
+    assert "Infinity Cache" in c["note"]
+    # GT forward, 2.45M nodes, H = 4, D = 32, bf16: K and V, 627 MB each -> HBM
+    c = bench.roofline_context("gt_fwd_main", 4, 32, 2, 2_450_000, 7804.0, None, 4430.0)
+    assert c["bound"] == "hbm" and not c["cache_resident"] and c["traffic_frac_of_gather_ceiling"] is None
+    assert c["gathered_table_bytes"] == 2 * 256 * 2_450_000
+    # a model rate above the HBM peak is flagged as no bound
+    c = bench.roofline_context("gt_bwd_src_main", 8, 64, 2, 1_000_000, 10164.0, 30.34e9, 6020.0)
+    assert not c["model_is_bound"] and "not a bound" in c["note"]
