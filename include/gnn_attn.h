@@ -45,6 +45,12 @@
  *     host before any HIP call is made. No exception crosses the ABI.
  *   - A plan may be used by one stream at a time (it owns reusable
  *     workspace); different plans are independent.
+ *   - Device memory the library allocates itself (plan arrays, workspace,
+ *     temporaries) fails with GNN_ERR_OOM when hipMalloc does. Test hook:
+ *     when the environment variable GNN_ALLOC_CAP_BYTES holds a non-negative
+ *     integer, every such allocation larger than it is refused the same way
+ *     before hipMalloc is called (read at each allocation); everything the
+ *     failing call had allocated is freed, and gnn_status_string names the cap.
  */
 #ifndef GNN_ATTN_H
 #define GNN_ATTN_H

@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -30,9 +31,29 @@ void set_hip_error(hipError_t e, const char *what) {
     snprintf(g_hip_msg, sizeof(g_hip_msg), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
+// Test hook: when the environment variable GNN_ALLOC_CAP_BYTES holds a
+// non-negative integer, every device allocation of the library larger than it
+// fails as out of memory before hipMalloc is called (read at each allocation,
+// so a test may set and clear it at run time).
+static bool alloc_capped(size_t bytes, long long *cap_out) {
+    const char *s = getenv("GNN_ALLOC_CAP_BYTES");
+    if (!s || !*s) return false;
+    char *end = nullptr;
+    const long long cap = strtoll(s, &end, 10);
+    if (end == s || *end != '\0' || cap < 0) return false;
+    *cap_out = cap;
+    return (unsigned long long)bytes > (unsigned long long)cap;
+}
+
 int dev_alloc(DevBuf &b, size_t bytes) {
     dev_free(b);
     if (bytes == 0) return GNN_OK;
+    long long cap = 0;
+    if (alloc_capped(bytes, &cap)) {
+        snprintf(g_hip_msg, sizeof(g_hip_msg), "device allocation of %zu bytes refused: above GNN_ALLOC_CAP_BYTES=%lld",
+                 bytes, cap);
+        return GNN_ERR_OOM;
+    }
     void *p = nullptr;
     hipError_t e = hipMalloc(&p, bytes);
     if (e != hipSuccess) {

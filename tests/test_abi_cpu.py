@@ -130,3 +130,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="HIP library missing"):
         g.lib()
 
+
+def test_alloc_cap_forces_oom_before_any_hip_call(g, monkeypatch):
+    """GNN_ALLOC_CAP_BYTES (a test hook) refuses every device allocation larger
+    than the cap before hipMalloc is called: plan creation and the CSR build
+    then fail cleanly with GNN_ERR_OOM, naming the cap, with no GPU needed."""
+    L = g.lib()
+    A = 0x10000
+    h = C.c_void_p()
+    e = C.c_int64()
+    monkeypatch.setenv("GNN_ALLOC_CAP_BYTES", "0")
+    assert L.gnn_plan_create(A, A, 10, 20, None, None, C.byref(h)) == -4
+    assert h.value is None                                     # *plan_out untouched on failure
+    assert "GNN_ALLOC_CAP_BYTES=0" in g.gnn_status_string(-4)
+    assert L.gnn_csr_build(A, A, 5, 3, 1, A, A, 10, C.byref(e), None) == -4
+    monkeypatch.setenv("GNN_ALLOC_CAP_BYTES", "32")            # below the first 64-byte request
+    assert L.gnn_plan_create(A, A, 10, 20, None, None, C.byref(h)) == -4
+    assert "GNN_ALLOC_CAP_BYTES=32" in g.gnn_status_string(-4)
+    with pytest.raises(g.GnnError) as err:
+        g._check(L.gnn_plan_create(A, A, 10, 20, None, None, C.byref(h)), "gnn_plan_create")
+    assert err.value.status == -4 and "GNN_ERR_OOM" in str(err.value)

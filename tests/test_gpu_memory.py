@@ -30,7 +30,30 @@ PAGE = 2 * MIB      # granularity at which the device free memory moves
 def g():
     import io_aware_sparse_amd as g
     g.lib()
+    _load_code_objects(g)
     return g
+
+
+def _load_code_objects(g):
+    """Run each attention code path once on a tiny graph. A code object is
+    loaded onto the device at its first kernel launch, with its static device
+    data (the allocation-free forward's 16 MiB scratch lives in the attention
+    code object): a one-time cost per process, which the audits below must
+    not count against the call they measure."""
+    import torch
+    wl = workloads.make("gt_comm16_n1m_deg27", 256, features=False)
+    ip, ix = g.gnn_csr_build(torch.from_numpy(wl.src).cuda(), torch.from_numpy(wl.dst).cuda(), wl.n_nodes)
+    plan = g.gnn_plan_create(ip, ix, want_csc=True, tile_density=0.75)
+    assert g.gnn_plan_export(plan)["n_tiles"] > 0
+    for dt, H, D in ((torch.bfloat16, 8, 64), (torch.float32, 2, 16)):
+        q = torch.randn(wl.n_nodes, H, D, device="cuda").to(dt)
+        O, L = g.gnn_attn_fwd(plan, ip, ix, q, q, q)
+        g.gnn_attn_bwd(plan, ip, ix, q, q, q, O, q, L)
+        if dt == torch.float32:
+            att = torch.randn(H, D, device="cuda")
+            O, L = g.gatv2_attn_fwd(plan, ip, ix, q, q, att)
+            g.gatv2_attn_bwd(plan, ip, ix, q, q, att, q, L)
+    torch.cuda.synchronize()
 
 
 def _dev(wl, nm):
@@ -122,3 +145,50 @@ def test_memory_audit(g, name, tiles):
     _audit(g, plan, wl, E, "forward", fwd, _ws_fwd(d, H, D))
     if backward:
         _audit(g, plan, wl, E, "backward", bwd, _ws_bwd(d, N, H, D, wl.kind == "gatv2"))
+
+
+def test_alloc_cap_fails_cleanly_midway(g, monkeypatch):
+    """With GNN_ALLOC_CAP_BYTES between the sizes of a plan's allocations,
+    gnn_plan_create fails with GNN_ERR_OOM part-way (after some arrays were
+    allocated) and frees everything it took; a forward whose workspace would
+    grow past the cap fails the same way and writes nothing; with the cap
+    cleared both succeed."""
+    import torch
+    from io_aware_sparse_amd import GnnError
+    wl = workloads.make("gatv2_zipf21_n100k", 20000, features=False)
+    n = wl.n_nodes
+    ip, ix = g.gnn_csr_build(torch.from_numpy(wl.src).cuda(), torch.from_numpy(wl.dst).cuda(), n)
+    E = int(ix.numel())
+    # the plan's first requests (validation, sortedness check, buckets) are far below
+    # 16 * E bytes, the transposed adjacency's temporary (24 bytes per edge) above it
+    monkeypatch.setenv("GNN_ALLOC_CAP_BYTES", str(16 * E))
+    plans = []
+
+    def attempt():
+        try:
+            plans.append(g.gnn_plan_create(ip, ix, want_csc=True, light_threshold=64, chunk=64))
+        except GnnError as e:
+            return e
+    err, taken = _library_bytes(attempt)
+    say(f"alloc cap {16 * E} B: {err}; library bytes left behind {taken}")
+    assert err is not None and err.status == -4 and "GNN_ALLOC_CAP_BYTES" in str(err)
+    assert not plans
+    assert taken <= PAGE, taken
+    monkeypatch.delenv("GNN_ALLOC_CAP_BYTES")
+    plan = g.gnn_plan_create(ip, ix, want_csc=True, light_threshold=64, chunk=64)
+    d = g.gnn_plan_export(plan)
+    assert d["n_groups"] > 0 and d["workspace_bytes"] == 0
+    H, D = 4, 32
+    q = torch.randn(n, H, D, device="cuda")
+    O = torch.full_like(q, 5.0)
+    monkeypatch.setenv("GNN_ALLOC_CAP_BYTES", str(_ws_fwd(d, H, D) - 1))
+    with pytest.raises(GnnError) as e:
+        g.gnn_attn_fwd(plan, ip, ix, q, q, q, O=O)
+    assert e.value.status == -4
+    torch.cuda.synchronize()
+    assert torch.all(O == 5.0) and g.gnn_plan_export(plan)["workspace_bytes"] == 0
+    monkeypatch.setenv("GNN_ALLOC_CAP_BYTES", str(_ws_fwd(d, H, D)))
+    g.gnn_attn_fwd(plan, ip, ix, q, q, q, O=O)
+    torch.cuda.synchronize()
+    assert g.gnn_plan_export(plan)["workspace_bytes"] == _ws_fwd(d, H, D)
+    assert not torch.any(O == 5.0)
