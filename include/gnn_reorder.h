@@ -36,9 +36,16 @@ typedef enum {
 
 /*
  * Node order for relabelling: perm[new id] = old id, int32 [N], written to
- * device memory. Deterministic (independent of scheduling). RCM costs one
- * label-propagation sweep per unit of the largest component's diameter and
- * one breadth-first level at a time; both are O(E) per step.
+ * device memory. Deterministic (independent of scheduling). RCM labels
+ * components by min-rank hooking with pointer jumping (about log2 of the
+ * largest component's diameter sweeps) and then searches breadth first one
+ * level at a time; both are O(E) per step with one host synchronisation.
+ * Both loops are capped: label sweeps at 64 + 8 * ceil(log2(N + 1)), search
+ * levels at 65,536 (a component deeper than that from its start, e.g. a
+ * path of more than 65,537 nodes); reaching a cap returns
+ * GNN_ERR_UNSUPPORTED (degree order has no such limit). The environment
+ * variables GNN_RCM_MAX_SWEEPS and GNN_RCM_MAX_LEVELS (positive integers)
+ * override the caps.
  * GNN_ERR_INVALID_ARG for bad sizes or method.
  */
 int gnn_reorder(const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, gnn_order_t method,

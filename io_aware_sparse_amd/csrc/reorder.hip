@@ -15,8 +15,13 @@
 // unvisited neighbours in ascending rank. Its order is computed here without
 // a sequential queue:
 //  * the start of a component is its member of smallest rank, and components
-//    come in the order of their starts; min-rank label propagation over the
-//    symmetrised graph labels every node with its start's rank;
+//    come in the order of their starts; min-rank labelling over the
+//    symmetrised graph labels every node with its start's rank. Each sweep
+//    hooks along every entry (the smaller label of its two ends is written to
+//    both ends and to the nodes whose ranks their labels are, the roots of
+//    their label trees) and then jumps every label one step up its tree
+//    (label[v] = label[node of rank label[v]]), so label chains shorten
+//    geometrically: about log2(diameter) sweeps instead of one per hop;
 //  * one breadth-first search runs from all starts at once, level by level.
 //    A node of level L is appended, in the sequential order, by its neighbour
 //    of level L-1 that comes first; among the level's new nodes of one
@@ -26,13 +31,16 @@
 //    parent index, degree, id) with two stable radix passes, which gives
 //    their own within-level indices;
 //  * the final order sorts all nodes by (component, level, within-level
-//    index). Work: O(E) per label sweep (sweeps = largest component diameter
-//    + 1), O(E) for the search, sorts of O(N); one host synchronisation per
-//    sweep and per level.
+//    index). Work: O(E) per label sweep, O(E) for the search, sorts of O(N);
+//    one host synchronisation per sweep and per level. Both loops are capped
+//    (label sweeps: 64 + 8 log2 N; search levels: 65,536); a graph that
+//    reaches a cap returns GNN_ERR_UNSUPPORTED (the environment variables
+//    GNN_RCM_MAX_SWEEPS and GNN_RCM_MAX_LEVELS override the caps).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
 #include <vector>
 
 #include "gnn_reorder.h"
@@ -81,11 +89,15 @@ __device__ __forceinline__ int wave_min(int x) {
     return x;
 }
 
-// one sweep of min-label propagation along every entry, both directions; one
-// wave per row: the smallest label of the row and its sources, then pushed to
-// every larger one
-__global__ void k_label_sweep(const int32_t *indptr, const int32_t *indices, int32_t n, int32_t *label,
-                              int32_t *changed) {
+// Labels are ranks of nodes of the same component and only decrease, so the
+// node of rank label[v] (node_of[label[v]]) is in v's component and its label
+// is a valid label for v.
+//
+// Hooking sweep along every entry, both directions; one wave per row: the
+// smallest label of the row and its sources is written to every larger one
+// and to the node owning that larger label (the root of its label tree)
+__global__ void k_label_hook(const int32_t *indptr, const int32_t *indices, int32_t n, const int32_t *node_of,
+                             int32_t *label, int32_t *changed) {
     const int64_t v = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWaveR;
     const int lane = threadIdx.x % kWaveR;
     if (v >= n) return;
@@ -96,16 +108,34 @@ __global__ void k_label_sweep(const int32_t *indptr, const int32_t *indices, int
     bool moved = false;
     for (int32_t e = e0 + lane; e < e1; e += kWaveR) {
         const int32_t u = indices[e];
-        if (lv < label[u]) {
+        const int32_t lu = label[u];
+        if (lv < lu) {
             atomicMin(label + u, lv);
+            atomicMin(label + node_of[lu], lv);
             moved = true;
         }
     }
-    if (lane == 0 && lv < label[v]) {
-        atomicMin(label + v, lv);
-        moved = true;
+    if (lane == 0) {
+        const int32_t l0 = label[v];
+        if (lv < l0) {
+            atomicMin(label + v, lv);
+            atomicMin(label + node_of[l0], lv);
+            moved = true;
+        }
     }
     if (moved) *changed = 1;
+}
+
+// one pointer-jumping step for every node: label[v] = label[node of rank label[v]]
+__global__ void k_label_jump(int32_t n, const int32_t *node_of, int32_t *label, int32_t *changed) {
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= n) return;
+    const int32_t l = label[v];
+    const int32_t up = label[node_of[l]];
+    if (up < l) {
+        atomicMin(label + v, up);
+        *changed = 1;
+    }
 }
 
 // starts: nodes whose label is their own rank; level 0, within-level index 0
@@ -247,7 +277,18 @@ static int degree_order(ReorderWs &w, int32_t n, int64_t e, int descending, int3
     return GNN_OK;
 }
 
+// loop cap from the environment variable `name` (a positive integer), else dflt
+static int64_t env_cap(const char *name, int64_t dflt) {
+    const char *s = getenv(name);
+    if (!s || !*s) return dflt;
+    char *end = nullptr;
+    const long long v = strtoll(s, &end, 10);
+    return (end != s && *end == '\0' && v > 0) ? (int64_t)v : dflt;
+}
+
 static int rcm(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, int32_t *perm, hipStream_t s) {
+    const int64_t max_sweeps = env_cap("GNN_RCM_MAX_SWEEPS", 64 + 8 * (int64_t)bits_for((int64_t)n + 1));
+    const int64_t max_levels = env_cap("GNN_RCM_MAX_LEVELS", 65536);
     ReorderWs w;
     GNN_TRY(reorder_ws(w, n));
     DevBuf cindptr, cindices;
@@ -257,12 +298,18 @@ static int rcm(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t
     if (rc == GNN_OK) rc = degree_order(w, n, e, 0, w.front, s);
     if (rc == GNN_OK) {
         hipLaunchKernelGGL(k_rank_of, grid1d(n), dim3(256), 0, s, w.front, n, w.rank, w.label);
-        // components: min-rank label propagation until a sweep changes nothing
-        for (;;) {
+        // components: hooking and one jump per sweep until a sweep changes
+        // nothing (w.front holds the node of each rank until the search starts)
+        for (int64_t sweep = 0;; ++sweep) {
+            if (sweep == max_sweeps) {
+                rc = GNN_ERR_UNSUPPORTED;
+                break;
+            }
             int32_t changed = 0;
             hipLaunchKernelGGL(k_set_i32, dim3(1), dim3(1), 0, s, w.flag, 0);
-            hipLaunchKernelGGL(k_label_sweep, grid1d((int64_t)n * kWaveR), dim3(256), 0, s, indptr, indices, n, w.label,
-                               w.flag);
+            hipLaunchKernelGGL(k_label_hook, grid1d((int64_t)n * kWaveR), dim3(256), 0, s, indptr, indices, n, w.front,
+                               w.label, w.flag);
+            hipLaunchKernelGGL(k_label_jump, grid1d(n), dim3(256), 0, s, n, w.front, w.label, w.flag);
             if ((rc = read_i32(w.flag, &changed, s)) != GNN_OK || !changed) break;
         }
     }
@@ -282,6 +329,10 @@ static int rcm(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t
         hipLaunchKernelGGL(k_expand, grid1d((int64_t)nf * kWaveR), dim3(256), 0, s, w.front, nf, indptr, indices,
                            as<int32_t>(cindptr), as<int32_t>(cindices), w.level, w.wr, w.pmin, w.cand, w.flag);
         if ((rc = read_i32(w.flag, &nc, s)) != GNN_OK || nc == 0) break;
+        if (L > max_levels) {      // level L has nodes: the search needs more levels than the cap
+            rc = GNN_ERR_UNSUPPORTED;
+            break;
+        }
         hipLaunchKernelGGL(k_cand_keys1, grid1d(nc), dim3(256), 0, s, w.cand, nc, w.deg, w.keys, w.vals);
         rc = radix_sort(w.keys, w.tmp, nc, 64, w.scratch, s, w.vals, w.vtmp);
         if (rc != GNN_OK) break;

@@ -138,3 +138,30 @@ def test_reorder_full_size(g, name):
     assert int(nip[-1].item()) == ix.size
     b0, b1 = oracle.bandwidth(ip, ix), oracle.bandwidth(nip.cpu().numpy(), nix.cpu().numpy())
     say(f"  bandwidth {b0} -> {b1} after RCM")
+
+
+def test_rcm_loop_caps_on_a_long_path(g, monkeypatch):
+    """A 10,000-node path with shuffled labels (diameter 9,999). Component
+    labelling (hooking with pointer jumping) finishes within
+    ceil(log2 N) + 8 = 22 sweeps: with the sweep cap set to that, the order
+    still equals the oracle's bit for bit. A sweep cap of 3, or a level cap
+    below the path's 9,999 search levels, returns GNN_ERR_UNSUPPORTED."""
+    from io_aware_sparse_amd import GnnError
+    rng = np.random.default_rng(33)
+    n = 10_000
+    q = rng.permutation(n)
+    ip, ix = oracle.csr_build(q[:-1], q[1:], n)
+    want = oracle.reorder(ip, ix, n, "rcm")
+    ip_d, ix_d = dev_i32(ip), dev_i32(ix)
+    monkeypatch.setenv("GNN_RCM_MAX_SWEEPS", str(int(np.ceil(np.log2(n))) + 8))
+    got = g.gnn_reorder(ip_d, ix_d, "rcm")
+    assert np.array_equal(got.cpu().numpy(), want)
+    for var, cap in (("GNN_RCM_MAX_SWEEPS", "3"), ("GNN_RCM_MAX_LEVELS", "9998")):
+        monkeypatch.delenv("GNN_RCM_MAX_SWEEPS", raising=False)
+        monkeypatch.setenv(var, cap)
+        with pytest.raises(GnnError) as e:
+            g.gnn_reorder(ip_d, ix_d, "rcm")
+        assert e.value.status == -2, (var, cap)
+        say(f"RCM on a {n}-node path with {var}={cap}: GNN_ERR_UNSUPPORTED")
+    monkeypatch.setenv("GNN_RCM_MAX_LEVELS", "9999")
+    assert np.array_equal(g.gnn_reorder(ip_d, ix_d, "rcm").cpu().numpy(), want)
