@@ -111,11 +111,13 @@ __device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp
     const int64_t rowlen = (int64_t)G.H * G.D;
     float q[NV];
     float a[NV];
+    typename VT::raw qraw = VT::zero();       // the GT score takes q packed (dot_vec)
 #pragma unroll
     for (int k = 0; k < NV; ++k) q[k] = a[k] = 0.f;
     if (lp.act) {
-        VT::unpack(load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col), q);
+        qraw = load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col);
         if (MODE != M_GT) {
+            VT::unpack(qraw, q);
 #pragma unroll
             for (int k = 0; k < NV; ++k) a[k] = P.att[lp.col + k] * kLog2e;
         }
@@ -153,13 +155,12 @@ __device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp
         float s[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float kf[NV];
-            VT::unpack(kr[u], kf);
             float t = 0.f;
             if (MODE == M_GT) {
-#pragma unroll
-                for (int k = 0; k < NV; ++k) t = fmaf(q[k], kf[k], t);
+                t = dot_vec(qraw, kr[u], 0.f);
             } else {
+                float kf[NV];
+                VT::unpack(kr[u], kf);
 #pragma unroll
                 for (int k = 0; k < NV; ++k) {
                     const float z = kf[k] + q[k];
@@ -258,9 +259,7 @@ __device__ __forceinline__ void bwd_dst_stream(const BwdParams &P, const LanePos
     constexpr int NV = VT::N;
     const Geom &G = P.g;
     const int64_t rowlen = (int64_t)G.H * G.D;
-    float q[NV], dof[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) q[k] = dof[k] = 0.f;
+    typename VT::raw q = VT::zero(), dof = VT::zero();   // both dot products take packed operands
     if (reset) {
 #pragma unroll
         for (int k = 0; k < NV; ++k) A[k] = B[k] = 0.f;
@@ -268,8 +267,8 @@ __device__ __forceinline__ void bwd_dst_stream(const BwdParams &P, const LanePos
     }
     lse2 = kNegInf;
     if (lp.act) {
-        VT::unpack(load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col), q);
-        VT::unpack(load_vec<T>(P.dO, (int64_t)node * rowlen + lp.col), dof);
+        q = load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col);
+        dof = load_vec<T>(P.dO, (int64_t)node * rowlen + lp.col);
         lse2 = P.LSE[(int64_t)node * G.H + lp.h] * kLog2e;
     }
     const int S = min(kWave, G.G * U);
@@ -290,15 +289,9 @@ __device__ __forceinline__ void bwd_dst_stream(const BwdParams &P, const LanePos
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float kf[NV], vf[NV];
+            float kf[NV];
             VT::unpack(kr[u], kf);
-            VT::unpack(vr[u], vf);
-            float ts = 0.f, tp = 0.f;
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                ts = fmaf(q[k], kf[k], ts);
-                tp = fmaf(dof[k], vf[k], tp);
-            }
+            float ts = dot_vec(q, kr[u], 0.f), tp = dot_vec(dof, vr[u], 0.f);
             ts = group_sum<LH>(ts);
             tp = group_sum<LH>(tp);
             const float p = (j[u] >= 0) ? fast_exp2(ts * P.mul - lse2) : 0.f;
@@ -325,16 +318,14 @@ __device__ __forceinline__ void bwd_src_stream(const BwdParams &P, const LanePos
     constexpr int NV = VT::N;
     const Geom &G = P.g;
     const int64_t rowlen = (int64_t)G.H * G.D;
-    float kf[NV], vf[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) kf[k] = vf[k] = 0.f;
+    typename VT::raw kown = VT::zero(), vown = VT::zero();   // both dot products take packed operands
     if (reset) {
 #pragma unroll
         for (int k = 0; k < NV; ++k) dk[k] = dv[k] = 0.f;
     }
     if (lp.act) {
-        VT::unpack(load_vec<T>(P.K, (int64_t)node * rowlen + lp.col), kf);
-        VT::unpack(load_vec<T>(P.V, (int64_t)node * rowlen + lp.col), vf);
+        kown = load_vec<T>(P.K, (int64_t)node * rowlen + lp.col);
+        vown = load_vec<T>(P.V, (int64_t)node * rowlen + lp.col);
     }
     const int S = min(kWave, G.G * U);
     const int UE = S / G.G;
@@ -359,12 +350,7 @@ __device__ __forceinline__ void bwd_src_stream(const BwdParams &P, const LanePos
             float qf[NV], gf[NV];
             VT::unpack(qr[u], qf);
             VT::unpack(gr[u], gf);
-            float ts = 0.f, tp = 0.f;
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                ts = fmaf(qf[k], kf[k], ts);
-                tp = fmaf(gf[k], vf[k], tp);
-            }
+            float ts = dot_vec(qr[u], kown, 0.f), tp = dot_vec(gr[u], vown, 0.f);
             ts = group_sum<LH>(ts);
             tp = group_sum<LH>(tp);
             const float p = (i[u] >= 0) ? fast_exp2(ts * P.mul - stt[u].x) : 0.f;

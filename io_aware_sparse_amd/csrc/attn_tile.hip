@@ -24,6 +24,14 @@
 // rows with the same code as the light path, continuing the same state, so
 // no cross-kernel merge is needed. P and dS enter the second products as
 // bf16 (rounding 2^-9 relative per term).
+//
+// Occupancy. The state hand-off buffer overlays the staging rows (it is
+// written only after the last tile's products have read them), so a
+// workgroup's LDS is the larger of the two, not their sum. When the head
+// group has fewer heads than the workgroup has waves (the backward passes at
+// D = 64 and 128), SPLIT waves share a head, each accumulating its own share
+// of the D output columns (the score products are recomputed by each): every
+// wave has MFMA work, and each holds 1/SPLIT of the accumulators.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -120,8 +128,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
     // store writes at once fall on different banks (an even SW put HW*SW a
     // multiple of the bank count)
     const int SW = D + 3;
-    float *state = lds;
-    uint16_t *vst = reinterpret_cast<uint16_t *>(lds + 16 * HW * SW);     // [16][stride]
+    float *state = lds;                                   // written after the last tile, over the staged rows
+    uint16_t *vst = reinterpret_cast<uint16_t *>(lds);   // [16][stride]
     const int row0 = rb * 16;
     const int m = l & 15, q4 = l >> 4;
 
@@ -233,10 +241,12 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
 
 // ----------------------------------------------------- backward, dst pass
 
-template <int LH, int D, int HS>
-__global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, TileArgs A) {
+// WPE: minimum waves per SIMD the register allocation must allow (1: no constraint)
+template <int LH, int D, int HS, int SPLIT, int WPE>
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(WPE))) void k_tile_bwd_dst(BwdParams P,
+                                                                                                         TileArgs A) {
     constexpr int NV = Vec<bf16_tag>::N;
-    constexpr int KC = D / 32, DC = D / 16;
+    constexpr int KC = D / 32, DC = D / 16, DCW = DC / SPLIT;
     extern __shared__ float lds[];
     const Geom &G = P.g;
     const int HW = G.HW, N = G.N;
@@ -247,20 +257,21 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, Tile
     const int64_t c0 = (int64_t)hg * HW * D;
     const int64_t valid = rowlen - c0;
     const int SW = 2 * D + 1;
-    float *state = lds;                                                    // [16][HW][2D+1]: A, B, Delta
-    uint16_t *kst = reinterpret_cast<uint16_t *>(lds + 16 * HW * SW);      // [16][stride]
+    float *state = lds;                                   // [16][HW][2D+1]: A, B, Delta (after the last tile)
+    uint16_t *kst = reinterpret_cast<uint16_t *>(lds);   // [16][stride]
     uint16_t *vst = kst + 16 * stride;
     const int row0 = rb * 16;
     const int m = l & 15, q4 = l >> 4;
+    const int part = w % SPLIT, c0w = part * DCW;        // this wave's output column chunks
 
-    f32x4_t Aa[HS][DC], Ba[HS][DC];
+    f32x4_t Aa[HS][DCW], Ba[HS][DCW];
     uint4 qop[HS][KC], gop[HS][KC];
     float lse2[HS], dl[HS];
     int hh[HS];
     bool hv[HS];
 #pragma unroll
     for (int s = 0; s < HS; ++s) {
-        hh[s] = w + kTileWaves * s;
+        hh[s] = w / SPLIT + (kTileWaves / SPLIT) * s;
         hv[s] = hh[s] < HW && hg * HW + hh[s] < G.H;
         const int h = hg * HW + hh[s];
         const bool ok = hv[s] && row0 + m < N;
@@ -273,7 +284,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, Tile
         lse2[s] = ok ? P.LSE[(int64_t)(row0 + m) * G.H + h] * kLog2e : 0.f;
         dl[s] = 0.f;
 #pragma unroll
-        for (int c = 0; c < DC; ++c) Aa[s][c] = Ba[s][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < DCW; ++c) Aa[s][c] = Ba[s][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     for (int t = A.tile_ptr[rb]; t < A.tile_ptr[rb + 1]; ++t) {
         const int col0 = A.tile_rc[2 * t + 1] * 16;
@@ -301,10 +312,11 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, Tile
             }
             const i16x4_t pb = pack4(p), pdb = pack4(pd);
 #pragma unroll
-            for (int c = 0; c < DC; ++c) {
+            for (int c = 0; c < DCW; ++c) {
                 i16x4_t ka;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ka[i] = (short)kst[(4 * q4 + i) * stride + hh[s] * D + c * 16 + m];
+                for (int i = 0; i < 4; ++i)
+                    ka[i] = (short)kst[(4 * q4 + i) * stride + hh[s] * D + (c0w + c) * 16 + m];
                 Aa[s][c] = mfma16(ka, pdb, Aa[s][c]);
                 Ba[s][c] = mfma16(ka, pb, Ba[s][c]);
             }
@@ -317,13 +329,13 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, Tile
         if (!hv[s]) continue;
         float *row = state + ((int64_t)m * HW + hh[s]) * SW;
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
+        for (int c = 0; c < DCW; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                row[c * 16 + 4 * q4 + i] = Aa[s][c][i];
-                row[D + c * 16 + 4 * q4 + i] = Ba[s][c][i];
+                row[(c0w + c) * 16 + 4 * q4 + i] = Aa[s][c][i];
+                row[D + (c0w + c) * 16 + 4 * q4 + i] = Ba[s][c][i];
             }
-        if (q4 == 0) row[2 * D] = d_row;
+        if (q4 == 0 && part == 0) row[2 * D] = d_row;
     }
     __syncthreads();
     const LanePos lp = lane_pos<LH, NV>(G, hg);
@@ -352,10 +364,11 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_dst(BwdParams P, Tile
 
 // ----------------------------------------------------- backward, src pass
 
-template <int LH, int D, int HS>
-__global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, TileArgs A) {
+template <int LH, int D, int HS, int SPLIT, int WPE>
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(WPE))) void k_tile_bwd_src(BwdParams P,
+                                                                                                         TileArgs A) {
     constexpr int NV = Vec<bf16_tag>::N;
-    constexpr int KC = D / 32, DC = D / 16;
+    constexpr int KC = D / 32, DC = D / 16, DCW = DC / SPLIT;
     extern __shared__ float lds[];
     const Geom &G = P.g;
     const int HW = G.HW, N = G.N;
@@ -365,20 +378,21 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
     const int width = HW * D, stride = width + kRowPad;
     const int64_t c0 = (int64_t)hg * HW * D;
     const int64_t valid = rowlen - c0;
-    const int SW = 2 * D + 1;                                              // odd: see the forward's state
-    float *state = lds;                                                    // [16][HW][SW]: dK, dV
-    uint16_t *qst = reinterpret_cast<uint16_t *>(lds + 16 * HW * SW);      // [16][stride]
+    const int SW = 2 * D + 1;                             // odd: see the forward's state
+    float *state = lds;                                   // [16][HW][SW]: dK, dV (after the last tile)
+    uint16_t *qst = reinterpret_cast<uint16_t *>(lds);   // [16][stride]
     uint16_t *gst = qst + 16 * stride;
     const int col0 = cb * 16;
     const int n = l & 15, q4 = l >> 4;
+    const int part = w % SPLIT, c0w = part * DCW;        // this wave's output column chunks
 
-    f32x4_t dKa[HS][DC], dVa[HS][DC];
+    f32x4_t dKa[HS][DCW], dVa[HS][DCW];
     uint4 kop[HS][KC], vop[HS][KC];
     int hh[HS];
     bool hv[HS];
 #pragma unroll
     for (int s = 0; s < HS; ++s) {
-        hh[s] = w + kTileWaves * s;
+        hh[s] = w / SPLIT + (kTileWaves / SPLIT) * s;
         hv[s] = hh[s] < HW && hg * HW + hh[s] < G.H;
         const int h = hg * HW + hh[s];
         const bool ok = hv[s] && col0 + n < N;
@@ -389,7 +403,7 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
             vop[s][kk] = ldg16(P.V, e, ok);
         }
 #pragma unroll
-        for (int c = 0; c < DC; ++c) dKa[s][c] = dVa[s][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < DCW; ++c) dKa[s][c] = dVa[s][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     for (int x = A.tile_ptr[cb]; x < A.tile_ptr[cb + 1]; ++x) {
         const int t = A.tile_ids[x];
@@ -422,12 +436,12 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
             }
             const i16x4_t pb = pack4(p), dsb = pack4(ds);
 #pragma unroll
-            for (int c = 0; c < DC; ++c) {
+            for (int c = 0; c < DCW; ++c) {
                 i16x4_t ga, qa;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    ga[i] = (short)gst[(4 * q4 + i) * stride + hh[s] * D + c * 16 + n];
-                    qa[i] = (short)qst[(4 * q4 + i) * stride + hh[s] * D + c * 16 + n];
+                    ga[i] = (short)gst[(4 * q4 + i) * stride + hh[s] * D + (c0w + c) * 16 + n];
+                    qa[i] = (short)qst[(4 * q4 + i) * stride + hh[s] * D + (c0w + c) * 16 + n];
                 }
                 dVa[s][c] = mfma16(ga, pb, dVa[s][c]);
                 dKa[s][c] = mfma16(qa, dsb, dKa[s][c]);
@@ -440,11 +454,11 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
         if (!hv[s]) continue;
         float *row = state + ((int64_t)n * HW + hh[s]) * SW;
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
+        for (int c = 0; c < DCW; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                row[c * 16 + 4 * q4 + i] = dKa[s][c][i];
-                row[D + c * 16 + 4 * q4 + i] = dVa[s][c][i];
+                row[(c0w + c) * 16 + 4 * q4 + i] = dKa[s][c][i];
+                row[D + (c0w + c) * 16 + 4 * q4 + i] = dVa[s][c][i];
             }
     }
     __syncthreads();
@@ -477,11 +491,20 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_bwd_src(BwdParams P, Tile
 
 bool tile_supported(gnn_dtype_t dt, int D) { return dt == GNN_BF16 && (D == 32 || D == 64 || D == 128); }
 
+// LDS of a tile workgroup: the state hand-off buffer overlays the staged rows
 static size_t tile_lds(int kind, int HW, int D) {
     const size_t stage = (size_t)16 * (HW * D + kRowPad) * 2;
-    if (kind == 0) return (size_t)16 * HW * (D + 3) * 4 + stage;
-    if (kind == 1) return (size_t)16 * HW * (2 * D + 1) * 4 + 2 * stage;
-    return (size_t)16 * HW * (2 * D + 1) * 4 + 2 * stage;
+    if (kind == 0) return std::max((size_t)16 * HW * (D + 3) * 4, stage);
+    return std::max((size_t)16 * HW * (2 * D + 1) * 4, 2 * stage);
+}
+
+// waves per head in the backward tile kernels: 8 / HW when that divides the
+// head's output chunks (D / 16), else 1
+static int tile_split(int HW, int D) {
+    const int dc = D / 16;
+    if (HW * 4 <= kTileWaves && dc % 4 == 0) return 4;
+    if (HW * 2 <= kTileWaves && dc % 2 == 0) return 2;
+    return 1;
 }
 
 // head-group geometry of the tile kernels: as the CSR path, with the head
@@ -510,21 +533,35 @@ static int tile_fwd_d(gnn_plan_t plan, FwdParams P, const TileArgs &A, hipStream
     return launch(plan, K_TILE_FWD, k_tile_fwd<D / 8, D, 1>, grid, dim3(kTileThreads), lds, s, P, A);
 }
 
+// Three 8-wave workgroups per CU need 6 waves per SIMD (80 VGPRs). The
+// variants that hold at most half a D = 64 head's accumulators per wave fit
+// that without spills; the others (two heads per wave at D = 32, a whole
+// D = 64 head, D = 128) keep their natural allocation rather than spill.
+template <int D, int HS, int SPLIT>
+static int launch_tile_bwd(gnn_plan_t plan, const BwdParams &P, const TileArgs &A, int kind, dim3 grid, size_t lds,
+                           hipStream_t s) {
+    constexpr int WPE = (HS == 1 && D <= 64 && D / SPLIT <= 32) ? 6 : 1;
+    if (kind == 1)
+        return launch(plan, K_TILE_BWD_DST, k_tile_bwd_dst<D / 8, D, HS, SPLIT, WPE>, grid, dim3(kTileThreads), lds,
+                      s, P, A);
+    return launch(plan, K_TILE_BWD_SRC, k_tile_bwd_src<D / 8, D, HS, SPLIT, WPE>, grid, dim3(kTileThreads), lds, s,
+                  P, A);
+}
+
 template <int D>
 static int tile_bwd_d(gnn_plan_t plan, BwdParams P, const TileArgs &A, int kind, hipStream_t s) {
     P.g = tile_geom(P.g, kind, D);
     const size_t lds = tile_lds(kind, P.g.HW, D);
     const dim3 grid((unsigned)((int64_t)A.n_blocks * P.g.NHG));
     if constexpr (D == 32) {
-        if (P.g.HW > kTileWaves) {
-            if (kind == 1)
-                return launch(plan, K_TILE_BWD_DST, k_tile_bwd_dst<D / 8, D, 2>, grid, dim3(kTileThreads), lds, s, P, A);
-            return launch(plan, K_TILE_BWD_SRC, k_tile_bwd_src<D / 8, D, 2>, grid, dim3(kTileThreads), lds, s, P, A);
-        }
+        if (P.g.HW > kTileWaves) return launch_tile_bwd<D, 2, 1>(plan, P, A, kind, grid, lds, s);
     }
-    if (kind == 1)
-        return launch(plan, K_TILE_BWD_DST, k_tile_bwd_dst<D / 8, D, 1>, grid, dim3(kTileThreads), lds, s, P, A);
-    return launch(plan, K_TILE_BWD_SRC, k_tile_bwd_src<D / 8, D, 1>, grid, dim3(kTileThreads), lds, s, P, A);
+    const int split = tile_split(P.g.HW, D);
+    if constexpr ((D / 16) % 4 == 0) {
+        if (split == 4) return launch_tile_bwd<D, 1, 4>(plan, P, A, kind, grid, lds, s);
+    }
+    if (split == 2) return launch_tile_bwd<D, 1, 2>(plan, P, A, kind, grid, lds, s);
+    return launch_tile_bwd<D, 1, 1>(plan, P, A, kind, grid, lds, s);
 }
 
 static TileArgs dst_args(gnn_plan_t p) {

@@ -105,6 +105,29 @@ struct Vec<bf16_tag> {
     __device__ __forceinline__ static raw zero() { return make_uint4(0u, 0u, 0u, 0u); }
 };
 
+// acc + <a, b> over one 16-byte vector pair. fp32: four fmas in element
+// order. bf16: v_dot2_f32_bf16 on each packed word (the two bf16 products are
+// exact in fp32), so the operands are never unpacked.
+__device__ __forceinline__ float dot_vec(const float4 &a, const float4 &b, float acc) {
+    acc = fmaf(a.x, b.x, acc);
+    acc = fmaf(a.y, b.y, acc);
+    acc = fmaf(a.z, b.z, acc);
+    return fmaf(a.w, b.w, acc);
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ float dot_vec(const uint4 &a, const uint4 &b, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc,
+                                          false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc,
+                                          false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc,
+                                          false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc,
+                                           false);
+}
+
 template <class T>
 __device__ __forceinline__ typename Vec<T>::raw load_vec(const void *base, int64_t elem_off) {
     using raw = typename Vec<T>::raw;
