@@ -114,6 +114,9 @@ int gnn_plan_opts_default(gnn_plan_opts *opts /*host*/);
  * if E > cap (indptr is then complete, indices truncated). Temporary device
  * memory (about 20 bytes per input edge) is allocated and freed inside.
  * Synchronises `stream` once.
+ * Source: the fused CSR attention kernels (technical summary, Methodology,
+ * attention-based layers) take the graph as CSR; by destination so a node's
+ * softmax runs over its in-neighbours (the workload descriptions).
  */
 int gnn_csr_build(const int32_t *src, const int32_t *dst, int64_t n_edges_in, int32_t n_nodes,
                   int32_t add_self_loops, int32_t *indptr, int32_t *indices, int64_t cap,
@@ -126,6 +129,11 @@ int gnn_csr_build(const int32_t *src, const int32_t *dst, int64_t n_edges_in, in
  * transposed adjacency with out-degree buckets and the 16x16 tile census.
  * opts NULL means defaults. Synchronises `stream` once. *plan_out is set only
  * on success.
+ * Source: technical summary, Methodology: degree-aware tiling (light and
+ * heavy node sets by a degree threshold, heavy neighbour lists cut into edge
+ * chunks reduced in parallel), graph metadata cached once and reused, the
+ * transposed adjacency precomputed for the backward pass, 16x16 block tiles
+ * for locally dense neighbourhoods.
  */
 int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nodes, int64_t n_edges,
                     const gnn_plan_opts *opts /*host, nullable*/, hipStream_t stream,
@@ -197,6 +205,11 @@ int gnn_plan_destroy(gnn_plan_t plan);
  * memory. plan NULL runs every node on the light (one wave per node) path;
  * otherwise the plan's buckets are used and must describe this graph.
  * scale <= 0 means 1/sqrt(D). LSE may be NULL.
+ * Source: technical summary, Methodology, attention-based layers, forward
+ * pass: score, softmax normalisation and aggregation fused in one streaming
+ * pass over the neighbours, running statistics in registers (online
+ * softmax), no edge-wise logits written; the per-node log-sum-exp is kept
+ * for the backward pass.
  */
 int gnn_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
                  int32_t H, int32_t D, const void *Q, const void *K, const void *V, void *O,
@@ -244,6 +257,10 @@ int gnn_attn_fwd_noalloc(gnn_plan_t plan, const int32_t *indptr, const int32_t *
  * The plan must have been created with want_csc. No atomics: results are
  * bitwise reproducible for the same inputs and plan. dQ, dK, dV must not
  * alias inputs.
+ * Source: technical summary, Methodology, attention-based layers, backward
+ * pass: a compact per-node statistic (the log-sum-exp) is cached instead of
+ * the edge weights, which are recomputed on the fly; the transposed
+ * adjacency (cached metadata) serves the source-side gradients.
  */
 int gnn_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
                  int32_t H, int32_t D, const void *Q, const void *K, const void *V, const void *O,
@@ -258,6 +275,10 @@ int gnn_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices,
  * given; O[i,h,:] = sum_j softmax_j(s_ij) V[j,h,:], where V is normally the
  * same buffer as K (then one row is gathered per edge). att is fp32 [H, D].
  * No score scaling. LSE may be NULL; plan as for gnn_attn_fwd.
+ * Source: technical summary, Methodology (GATv2 among the attention-based
+ * layers computed by the fused streaming pass) and Results (GATv2 speed and
+ * peak-memory figures); the score is GATv2's, as the workload descriptions
+ * give it.
  */
 int gatv2_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
                    int32_t H, int32_t D, const void *Q, const void *K, const void *V, const float *att,
@@ -278,6 +299,9 @@ int gatv2_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indice
  * The plan must have been created with want_csc. No atomics: d_att is a
  * fixed-order sum and every output is bitwise reproducible. The plan
  * workspace grows by N*H*D fp32 for the per-node d_att rows.
+ * Source: technical summary, Methodology (the backward pass's log-sum-exp
+ * recompute, applied to GATv2) and Results (GATv2 training memory); the
+ * gradient is the chain rule of the GATv2 score.
  */
 int gatv2_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
                    int32_t H, int32_t D, const void *Q, const void *K, const void *V, const float *att,

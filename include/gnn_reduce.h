@@ -54,6 +54,9 @@ typedef enum { GNN_MSG_SRC = 0, GNN_MSG_DIFF = 1 } gnn_msg_t;
  *   Errors: GNN_ERR_INVALID_ARG (sizes, NULL arrays, op / msg, plan built on
  *   other arrays), GNN_ERR_ALIGNMENT (X, out or arg not 16-byte aligned),
  *   GNN_ERR_OOM / GNN_ERR_HIP.
+ * Source: technical summary, Methodology, reduction-based aggregations (a
+ * per-edge computation followed by a neighbourhood min/max; degree-aware
+ * light/heavy tiling; heavy partials merged by packed (value, index) atomics).
  */
 int gnn_reduce_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
                    const void *X, void *out, int32_t *arg /*nullable*/, gnn_reduce_op_t op, gnn_msg_t msg,
@@ -72,6 +75,8 @@ int gnn_reduce_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indice
  *         out-degree buckets); heavy sources use n_groups * F * 4 bytes of
  *         workspace. GNN_ERR_INVALID_ARG without a plan, GNN_ERR_UNSUPPORTED
  *         when it has no transposed adjacency.
+ * Source: the training pass of the same reduction layer (technical summary,
+ * Methodology); the gradient is the chain rule through the winners.
  */
 int gnn_reduce_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
                    const void *dOut, const int32_t *arg, void *dX, gnn_msg_t msg, gnn_dtype_t dtype,

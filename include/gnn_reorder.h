@@ -47,6 +47,8 @@ typedef enum {
  * variables GNN_RCM_MAX_SWEEPS and GNN_RCM_MAX_LEVELS (positive integers)
  * override the caps.
  * GNN_ERR_INVALID_ARG for bad sizes or method.
+ * Source: technical summary, Methodology (graph reordering revisited for
+ * neighbour- and feature-parallel kernels).
  */
 int gnn_reorder(const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, gnn_order_t method,
                 int32_t *perm /*[N]*/, hipStream_t stream);
@@ -56,6 +58,7 @@ int gnn_reorder(const int32_t *indptr, const int32_t *indices, int32_t N, int64_
  * to the new id of j, each row sorted ascending; repeated entries are kept.
  * new_indptr [N+1], new_indices [E] (caller-allocated). perm must name every
  * node exactly once, else GNN_ERR_INVALID_ARG.
+ * Source: as gnn_reorder (applying a reordering to the graph).
  */
 int gnn_permute_graph(const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, const int32_t *perm,
                       int32_t *new_indptr, int32_t *new_indices, hipStream_t stream);
@@ -66,6 +69,7 @@ int gnn_permute_graph(const int32_t *indptr, const int32_t *indices, int32_t N, 
  * (a multiple of 16, else GNN_ERR_UNSUPPORTED); src and dst distinct and
  * 16-byte aligned (GNN_ERR_ALIGNMENT). perm is checked to name every node
  * once (GNN_ERR_INVALID_ARG); the copy itself is asynchronous on `stream`.
+ * Source: as gnn_reorder (applying a reordering to the node features).
  */
 int gnn_permute_rows(const void *src, void *dst, int32_t N, int64_t row_bytes, const int32_t *perm, int32_t back,
                      hipStream_t stream);

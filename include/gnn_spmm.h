@@ -36,6 +36,8 @@ typedef enum {
  * first call; later calls rewrite those buffers in place, ordered after
  * earlier work on `stream` (products still running on another stream race
  * with it). GNN_ERR_INVALID_ARG for a NULL plan or an unknown norm.
+ * Source: technical summary, Methodology, SpMM-based convolutions
+ * (graph-specific metadata such as normalised weights cached once).
  */
 int gnn_spmm_prepare(gnn_plan_t plan, gnn_norm_t norm, hipStream_t stream);
 
@@ -51,6 +53,9 @@ int gnn_spmm_prepare(gnn_plan_t plan, gnn_norm_t norm, hipStream_t stream);
  * fp32 accumulation in a fixed order (no atomics: bitwise reproducible), Y
  * rounded to the storage type (nearest even). Heavy rows use n_groups * F * 4
  * bytes of plan workspace.
+ * Source: technical summary, Methodology, SpMM-based convolutions (the
+ * aggregation of H' = sigma(A H W); the transposed adjacency precomputed for
+ * the backward pass).
  */
 int gnn_spmm(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
              const void *X, void *Y, int32_t transpose, gnn_dtype_t dtype, hipStream_t stream);

@@ -29,6 +29,8 @@ of the case it names:
   spmm_chunglu25_n169k    the degree-2.5 Chung-Lu graph, F = 128 fp32, for
                           the SpMM aggregation (GCN / GraphConv)
   spmm_chunglu22_n2450k   the degree-2.2 Chung-Lu graph, F = 128 bf16
+  spmm_comm16_n1m_deg27   the clustered graph with 11 inter-community sources,
+                          F = 128 bf16 (the graph the 16x16 block path targets)
 
 Self-loops are never emitted here; the CSR builder adds exactly one per node.
 
@@ -318,6 +320,8 @@ SPECS = {
     "spmm_chunglu25_n169k": dict(seed=1002, kind="spmm", graph="gt_chunglu25_n169k", n=169_343, heads=1,
                                  dim=128, dtype="f32", backward=False),
     "spmm_chunglu22_n2450k": dict(seed=1004, kind="spmm", graph="gt_chunglu22_n2450k", n=2_450_000, heads=1,
+                                  dim=128, dtype="bf16", backward=False),
+    "spmm_comm16_n1m_deg27": dict(seed=1005, kind="spmm", graph="gt_comm16_n1m_deg27", n=1_000_000, heads=1,
                                   dim=128, dtype="bf16", backward=False),
 }
 
