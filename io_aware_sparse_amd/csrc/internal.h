@@ -126,9 +126,12 @@ struct gnn_plan_s {
     int64_t n_residual = 0;
     gnn::DevBuf tile_rc, tile_mask, tile_ptr, trb, rindptr, rindices, light_nt;
     gnn::DevBuf ctile, ctile_ptr, tcb, rcindptr, rcindices, c_light_nt;
-    // cached SpMM weights (CSR order; transposed-adjacency order with the transpose), -1: none
+    // cached SpMM weights (CSR order; transposed-adjacency order with the transpose), -1: none;
+    // and each light row's entry range [e0, e1) in the descending-degree launch order (int2
+    // [n_light]; over the transposed adjacency too), so a packed wave reads its rows' ranges
+    // without first reading the row ids
     int32_t spmm_norm = -1;
-    gnn::DevBuf spmm_w, spmm_cw;
+    gnn::DevBuf spmm_w, spmm_cw, spmm_rng, spmm_crng;
     // workspace (heavy partials, backward statistics), grows on demand
     gnn::DevBuf ws;
     int64_t largest_ws = 0;

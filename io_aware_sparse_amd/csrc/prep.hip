@@ -663,7 +663,7 @@ std::vector<DevBuf *> gnn_plan_s::structures() {
     return {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &fwd.sched, &fwd.by_degree, &cindptr, &cindices,
             &bwd.light, &bwd.heavy, &bwd.groups, &bwd.partial_ofs, &bwd.sched, &bwd.by_degree, &tile_rc, &tile_mask,
             &tile_ptr, &trb, &rindptr, &rindices, &light_nt, &ctile, &ctile_ptr, &tcb, &rcindptr, &rcindices,
-            &c_light_nt, &spmm_w, &spmm_cw};
+            &c_light_nt, &spmm_w, &spmm_cw, &spmm_rng, &spmm_crng};
 }
 
 int64_t gnn_plan_s::structure_bytes() {

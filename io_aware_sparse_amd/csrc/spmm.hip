@@ -17,7 +17,9 @@
 // one 16-byte slice of a feature row; light rows run from the
 // descending-degree list 4 per wave when a row spans at most 16 lanes
 // (256 bytes), 2 per wave with 8 edges per step when it spans 17-32 lanes
-// (512 bytes), else one per wave; heavy rows run as the plan's chunk groups, their W waves
+// (512 bytes), else one per wave; the packed waves read each row's entry
+// range from a record cached by gnn_spmm_prepare, alongside the row id
+// (rows are short: one dependent load fewer before the gathers); heavy rows run as the plan's chunk groups, their W waves
 // summed in LDS and the groups summed in ascending order by a second pass.
 // fp32 accumulation, output rounded to the storage type; no atomics, so the
 // result is bitwise reproducible. The transposed product (dX = A_w^T dY) is
@@ -72,6 +74,15 @@ struct SpGeom {
     int32_t N = 0, F = 0, L = 0, lr_shift = 0, G = 1, NFG = 1;
 };
 
+// entry range of each light row, in the order of the list `light`
+__global__ void k_spmm_ranges(const int32_t *indptr, const int32_t *light, int32_t n_light, int2 *rng) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k < n_light) {
+        const int32_t v = light[k];
+        rng[k] = make_int2(indptr[v], indptr[v + 1]);
+    }
+}
+
 struct SpParams {
     SpGeom g;
     const int32_t *indptr, *indices;   // CSR, or the transposed adjacency for the transposed product
@@ -79,6 +90,7 @@ struct SpParams {
     const void *X;
     void *Y;
     const int32_t *light;
+    const int2 *rng;                   // entry range of each entry of `light` (packed launches), or null
     int32_t n_light;
     const int32_t *groups;
     int32_t n_groups;
@@ -212,6 +224,15 @@ __global__ __launch_bounds__(512) void k_spmm_main(SpParams P) {
         if (ni0 >= P.n_light) return;
         const int64_t ni = ni0 + (lane_id() / (kWave / RPW));
         node = ni < P.n_light ? P.light[ni] : -1;
+        if (P.rng) {
+            // the row's range from the cached records, loaded alongside the row id rather than after it
+            const int2 r = ni < P.n_light ? P.rng[ni] : make_int2(0, 0);
+            const SpLane<NV, RPW> lp(G, fg);
+            sp_stream<T, U, RPW>(P, lp, r.x, r.y, acc);
+            if (lp.g != 0 || !lp.act || node < 0) return;
+            store_vec<T>(P.Y, (int64_t)node * G.F + lp.col, VT::pack(acc));
+            return;
+        }
     }
     const SpLane<NV, RPW> lp(G, fg);
     const int e0 = node >= 0 ? P.indptr[node] : 0, e1 = node >= 0 ? P.indptr[node + 1] : 0;
@@ -270,11 +291,12 @@ static int launch_spmm_main(gnn_plan_t plan, const SpParams &P, int kind, hipStr
 }
 
 template <class T, bool TR>
-static int run_spmm(gnn_plan_t plan, SpParams &P, const int32_t *by_degree, hipStream_t s) {
+static int run_spmm(gnn_plan_t plan, SpParams &P, const int32_t *by_degree, const int2 *rng, hipStream_t s) {
     const int k_main = TR ? K_SPMM_T_MAIN : K_SPMM_MAIN, k_merge = TR ? K_SPMM_T_MERGE : K_SPMM_MERGE;
     if (by_degree && P.g.NFG == 1 && P.g.G >= 2) {
         SpParams Q = P;
         Q.light = by_degree;
+        Q.rng = rng;
         if (P.g.G >= 4) GNN_TRY((launch_spmm_main<T, 4, TR>(plan, Q, k_main, s)));
         else GNN_TRY((launch_spmm_main<T, 2, TR, 8>(plan, Q, k_main, s)));
     } else {
@@ -303,12 +325,28 @@ int gnn_spmm_prepare(gnn_plan_t plan, gnn_norm_t norm, hipStream_t stream) {
     if (n > 0)
         hipLaunchKernelGGL(k_spmm_w_rows, grid1d((int64_t)n * kWave), dim3(256), 0, stream, plan->indptr,
                            plan->indices, n, (int)norm, as<float>(plan->spmm_w));
+    // entry ranges of the light rows in descending-degree order (graph structure only: built once)
+    const size_t rb = (size_t)std::max(plan->fwd.n_light, 1) * sizeof(int2);
+    if (plan->spmm_rng.bytes != rb) {
+        GNN_TRY(dev_alloc(plan->spmm_rng, rb));
+        if (plan->fwd.n_light > 0)
+            hipLaunchKernelGGL(k_spmm_ranges, grid1d(plan->fwd.n_light), dim3(256), 0, stream, plan->indptr,
+                               as<int32_t>(plan->fwd.by_degree), plan->fwd.n_light, as<int2>(plan->spmm_rng));
+    }
     if (plan->has_csc) {
         if (plan->spmm_cw.bytes != bytes) GNN_TRY(dev_alloc(plan->spmm_cw, bytes));
         if (n > 0)
             hipLaunchKernelGGL(k_spmm_w_cols, grid1d((int64_t)n * kWave), dim3(256), 0, stream, plan->indptr,
                                as<int32_t>(plan->cindptr), as<int32_t>(plan->cindices), n, (int)norm,
                                as<float>(plan->spmm_cw));
+        const size_t cb = (size_t)std::max(plan->bwd.n_light, 1) * sizeof(int2);
+        if (plan->spmm_crng.bytes != cb) {
+            GNN_TRY(dev_alloc(plan->spmm_crng, cb));
+            if (plan->bwd.n_light > 0)
+                hipLaunchKernelGGL(k_spmm_ranges, grid1d(plan->bwd.n_light), dim3(256), 0, stream,
+                                   as<int32_t>(plan->cindptr), as<int32_t>(plan->bwd.by_degree), plan->bwd.n_light,
+                                   as<int2>(plan->spmm_crng));
+        }
     }
     GNN_HIP(hipGetLastError());
     plan->spmm_norm = (int32_t)norm;
@@ -351,11 +389,12 @@ int gnn_spmm(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int
         P.part = (float *)ws;
     }
     const int32_t *by_degree = as<int32_t>(b.by_degree);
+    const int2 *rng = as<int2>(transpose ? plan->spmm_crng : plan->spmm_rng);
     if (dtype == GNN_BF16)
-        return transpose ? run_spmm<bf16_tag, true>(plan, P, by_degree, stream)
-                         : run_spmm<bf16_tag, false>(plan, P, by_degree, stream);
-    return transpose ? run_spmm<float, true>(plan, P, by_degree, stream)
-                     : run_spmm<float, false>(plan, P, by_degree, stream);
+        return transpose ? run_spmm<bf16_tag, true>(plan, P, by_degree, rng, stream)
+                         : run_spmm<bf16_tag, false>(plan, P, by_degree, rng, stream);
+    return transpose ? run_spmm<float, true>(plan, P, by_degree, rng, stream)
+                     : run_spmm<float, false>(plan, P, by_degree, rng, stream);
 }
 
 }  // extern "C"
