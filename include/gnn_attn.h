@@ -186,8 +186,9 @@ typedef struct {
     int64_t workspace_bytes;    /* heavy partials and backward statistics (grows lazily) */
     int64_t largest_workspace_alloc;
     int32_t rows_sorted;        /* 1: every CSR row lists its sources in non-decreasing order */
-    const int32_t *light_by_degree; /* [n_light] light nodes by descending in-degree, ties by
-                                       ascending id (launch order 1, whatever sched_order is) */
+    const int32_t *light_by_degree; /* [n_light] light nodes in the order of the launches that pack
+                                       several rows per wave: descending ceil(in-degree / 4),
+                                       ties by ascending id (whatever sched_order is) */
     const int32_t *c_light_by_degree; /* [c_n_light] the same over out-degrees (with want_csc) */
     int32_t spmm_norm;          /* gnn_norm_t cached by gnn_spmm_prepare, -1: none          */
     const float *spmm_w;        /* [n_edges] cached SpMM weights in CSR order (or NULL)     */

@@ -460,6 +460,8 @@ __global__ void k_sched_keys(const int32_t *indptr, const int32_t *light, int32_
     uint64_t hi;
     if (order == 1) {
         hi = (uint64_t)(cap - deg);
+    } else if (order == 3) {
+        hi = (uint64_t)(cap - (deg + 3) / 4);      // descending 4-edge steps
     } else {
         int b = 0;
         while (b < 62 && (2ll << b) <= deg) ++b;   // floor(log2(deg)) for deg >= 1
@@ -492,7 +494,7 @@ static int build_sched(const int32_t *indptr, int32_t T, int64_t max_deg, int32_
     const int64_t hoist = std::max<int64_t>(1, T / 4);
     hipLaunchKernelGGL(k_sched_keys, grid1d(m), dim3(256), 0, s, indptr, as<int32_t>(b.light), b.n_light, cap,
                        sched_order, hoist, keys);
-    int rc = radix_sort(keys, kt, m, 32 + (sched_order == 1 ? bits_for(cap + 2) : 7), scr, s);
+    int rc = radix_sort(keys, kt, m, 32 + (sched_order == 1 || sched_order == 3 ? bits_for(cap + 2) : 7), scr, s);
     if (rc == GNN_OK) {
         hipLaunchKernelGGL(k_low32_i32, grid1d(m), dim3(256), 0, s, keys, m, as<int32_t>(dst));
         if (hipStreamSynchronize(s) != hipSuccess) {
@@ -552,8 +554,12 @@ int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_
             goto done;
         }
         rc = build_sched(indptr, T, (int64_t)ends[1] - ends[0], sched_order, b, b.sched, s);
+        // the packed launches' order: descending ceil(degree / 4), ties by ascending id
+        // (order 3). Rows packed into one wave then need the same number of
+        // 4- (and 8-) edge steps, and rows of one class keep their id order,
+        // so rows that share sources (a community) stay next to each other.
         if (rc == GNN_OK && by_degree)
-            rc = build_sched(indptr, T, (int64_t)ends[1] - ends[0], 1, b, b.by_degree, s);
+            rc = build_sched(indptr, T, (int64_t)ends[1] - ends[0], 3, b, b.by_degree, s);
     }
 done:
     dev_free(tmp);

@@ -157,7 +157,8 @@ def launch_order(indptr, light, order: int = 2, threshold: int = 512):
 
     order 0: the light list itself; order 1: descending degree; order 2:
     nodes of degree > max(1, threshold // 4) first, by descending
-    floor(log2(degree)), then all others; ties by ascending id."""
+    floor(log2(degree)), then all others; order 3 (the packed launches'
+    order): descending ceil(degree / 4); ties by ascending id."""
     ip = np.asarray(indptr, np.int64)
     l = np.asarray(light, np.int64)
     if order == 0:
@@ -165,6 +166,9 @@ def launch_order(indptr, light, order: int = 2, threshold: int = 512):
     deg = ip[l + 1] - ip[l]
     if order == 1:
         return l[np.lexsort((l, -deg))].astype(np.int32)
+    if order == 3:
+        steps = (deg + 3) // 4
+        return l[np.lexsort((l, -steps))].astype(np.int32)
     hoist = max(1, int(threshold) // 4)
     b = np.floor(np.log2(np.maximum(deg, 1))).astype(np.int64)
     key = np.where(deg > hoist, 63 - b, 64)

@@ -71,14 +71,14 @@ def test_buckets_and_csc(g, T, C, W, order):
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d[k], ref[k]), k
     assert np.array_equal(d["light_sched"], oracle.launch_order(rp, ref["light"], order, T))
-    assert np.array_equal(d["light_by_degree"], oracle.launch_order(rp, ref["light"], 1, T))
+    assert np.array_equal(d["light_by_degree"], oracle.launch_order(rp, ref["light"], 3, T))
     cip, cix = oracle.csc(rp, rx, n)
     assert np.array_equal(d["cindptr"], cip) and np.array_equal(d["cindices"], cix)
     cref = oracle.bucketing(cip, T, C, W)
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d["c_" + k], cref[k]), "c_" + k
     assert np.array_equal(d["c_light_sched"], oracle.launch_order(cip, cref["light"], order, T))
-    assert np.array_equal(d["c_light_by_degree"], oracle.launch_order(cip, cref["light"], 1, T))
+    assert np.array_equal(d["c_light_by_degree"], oracle.launch_order(cip, cref["light"], 3, T))
     assert d["n_light"] + d["n_heavy"] == n
 
 

@@ -220,3 +220,9 @@ def test_launch_order():
     assert oracle.launch_order(indptr, light, 2, 8).tolist() == [0, 4, 1, 3, 5]
     ip = np.array([0, 1, 9, 14, 14, 30], np.int32)            # degrees 1, 8, 5, 0, 16
     assert oracle.launch_order(ip, np.arange(5), 2, 8).tolist() == [4, 1, 2, 0, 3]
+    # order 3 (packed launches): descending ceil(degree / 4), ties by id.
+    # degrees 7, 5, 8, 4, 1, 6, 0, 9: 4-edge steps 2, 2, 2, 1, 1, 2, 0, 3
+    ip = np.concatenate([[0], np.cumsum([7, 5, 8, 4, 1, 6, 0, 9])]).astype(np.int32)
+    assert oracle.launch_order(ip, np.arange(8), 3).tolist() == [7, 0, 1, 2, 5, 3, 4, 6]
+    # strict descending degree would interleave the step-2 rows: 2, 0, 5, 1
+    assert oracle.launch_order(ip, np.arange(8), 1).tolist() == [7, 2, 0, 5, 1, 3, 4, 6]
