@@ -525,11 +525,11 @@ static int launch_red_main(gnn_plan_t plan, const RedParams &P, hipStream_t s) {
 }
 
 // Sorted rows on a plan, rows of up to 32 lanes (512 bytes): the light rows
-// run from the descending-degree list, 4 per wave (rows of up to 256 bytes)
-// or 2 per wave with 8 edges per step (up to 512 bytes, so a row keeps the
-// 8 edges per step it has alone), so rows of similar length share a wave and
-// each row merges only its own edge groups. Otherwise (wider rows, or
-// unsorted rows) one row per wave.
+// run from the packed-order list, 4 per wave (rows of up to 256 bytes) or 2
+// per wave with 10 edges per step in fp32, 8 in bf16 (up to 512 bytes, so a
+// row keeps at least the 8 edges per step it has alone), so rows of similar
+// length share a wave and each row merges only its own edge groups.
+// Otherwise (wider rows, or unsorted rows) one row per wave.
 template <class T, int OP, int MSG>
 static int run_red_fwd(gnn_plan_t plan, RedParams &P, hipStream_t s) {
     const int64_t nk = (int64_t)P.n_heavy * P.g.F;
@@ -538,8 +538,9 @@ static int run_red_fwd(gnn_plan_t plan, RedParams &P, hipStream_t s) {
         if (P.g.NFG == 1 && P.g.G >= 2) {
             RedParams Q = P;
             Q.light = as<int32_t>(plan->fwd.by_degree);
+            constexpr int U2 = Vec<T>::bytes == 4 ? 10 : 8;
             if (P.g.G >= 4) GNN_TRY((launch_red_main<T, OP, MSG, true, 4>(plan, Q, s)));
-            else GNN_TRY((launch_red_main<T, OP, MSG, true, 2, 8>(plan, Q, s)));
+            else GNN_TRY((launch_red_main<T, OP, MSG, true, 2, U2>(plan, Q, s)));
         } else {
             GNN_TRY((launch_red_main<T, OP, MSG, true, 1>(plan, P, s)));
         }

@@ -15,9 +15,9 @@
 //
 // The product uses the degree-aware layout of the other kernels: a lane holds
 // one 16-byte slice of a feature row; light rows run from the
-// descending-degree list 4 per wave when a row spans at most 16 lanes
-// (256 bytes), 2 per wave with 8 edges per step when it spans 17-32 lanes
-// (512 bytes), else one per wave; the packed waves read each row's entry
+// packed-order list 4 per wave when a row spans at most 16 lanes
+// (256 bytes), 2 per wave with 10 edges per step in fp32 (8 in bf16) when it
+// spans 17-32 lanes (512 bytes), else one per wave; the packed waves read each row's entry
 // range from a record cached by gnn_spmm_prepare, alongside the row id
 // (rows are short: one dependent load fewer before the gathers); heavy rows run as the plan's chunk groups, their W waves
 // summed in LDS and the groups summed in ascending order by a second pass.
@@ -297,8 +297,11 @@ static int run_spmm(gnn_plan_t plan, SpParams &P, const int32_t *by_degree, cons
         SpParams Q = P;
         Q.light = by_degree;
         Q.rng = rng;
+        // two rows per wave: 10 entries per step in fp32 (on the mean-degree-8 power-law
+        // graph 9, 11 and 12 measured slower, and 8 slower still), 8 in bf16
+        constexpr int U2 = Vec<T>::bytes == 4 ? 10 : 8;
         if (P.g.G >= 4) GNN_TRY((launch_spmm_main<T, 4, TR>(plan, Q, k_main, s)));
-        else GNN_TRY((launch_spmm_main<T, 2, TR, 8>(plan, Q, k_main, s)));
+        else GNN_TRY((launch_spmm_main<T, 2, TR, U2>(plan, Q, k_main, s)));
     } else {
         GNN_TRY((launch_spmm_main<T, 1, TR>(plan, P, k_main, s)));
     }
