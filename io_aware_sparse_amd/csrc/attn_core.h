@@ -202,7 +202,7 @@ __device__ __forceinline__ void write_out(const FwdParams &P, const LanePos &lp,
     float o[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) o[k] = st.acc[k] * inv;
-    store_vec<T>(P.O, (int64_t)node * rowlen + lp.col, VT::pack(o));
+    store_vec_nt<T>(P.O, (int64_t)node * rowlen + lp.col, VT::pack(o));
     if (P.LSE && lp.dv == 0)
         P.LSE[(int64_t)node * P.g.H + lp.h] = st.l > 0.f ? (st.m + fast_log2(st.l)) * kLn2 : kNegInf;
 }
@@ -243,7 +243,7 @@ __device__ __forceinline__ void store_scaled(void *base, int64_t off, const floa
     float o[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) o[k] = x[k] * sc;
-    store_vec<T>(base, off, Vec<T>::pack(o));
+    store_vec_nt<T>(base, off, Vec<T>::pack(o));
 }
 
 // Destination side over edges [e0, e1) of `node`. With p = exp(s - LSE) and

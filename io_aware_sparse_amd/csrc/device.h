@@ -140,4 +140,15 @@ __device__ __forceinline__ void store_vec(void *base, int64_t elem_off, const ty
     *reinterpret_cast<raw *>(reinterpret_cast<char *>(base) + elem_off * Vec<T>::bytes) = v;
 }
 
+// the same 16-byte store with the non-temporal hint (a streamed output row that
+// the kernel does not read back, so it need not displace gathered rows in L2)
+template <class T>
+__device__ __forceinline__ void store_vec_nt(void *base, int64_t elem_off, const typename Vec<T>::raw &v) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    static_assert(sizeof(typename Vec<T>::raw) == sizeof(u4), "16-byte vectors");
+    u4 x;
+    __builtin_memcpy(&x, &v, sizeof(x));
+    __builtin_nontemporal_store(x, reinterpret_cast<u4 *>(reinterpret_cast<char *>(base) + elem_off * Vec<T>::bytes));
+}
+
 }  // namespace gnn

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(512) void k_spmm_main(SpParams P) {
             const SpLane<NV, RPW> lp(G, fg);
             sp_stream<T, U, RPW>(P, lp, r.x, r.y, acc);
             if (lp.g != 0 || !lp.act || node < 0) return;
-            store_vec<T>(P.Y, (int64_t)node * G.F + lp.col, VT::pack(acc));
+            store_vec_nt<T>(P.Y, (int64_t)node * G.F + lp.col, VT::pack(acc));
             return;
         }
     }
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(512) void k_spmm_main(SpParams P) {
     const int e0 = node >= 0 ? P.indptr[node] : 0, e1 = node >= 0 ? P.indptr[node + 1] : 0;
     sp_stream<T, U, RPW>(P, lp, e0, e1, acc);
     if (lp.g != 0 || !lp.act || node < 0) return;
-    store_vec<T>(P.Y, (int64_t)node * G.F + lp.col, VT::pack(acc));
+    store_vec_nt<T>(P.Y, (int64_t)node * G.F + lp.col, VT::pack(acc));
 }
 
 // heavy rows: the groups' partials summed in ascending group order
