@@ -193,6 +193,10 @@ typedef struct {
     int32_t spmm_norm;          /* gnn_norm_t cached by gnn_spmm_prepare, -1: none          */
     const float *spmm_w;        /* [n_edges] cached SpMM weights in CSR order (or NULL)     */
     const float *spmm_cw;       /* [n_edges] the same in transposed-adjacency order (or NULL) */
+    int32_t n_long_light;       /* light nodes of in-degree above 128: the first entries of
+                                   light_by_degree, each given a wave of its own by the packed
+                                   SpMM launches */
+    int32_t c_n_long_light;     /* the same over out-degrees and c_light_by_degree (want_csc) */
 } gnn_plan_info;
 
 int gnn_plan_export(gnn_plan_t plan, gnn_plan_info *info /*host*/);

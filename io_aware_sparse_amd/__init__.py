@@ -72,7 +72,8 @@ class PlanInfo(C.Structure):
                 ("structure_bytes", C.c_int64), ("workspace_bytes", C.c_int64),
                 ("largest_workspace_alloc", C.c_int64), ("rows_sorted", C.c_int32),
                 ("light_by_degree", C.c_void_p), ("c_light_by_degree", C.c_void_p), ("spmm_norm", C.c_int32),
-                ("spmm_w", C.c_void_p), ("spmm_cw", C.c_void_p)]
+                ("spmm_w", C.c_void_p), ("spmm_cw", C.c_void_p),
+                ("n_long_light", C.c_int32), ("c_n_long_light", C.c_int32)]
 
 
 _lib = None

@@ -54,10 +54,18 @@ struct Buckets {
     // launch order of the light list, as gnn_plan_opts::sched_order asks (order
     // 0 is a copy of the light list); kernel results do not depend on it
     DevBuf sched;
-    // the light list by descending degree, ties by ascending id (launch
-    // order 1), for kernels that pack several rows per wave
+    // the light list in the packed launch order (descending ceil(degree / 4),
+    // ties by ascending id), for kernels that pack several rows per wave
     DevBuf by_degree;
+    // light rows of more than kLongRow entries; in the packed order they are
+    // the first n_long entries of by_degree
+    int32_t n_long = 0;
 };
+
+// A light row longer than this gets a wave of its own in the packed SpMM
+// launches rather than a share of one (a packed row steps through its entries
+// a few at a time, so the longest rows would set the kernel's duration).
+constexpr int32_t kLongRow = 128;
 
 // Per-kernel timing log.
 struct TimingRec {

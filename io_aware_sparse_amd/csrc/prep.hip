@@ -417,15 +417,22 @@ __global__ void k_transpose_keys(const int32_t *indptr, const int32_t *indices, 
 
 // ---------------------------------------------------------------- buckets
 
+// n_long (zeroed beforehand) counts the light rows of more than kLongRow
+// entries: one atomic add per wave
 __global__ void k_bucket_flags(const int32_t *indptr, int32_t n, int32_t T, int64_t span, int32_t *fl,
-                               int32_t *fh, int32_t *ng) {
+                               int32_t *fh, int32_t *ng, int32_t *n_long) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int64_t deg = (int64_t)indptr[i + 1] - indptr[i];
-    const bool heavy = deg > T;
-    fl[i] = heavy ? 0 : 1;
-    fh[i] = heavy ? 1 : 0;
-    ng[i] = heavy ? (int32_t)((deg + span - 1) / span) : 0;
+    bool is_long = false;
+    if (i < n) {
+        const int64_t deg = (int64_t)indptr[i + 1] - indptr[i];
+        const bool heavy = deg > T;
+        fl[i] = heavy ? 0 : 1;
+        fh[i] = heavy ? 1 : 0;
+        ng[i] = heavy ? (int32_t)((deg + span - 1) / span) : 0;
+        is_long = !heavy && deg > kLongRow;
+    }
+    const uint64_t m = __ballot(is_long);
+    if (m && lane_id() == 0) atomicAdd(n_long, (int32_t)__popcll(m));
 }
 
 __global__ void k_bucket_emit(const int32_t *indptr, int32_t n, int32_t T, int64_t span, const int32_t *lpos,
@@ -511,13 +518,14 @@ int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_
     const int64_t span = (int64_t)C * W;
     DevBuf tmp;
     const int64_t sc = scan_scratch(n);
-    GNN_TRY(dev_alloc(tmp, (size_t)(6 * (int64_t)n + 3 + sc) * 4));
+    GNN_TRY(dev_alloc(tmp, (size_t)(6 * (int64_t)n + 4 + sc) * 4));
     int32_t *fl = as<int32_t>(tmp), *fh = fl + n, *ng = fh + n, *lpos = ng + n, *hpos = lpos + n,
-            *gofs = hpos + n, *tot = gofs + n, *scr = tot + 3;
+            *gofs = hpos + n, *tot = gofs + n, *scr = tot + 4;
     int rc = GNN_OK;
-    int32_t h_tot[3] = {0, 0, 0};
+    int32_t h_tot[4] = {0, 0, 0, 0};
     if (n > 0) {
-        hipLaunchKernelGGL(k_bucket_flags, grid1d(n), dim3(256), 0, s, indptr, n, T, span, fl, fh, ng);
+        hipLaunchKernelGGL(k_set_i32, dim3(1), dim3(1), 0, s, tot + 3, 0);
+        hipLaunchKernelGGL(k_bucket_flags, grid1d(n), dim3(256), 0, s, indptr, n, T, span, fl, fh, ng, tot + 3);
         if ((rc = scan_rec(fl, lpos, n, tot + 0, scr, s)) != GNN_OK) goto done;
         if ((rc = scan_rec(fh, hpos, n, tot + 1, scr, s)) != GNN_OK) goto done;
         if ((rc = scan_rec(ng, gofs, n, tot + 2, scr, s)) != GNN_OK) goto done;
@@ -531,6 +539,7 @@ int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_
     b.n_light = h_tot[0];
     b.n_heavy = h_tot[1];
     b.n_groups = h_tot[2];
+    b.n_long = h_tot[3];
     if ((rc = dev_alloc(b.light, (size_t)std::max(1, b.n_light) * 4)) != GNN_OK) goto done;
     if ((rc = dev_alloc(b.heavy, (size_t)std::max(1, b.n_heavy) * 4)) != GNN_OK) goto done;
     if ((rc = dev_alloc(b.partial_ofs, (size_t)(b.n_heavy + 1) * 4)) != GNN_OK) goto done;
@@ -870,6 +879,8 @@ int gnn_plan_export(gnn_plan_t p, gnn_plan_info *info) {
     info->spmm_norm = p->spmm_norm;
     info->spmm_w = as<float>(p->spmm_w);
     info->spmm_cw = as<float>(p->spmm_cw);
+    info->n_long_light = p->fwd.n_long;
+    info->c_n_long_light = p->bwd.n_long;
     return GNN_OK;
 }
 

@@ -19,7 +19,11 @@
 // (256 bytes), 2 per wave with 10 edges per step in fp32 (8 in bf16) when it
 // spans 17-32 lanes (512 bytes), else one per wave; the packed waves read each row's entry
 // range from a record cached by gnn_spmm_prepare, alongside the row id
-// (rows are short: one dependent load fewer before the gathers); heavy rows run as the plan's chunk groups, their W waves
+// (rows are short: one dependent load fewer before the gathers). The light
+// rows of more than 128 entries, which head the packed list, get a wave each
+// in the same launch (all its edge groups on one row), so the longest light
+// rows take half or a quarter of the steps they would take packed; heavy
+// rows run as the plan's chunk groups, their W waves
 // summed in LDS and the groups summed in ascending order by a second pass.
 // fp32 accumulation, output rounded to the storage type; no atomics, so the
 // result is bitwise reproducible. The transposed product (dX = A_w^T dY) is
@@ -92,6 +96,7 @@ struct SpParams {
     const int32_t *light;
     const int2 *rng;                   // entry range of each entry of `light` (packed launches), or null
     int32_t n_light;
+    int32_t n_long;                    // packed launches: the first n_long rows get a wave each
     const int32_t *groups;
     int32_t n_groups;
     const int32_t *heavy, *partial_ofs;
@@ -220,7 +225,17 @@ __global__ __launch_bounds__(512) void k_spmm_main(SpParams P) {
         fg = (int)(item % G.NFG);
         node = P.light ? P.light[ni] : (int)ni;
     } else {
-        const int64_t ni0 = item * RPW;
+        if (item < P.n_long) {
+            // a long row at the head of the packed list: the whole wave, all its edge groups
+            node = P.light[item];
+            const int2 r = P.rng[item];
+            const SpLane<NV, 1> lp(G, 0);
+            sp_stream<T, U, 1>(P, lp, r.x, r.y, acc);
+            if (lp.g != 0 || !lp.act) return;
+            store_vec_nt<T>(P.Y, (int64_t)node * G.F + lp.col, VT::pack(acc));
+            return;
+        }
+        const int64_t ni0 = P.n_long + (item - P.n_long) * RPW;
         if (ni0 >= P.n_light) return;
         const int64_t ni = ni0 + (lane_id() / (kWave / RPW));
         node = ni < P.n_light ? P.light[ni] : -1;
@@ -283,7 +298,8 @@ static SpGeom sp_geom(int32_t N, int32_t F, gnn_dtype_t dt) {
 template <class T, int RPW, bool TR, int U = 4>
 static int launch_spmm_main(gnn_plan_t plan, const SpParams &P, int kind, hipStream_t s) {
     constexpr int NV = Vec<T>::N;
-    const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NFG : ((int64_t)P.n_light + RPW - 1) / RPW;
+    const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NFG
+                                         : P.n_long + ((int64_t)P.n_light - P.n_long + RPW - 1) / RPW;
     const int64_t blocks = (int64_t)P.n_groups * P.g.NFG + (light_waves + P.W - 1) / P.W;
     if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
     const size_t lds = P.n_groups ? (size_t)P.W * (1 << P.g.lr_shift) * NV * sizeof(float) : 0;
@@ -291,12 +307,14 @@ static int launch_spmm_main(gnn_plan_t plan, const SpParams &P, int kind, hipStr
 }
 
 template <class T, bool TR>
-static int run_spmm(gnn_plan_t plan, SpParams &P, const int32_t *by_degree, const int2 *rng, hipStream_t s) {
+static int run_spmm(gnn_plan_t plan, SpParams &P, const int32_t *by_degree, const int2 *rng, int32_t n_long,
+                    hipStream_t s) {
     const int k_main = TR ? K_SPMM_T_MAIN : K_SPMM_MAIN, k_merge = TR ? K_SPMM_T_MERGE : K_SPMM_MERGE;
     if (by_degree && P.g.NFG == 1 && P.g.G >= 2) {
         SpParams Q = P;
         Q.light = by_degree;
         Q.rng = rng;
+        Q.n_long = rng ? n_long : 0;
         // two rows per wave: 10 entries per step in fp32 (on the mean-degree-8 power-law
         // graph 9, 11 and 12 measured slower, and 8 slower still), 8 in bf16
         constexpr int U2 = Vec<T>::bytes == 4 ? 10 : 8;
@@ -394,10 +412,10 @@ int gnn_spmm(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int
     const int32_t *by_degree = as<int32_t>(b.by_degree);
     const int2 *rng = as<int2>(transpose ? plan->spmm_crng : plan->spmm_rng);
     if (dtype == GNN_BF16)
-        return transpose ? run_spmm<bf16_tag, true>(plan, P, by_degree, rng, stream)
-                         : run_spmm<bf16_tag, false>(plan, P, by_degree, rng, stream);
-    return transpose ? run_spmm<float, true>(plan, P, by_degree, rng, stream)
-                     : run_spmm<float, false>(plan, P, by_degree, rng, stream);
+        return transpose ? run_spmm<bf16_tag, true>(plan, P, by_degree, rng, b.n_long, stream)
+                         : run_spmm<bf16_tag, false>(plan, P, by_degree, rng, b.n_long, stream);
+    return transpose ? run_spmm<float, true>(plan, P, by_degree, rng, b.n_long, stream)
+                     : run_spmm<float, false>(plan, P, by_degree, rng, b.n_long, stream);
 }
 
 }  // extern "C"

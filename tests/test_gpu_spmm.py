@@ -86,6 +86,51 @@ def test_spmm_parity(g, dtype, F, plan_kind):
             assert np.array_equal(host(Y2), host(Y)), "not reproducible"
 
 
+@pytest.mark.parametrize("dtype,F", [("f32", 128), ("f32", 64), ("bf16", 128), ("bf16", 256)])
+@pytest.mark.parametrize("threshold", [512, 200])
+def test_spmm_long_light_rows(g, dtype, F, threshold):
+    """Light rows of more than 128 entries head the packed order and get a wave
+    each (2 or 4 rows per wave for the rest): rows of 100-700 entries and 150
+    popular sources put such rows on both sides of 128 and of the light
+    threshold, in the product and in the transposed product."""
+    rng = np.random.default_rng(F + threshold)
+    n = 3000
+    deg = rng.poisson(6, n)
+    deg[rng.choice(n, 200, replace=False)] = rng.integers(100, 700, 200)
+    popular = rng.choice(n, 150, replace=False)
+    rows = []
+    for d in deg:
+        src = rng.integers(0, n, d)
+        pick = rng.random(d) < 0.3
+        src[pick] = popular[rng.integers(0, popular.size, int(pick.sum()))]
+        rows.append(np.sort(src))
+    ip = np.concatenate([[0], np.cumsum(deg)]).astype(np.int32)
+    ix = np.concatenate(rows).astype(np.int32)
+    indeg, outdeg = np.diff(ip), np.bincount(ix, minlength=n)
+    X = _feats(rng, n, F, dtype)
+    ip_d, ix_d = dev_i32(ip), dev_i32(ix)
+    plan = g.gnn_plan_create(ip_d, ix_d, light_threshold=threshold, want_csc=True)
+    d = g.gnn_plan_export(plan, arrays=True)
+    n_long = int(((indeg > 128) & (indeg <= threshold)).sum())
+    c_n_long = int(((outdeg > 128) & (outdeg <= threshold)).sum())
+    say(f"n={n} E={ip[-1]} threshold={threshold}: {n_long} long light rows, {c_n_long} long light sources")
+    assert n_long > 0 and c_n_long > 0
+    assert d["n_long_light"] == n_long and d["c_n_long_light"] == c_n_long
+    assert np.all(indeg[d["light_by_degree"][:n_long]] > 128)          # the head of the packed order
+    assert np.all(indeg[d["light_by_degree"][n_long:]] <= 128)
+    assert np.all(outdeg[d["c_light_by_degree"][:c_n_long]] > 128)
+    Xd = dev_feat(X, dtype)
+    for norm in ("gcn", "sum"):
+        g.gnn_spmm_prepare(plan, norm)
+        for tr in (False, True):
+            Y = g.gnn_spmm(plan, ip_d, ix_d, Xd, transpose=tr)
+            ref = oracle.spmm(ip, ix, X, norm, transpose=tr)
+            check(f"spmm long rows {dtype} F={F} T={threshold} {norm} transpose={tr}", host(Y), ref["Y"],
+                  ref["S"], dtype)
+            Y2 = g.gnn_spmm(plan, ip_d, ix_d, Xd, transpose=tr)
+            assert np.array_equal(host(Y2), host(Y)), "not reproducible"
+
+
 def test_spmm_errors_and_empty(g):
     import torch
     rng = np.random.default_rng(3)
