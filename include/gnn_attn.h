@@ -195,7 +195,7 @@ typedef struct {
     const float *spmm_cw;       /* [n_edges] the same in transposed-adjacency order (or NULL) */
     int32_t n_long_light;       /* light nodes of in-degree above 128: the first entries of
                                    light_by_degree, each given a wave of its own by the packed
-                                   SpMM launches */
+                                   SpMM and attention-forward launches */
     int32_t c_n_long_light;     /* the same over out-degrees and c_light_by_degree (want_csc) */
 } gnn_plan_info;
 

@@ -80,7 +80,17 @@ __global__ __launch_bounds__(512) void k_fwd_main(FwdParams P) {
     const int64_t lblock = blockIdx.x - heavy_blocks;
     const int64_t item = (RPW > 1 ? lblock : xcd_block(lblock, gridDim.x - heavy_blocks)) * P.W + w;
     if (RPW > 1) {                        // RPW rows of the light list per wave (NHG == 1)
-        const int64_t ni0 = item * RPW;
+        if (item < P.n_long) {
+            // a long row at the head of the packed list: the whole wave, all its edge groups
+            const int node = P.light[item];
+            const int e0 = P.indptr[node], e1 = P.indptr[node + 1];
+            const LanePos lp = lane_pos<LH, NV>(P.g, 0);
+            SoftState<NV> st;
+            fwd_stream<T, LH, MODE, U>(P, lp, node, e0, e1, st);
+            write_out<T, NV>(P, lp, node, st);
+            return;
+        }
+        const int64_t ni0 = P.n_long + (item - P.n_long) * RPW;
         if (ni0 >= P.n_light) return;
         const int64_t ni = ni0 + lane_id() / (kWave / RPW);
         const int node = ni < P.n_light ? P.light[ni] : -1;
@@ -300,7 +310,8 @@ template <class T, int LH, int MODE, int U, int RPW>
 static int launch_fwd_main(gnn_plan_t plan, const FwdParams &P, hipStream_t s) {
     constexpr int NV = Vec<T>::N;
     const int kind_main = MODE == M_GT ? K_FWD_MAIN : K_GAT_MAIN;
-    const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NHG : ((int64_t)P.n_light + RPW - 1) / RPW;
+    const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NHG
+                                         : P.n_long + ((int64_t)P.n_light - P.n_long + RPW - 1) / RPW;
     const int64_t blocks = (int64_t)P.n_groups * P.g.NHG + (light_waves + P.W - 1) / P.W;
     if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
     const size_t lds = P.n_groups ? (size_t)P.W * (1 << P.g.lr_shift) * (NV + 2) * sizeof(float) : 0;
@@ -309,16 +320,19 @@ static int launch_fwd_main(gnn_plan_t plan, const FwdParams &P, hipStream_t s) {
 }
 
 // Light rows of 257-512 bytes (two edge groups per wave) on a plan run from
-// the descending-degree list, 2 per wave with 8 edges per step, so each row
+// the packed-order list, 2 per wave with 8 edges per step, so each row
 // keeps the edges per step it would have alone and a wave has twice the
-// rows in flight; otherwise one (row, head group) per wave, 4 edges per
-// group and step.
+// rows in flight; the rows of more than 128 edges at the head of that list
+// take a wave each (both edge groups, 16 edges per step), so the longest
+// light rows do not set the kernel's duration. Otherwise one (row, head
+// group) per wave, 4 edges per group and step.
 template <class T, int LH, int MODE>
 static int run_fwd(gnn_plan_t plan, FwdParams &P, const int32_t *by_degree, hipStream_t s) {
     const int kind_merge = MODE == M_GT ? K_FWD_MERGE : K_GAT_MERGE;
     if (by_degree && P.g.NHG == 1 && P.g.G == 2) {
         FwdParams Q = P;
         Q.light = by_degree;
+        Q.n_long = plan->fwd.n_long;
         GNN_TRY((launch_fwd_main<T, LH, MODE, 8, 2>(plan, Q, s)));
     } else {
         GNN_TRY((launch_fwd_main<T, LH, MODE, 4, 1>(plan, P, s)));

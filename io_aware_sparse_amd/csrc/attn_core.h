@@ -34,6 +34,7 @@ struct FwdParams {
     float slope, mul;   // mul: score multiplier into log2 units
     const int32_t *light;
     int32_t n_light;
+    int32_t n_long;     // packed launches: the first n_long rows of `light` get a wave each
     const int32_t *groups;
     int32_t n_groups, C;
     const int32_t *heavy, *partial_ofs;

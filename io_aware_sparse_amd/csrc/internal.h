@@ -62,9 +62,10 @@ struct Buckets {
     int32_t n_long = 0;
 };
 
-// A light row longer than this gets a wave of its own in the packed SpMM
-// launches rather than a share of one (a packed row steps through its entries
-// a few at a time, so the longest rows would set the kernel's duration).
+// A light row longer than this gets a wave of its own in the packed SpMM and
+// attention-forward launches rather than a share of one (a packed row steps
+// through its entries a few at a time, so the longest rows would set the
+// kernel's duration).
 constexpr int32_t kLongRow = 128;
 
 // Per-kernel timing log.
