@@ -78,6 +78,9 @@ def test_buckets_and_csc(g, T, C, W, order):
     for k in ("light", "heavy", "groups", "partial_ofs"):
         assert np.array_equal(d["c_" + k], cref[k]), "c_" + k
     assert np.array_equal(d["c_light_sched"], oracle.launch_order(cip, cref["light"], order, T))
+    # the long light rows (a wave each in the packed launches) head the packed order
+    assert d["n_long_light"] == int((np.diff(rp)[ref["light"]] > 128).sum())
+    assert d["c_n_long_light"] == int((np.diff(cip)[cref["light"]] > 128).sum())
     assert np.array_equal(d["c_light_by_degree"], oracle.launch_order(cip, cref["light"], 3, T))
     assert d["n_light"] + d["n_heavy"] == n
 
@@ -145,3 +148,47 @@ def test_tile_census(g, case, tau, T):
     n_pop = int(sum(bin(int(w)).count("1") for w in d["tile_mask"].ravel()))
     assert n_pop + d["n_residual"] == rx.size
     say(f"  tiles {d['n_tiles']} residual {d['n_residual']} of {rx.size}")
+
+
+def _bits(t):
+    return t.contiguous().view(-1).view(__import__("torch").uint8).cpu()
+
+
+@pytest.mark.parametrize("dtype,H,D,F", [("f32", 4, 64, 256), ("bf16", 8, 64, 512)])
+def test_results_do_not_depend_on_launch_order(g, dtype, H, D, F):
+    """The launch order of the light list only schedules work: each light row
+    is computed by one wave on its own, so every output of every kernel family
+    (GT forward and backward, GATv2 forward and backward, the max reduction and
+    its gradient, both SpMM products) is bit for bit the same under launch
+    orders 0, 1 and 2. Rows of 1 KiB run one per wave, from the launch order;
+    a small threshold and chunk put hubs on the heavy path as well."""
+    import torch
+    wl = workloads.make("gatv2_zipf21_n100k", 12000, features=False)
+    n = wl.n_nodes
+    ip, ix, rp, rx = _csr_case(g, wl.src, wl.dst, n, True)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    rnd = lambda *shape: torch.randn(*shape, generator=gen).to(dt).cuda()
+    Q, K, V, dO = rnd(n, H, D), rnd(n, H, D), rnd(n, H, D), rnd(n, H, D)
+    att = torch.randn(H, D, generator=gen).cuda()
+    X, dY = rnd(n, F), rnd(n, F)
+    outs = []
+    for order in (0, 1, 2):
+        say("launch order", order, dtype, H, D, F)
+        plan = g.gnn_plan_create(ip, ix, light_threshold=96, chunk=64, want_csc=True, sched_order=order)
+        O, LSE = g.gnn_attn_fwd(plan, ip, ix, Q, K, V)
+        r = [O, LSE, *g.gnn_attn_bwd(plan, ip, ix, Q, K, V, O, dO, LSE)]
+        GO, GL = g.gatv2_attn_fwd(plan, ip, ix, Q, K, att)
+        r += [GO, GL] + [t for t in g.gatv2_attn_bwd(plan, ip, ix, Q, K, att, dO, GL) if t is not None]
+        R, arg = g.gnn_reduce_fwd(plan, ip, ix, X)
+        r += [R, arg, g.gnn_reduce_bwd(plan, ip, ix, dY, arg)]
+        g.gnn_spmm_prepare(plan, "gcn")
+        r += [g.gnn_spmm(plan, ip, ix, X), g.gnn_spmm(plan, ip, ix, X, transpose=True)]
+        torch.cuda.synchronize()
+        outs.append([_bits(t) for t in r])
+    names = ["O", "LSE", "dQ", "dK", "dV", "gatv2 O", "gatv2 LSE", "dXD", "dXS", "d_att", "max", "argmax",
+             "max grad", "spmm", "spmm transposed"]
+    assert len(outs[0]) == len(names)
+    for order, o in ((1, outs[1]), (2, outs[2])):
+        for nm, a, b in zip(names, outs[0], o):
+            assert torch.equal(a, b), f"{nm} differs between launch orders 0 and {order}"
