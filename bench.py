@@ -178,6 +178,10 @@ def kernel_bytes(kind, c, H, D, s, v_alias=True):
     ts, tse = c.get("tile_srcs", 0), c.get("tile_res_src_edges", 0)
     if kind == "gt_tile_bwd_src":     # tiles: Q, dO blocks + 16 row stats; sources: K, V in, dK, dV out
         return 40 * t + (32 * R + 16 * 8 * H) * t + 4 * (ts + 1) + (4 + 2 * R + 8 * H) * tse + 4 * R * ts
+    if kind == "spmm_wsb":            # tiles: mask, X block, 16 degrees; rows: residual range, degree, Y out;
+        return 40 * t + (16 * rsz + 128) * t + 4 * (tr + 1) + 8 * tr + (8 + rsz) * te + rsz * tr  # residual entries
+    if kind == "spmm_t_wsb":          # the same by column block over the transposed residual
+        return 40 * t + (16 * rsz + 128) * t + 4 * (ts + 1) + 8 * ts + (8 + rsz) * tse + rsz * ts
     return 0
 
 
@@ -204,7 +208,7 @@ def gathered_tables(kind, H, D, s, N, v_alias=True):
         return 2 * R * N, R
     if kind in ("gatv2_fwd_main", "gatv2_bwd_dst_main"):
         return (1 if v_alias else 2) * R * N, R
-    if kind in ("reduce_fwd_main", "spmm_main", "spmm_t_main"):
+    if kind in ("reduce_fwd_main", "spmm_main", "spmm_t_main", "spmm_wsb", "spmm_t_wsb"):
         return R * N, R
     if kind == "reduce_bwd_main":                 # dOut rows and winner rows (int32 per feature)
         return (R + F4) * N, R
@@ -766,7 +770,10 @@ def bench(args) -> int:
     value = E / (ms_step * 1e-3) / 1e9
 
     v_alias = True
-    tiled = bool(info["has_tiles"]) and wl.dtype == "bf16" and D in (32, 64, 128) and wl.kind == "gt"
+    if wl.kind == "spmm":             # the block kernel serves rows of whole 16-feature chunks, <= 256 bytes
+        tiled = bool(info["has_tiles"]) and (H * D) % 16 == 0 and H * D * s <= 256
+    else:
+        tiled = bool(info["has_tiles"]) and wl.dtype == "bf16" and D in (32, 64, 128) and wl.kind == "gt"
     counts = step_counts(g.gnn_plan_export(plan, arrays=True), indptr.cpu().numpy(), indices.cpu().numpy(), tiled)
     counts["msg"] = args.msg
     kernels = {}

@@ -53,9 +53,17 @@ int gnn_spmm_prepare(gnn_plan_t plan, gnn_norm_t norm, hipStream_t stream);
  * fp32 accumulation in a fixed order (no atomics: bitwise reproducible), Y
  * rounded to the storage type (nearest even). Heavy rows use n_groups * F * 4
  * bytes of plan workspace.
+ * On a plan created with tile_density > 0 (a 16x16 tile census), when F is a
+ * multiple of 16 and a row is at most 256 bytes, the tiled 16-row blocks
+ * (16-column blocks for the transpose) run on the block kernel: the tiles'
+ * products on the matrix cores in fp32 (weights from the in-degrees, the
+ * same expression as the cached ones), then the blocks' residual entries
+ * with cached weights (gnn_spmm_prepare caches them for tiled plans, 4 bytes
+ * per residual entry and order); other rows run as above.
  * Source: technical summary, Methodology, SpMM-based convolutions (the
  * aggregation of H' = sigma(A H W); the transposed adjacency precomputed for
- * the backward pass).
+ * the backward pass; the Weighted Block Sparse option for the matrix units
+ * on locally dense graphs).
  */
 int gnn_spmm(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
              const void *X, void *Y, int32_t transpose, gnn_dtype_t dtype, hipStream_t stream);

@@ -100,6 +100,8 @@ enum KernelKind {
     K_SPMM_MERGE,
     K_SPMM_T_MAIN,
     K_SPMM_T_MERGE,
+    K_SPMM_WSB,
+    K_SPMM_T_WSB,
     K_NUM_KINDS
 };
 extern const char *kKernelNames[K_NUM_KINDS];
@@ -141,6 +143,9 @@ struct gnn_plan_s {
     // without first reading the row ids
     int32_t spmm_norm = -1;
     gnn::DevBuf spmm_w, spmm_cw, spmm_rng, spmm_crng;
+    // tiled plans: cached weights of the residual entries (residual CSR order;
+    // transposed-residual order with the transpose)
+    gnn::DevBuf spmm_rw, spmm_rcw;
     // workspace (heavy partials, backward statistics), grows on demand
     gnn::DevBuf ws;
     int64_t largest_ws = 0;

@@ -79,7 +79,7 @@ const char *kKernelNames[K_NUM_KINDS] = {
     "gt_bwd_dst_merge", "gt_bwd_src_main", "gt_bwd_src_merge", "gt_tile_fwd", "gt_tile_bwd_dst", "gt_tile_bwd_src",
     "gatv2_bwd_dst_main", "gatv2_bwd_dst_merge", "gatv2_bwd_src_main", "gatv2_bwd_src_merge", "gatv2_bwd_datt",
     "reduce_fwd_init", "reduce_fwd_main", "reduce_fwd_final", "reduce_bwd_main", "reduce_bwd_merge",
-    "spmm_main", "spmm_merge", "spmm_t_main", "spmm_t_merge"};
+    "spmm_main", "spmm_merge", "spmm_t_main", "spmm_t_merge", "spmm_wsb", "spmm_t_wsb"};
 
 hipEvent_t Timer::get() {
     if (!pool.empty()) {
@@ -678,7 +678,7 @@ std::vector<DevBuf *> gnn_plan_s::structures() {
     return {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &fwd.sched, &fwd.by_degree, &cindptr, &cindices,
             &bwd.light, &bwd.heavy, &bwd.groups, &bwd.partial_ofs, &bwd.sched, &bwd.by_degree, &tile_rc, &tile_mask,
             &tile_ptr, &trb, &rindptr, &rindices, &light_nt, &ctile, &ctile_ptr, &tcb, &rcindptr, &rcindices,
-            &c_light_nt, &spmm_w, &spmm_cw, &spmm_rng, &spmm_crng};
+            &c_light_nt, &spmm_w, &spmm_cw, &spmm_rng, &spmm_crng, &spmm_rw, &spmm_rcw};
 }
 
 int64_t gnn_plan_s::structure_bytes() {

@@ -38,6 +38,17 @@
 
 namespace gnn {
 
+// weight of entry (destination i, source j) from their in-degrees
+__device__ __forceinline__ float spmm_weight(int norm, float di, float dj) {
+    if (norm == GNN_NORM_MEAN) return 1.f / di;
+    if (norm == GNN_NORM_GCN) return dj > 0.f ? 1.f / sqrtf(di * dj) : 0.f;   // a source without entries: nothing
+    return 1.f;
+}
+
+__device__ __forceinline__ float in_degree(const int32_t *indptr, int32_t v) {
+    return (float)(indptr[v + 1] - indptr[v]);
+}
+
 // weights in CSR order: one wave per row
 __global__ void k_spmm_w_rows(const int32_t *indptr, const int32_t *indices, int32_t n, int norm, float *w) {
     const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
@@ -45,16 +56,8 @@ __global__ void k_spmm_w_rows(const int32_t *indptr, const int32_t *indices, int
     if (i >= n) return;
     const int32_t e0 = indptr[i], e1 = indptr[i + 1];
     const float di = (float)(e1 - e0);
-    for (int32_t e = e0 + lane; e < e1; e += kWave) {
-        float v = 1.f;
-        if (norm == GNN_NORM_MEAN) v = 1.f / di;
-        if (norm == GNN_NORM_GCN) {
-            const int32_t j = indices[e];
-            const float dj = (float)(indptr[j + 1] - indptr[j]);
-            v = dj > 0.f ? 1.f / sqrtf(di * dj) : 0.f;      // a source without entries contributes nothing
-        }
-        w[e] = v;
-    }
+    for (int32_t e = e0 + lane; e < e1; e += kWave)
+        w[e] = spmm_weight(norm, di, norm == GNN_NORM_GCN ? in_degree(indptr, indices[e]) : 0.f);
 }
 
 // weights in transposed order: the entries of source j name destinations i
@@ -63,14 +66,23 @@ __global__ void k_spmm_w_cols(const int32_t *indptr, const int32_t *cindptr, con
     const int64_t j = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
     const int lane = threadIdx.x % kWave;
     if (j >= n) return;
-    const float dj = (float)(indptr[j + 1] - indptr[j]);
-    for (int32_t e = cindptr[j] + lane; e < cindptr[j + 1]; e += kWave) {
-        const int32_t i = cindices[e];
-        const float di = (float)(indptr[i + 1] - indptr[i]);
-        float v = 1.f;
-        if (norm == GNN_NORM_MEAN) v = 1.f / di;
-        if (norm == GNN_NORM_GCN) v = dj > 0.f ? 1.f / sqrtf(di * dj) : 0.f;
-        cw[e] = v;
+    const float dj = in_degree(indptr, (int32_t)j);
+    for (int32_t e = cindptr[j] + lane; e < cindptr[j + 1]; e += kWave)
+        cw[e] = spmm_weight(norm, in_degree(indptr, cindices[e]), dj);
+}
+
+// weights of a tiled plan's residual entries, in the order of a residual
+// structure (rptr, ridx) whose rows are destinations (residual CSR) or
+// sources (transposed residual); degrees from the full CSR
+__global__ void k_spmm_w_res(const int32_t *indptr, const int32_t *rptr, const int32_t *ridx, int32_t n, int norm,
+                             int rows_are_dst, float *w) {
+    const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (r >= n) return;
+    const float dr = in_degree(indptr, (int32_t)r);
+    for (int32_t e = rptr[r] + lane; e < rptr[r + 1]; e += kWave) {
+        const float dother = in_degree(indptr, ridx[e]);
+        w[e] = rows_are_dst ? spmm_weight(norm, dr, dother) : spmm_weight(norm, dother, dr);
     }
 }
 
@@ -328,6 +340,144 @@ static int run_spmm(gnn_plan_t plan, SpParams &P, const int32_t *by_degree, cons
     return GNN_OK;
 }
 
+// ------------------------------------------------- 16x16 block tiles (WSB)
+//
+// On a plan with a tile census, each tiled 16-row block (a 16-column block for
+// the transposed product) runs in one 4-wave workgroup. Tile phase: per tile,
+// the 16 gathered rows of X are staged in LDS as fp32 and the block product
+// Y_b += W_t X_t runs on the matrix cores as 16x16x4 fp32 MFMA steps (wave w
+// takes the 16-feature chunks w and w + 4), with W_t built in registers from
+// the tile's bit mask and the entries' weights (from the in-degrees, the same
+// expression as the cached weights). The 16 x F block result goes through LDS
+// to the CSR lane geometry (4 rows per wave, 16-byte slices), which streams
+// the block's residual entries with the cached residual weights, adds the
+// tile result and writes the row once. fp32 throughout, one rounding to the
+// storage type; no atomics.
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr int kWsbWaves = 4;
+
+struct WsbArgs {
+    const int32_t *blocks;      // tiled row blocks (product) or column blocks (transposed product)
+    int32_t n_blocks;
+    const int32_t *tile_ptr;    // tile range of each block
+    const int32_t *tile_ids;    // null: tiles in range order; else tile ids (by column block)
+    const int32_t *tile_rc;     // (row block, column block) per tile
+    const uint64_t *tile_mask;  // 4 words per tile, bit (dst % 16) * 16 + (src % 16)
+    const int32_t *rptr, *ridx; // residual structure
+    const float *rw;            // residual weights
+    const int32_t *indptr;      // the CSR (in-degrees for the tile weights)
+    int32_t norm;
+};
+
+// fp32 row stride of the staged block, 16 (mod 64) floats: the four rows one
+// operand read touches start 16 banks apart
+__host__ __device__ constexpr int wsb_stride(int F) { return F + ((16 - F) % 64 + 64) % 64; }
+
+static size_t wsb_lds(int F) { return (size_t)(16 * wsb_stride(F) + 16 * (F + 4) + 16) * sizeof(float); }
+
+// rows of at most 16 lanes (the residual pass packs 4 rows per wave) and whole 16-feature chunks
+static bool wsb_supported(const SpGeom &g) { return g.F % 16 == 0 && g.L <= 16; }
+
+template <class T, int U, bool TR>
+__global__ __launch_bounds__(kWsbWaves * kWave) void k_spmm_wsb(SpParams P, WsbArgs A) {
+    using VT = Vec<T>;
+    constexpr int NV = VT::N;
+    extern __shared__ float lds[];
+    const SpGeom &G = P.g;
+    const int F = G.F, N = G.N;
+    const int xstride = wsb_stride(F), hstride = F + 4;
+    float *xs = lds;                                   // [16][xstride] staged gathered rows
+    float *hand = lds + 16 * xstride;                  // [16][hstride] tile result per output row
+    float *gdeg = hand + 16 * hstride;                 // [16] in-degrees of the gathered rows
+    const int blk = A.blocks[blockIdx.x];
+    const int row0 = blk * 16;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), l = lane_id();
+    const int m = l & 15, kq = l >> 4;
+    const int nch = F / 16;
+    f32x4_t acc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // this lane's A-operand row: output row m of the block
+    const float dout = row0 + m < N ? in_degree(A.indptr, row0 + m) : 0.f;
+    const int t0 = A.tile_ptr[blk], t1 = A.tile_ptr[blk + 1];
+    for (int t = t0; t < t1; ++t) {
+        const int tid = A.tile_ids ? A.tile_ids[t] : t;
+        const int s0 = 16 * A.tile_rc[2 * tid + (TR ? 0 : 1)];   // first gathered row
+        __syncthreads();                                          // the previous tile's operands are read
+        const int nvec = F / NV;
+        for (int v = threadIdx.x; v < 16 * nvec; v += kWsbWaves * kWave) {
+            const int r = v / nvec, c = (v % nvec) * NV;
+            float x[NV];
+            if (s0 + r < N) {
+                VT::unpack(load_vec<T>(P.X, (int64_t)(s0 + r) * F + c), x);
+            } else {
+#pragma unroll
+                for (int k = 0; k < NV; ++k) x[k] = 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < NV; ++k) xs[r * xstride + c + k] = x[k];
+        }
+        if (threadIdx.x < 16) gdeg[threadIdx.x] = s0 + (int)threadIdx.x < N ? in_degree(A.indptr, s0 + threadIdx.x) : 0.f;
+        const uint64_t w0 = A.tile_mask[4 * tid], w1 = A.tile_mask[4 * tid + 1], w2 = A.tile_mask[4 * tid + 2],
+                       w3 = A.tile_mask[4 * tid + 3];
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            // A operand of this step: lane (m, kq) holds W[m][4 st + kq]
+            const int k = 4 * st + kq;
+            const int bit = TR ? k * 16 + m : m * 16 + k;
+            const uint64_t word = (bit >> 6) == 0 ? w0 : (bit >> 6) == 1 ? w1 : (bit >> 6) == 2 ? w2 : w3;
+            const bool on = (word >> (bit & 63)) & 1ull;
+            const float dg = gdeg[k];
+            const float a = on ? (TR ? spmm_weight(A.norm, dg, dout) : spmm_weight(A.norm, dout, dg)) : 0.f;
+#pragma unroll
+            for (int ci = 0; ci < 2; ++ci) {
+                const int c = w + kWsbWaves * ci;
+                // B operand: lane (m, kq) holds X_t[4 st + kq][16 c + m]
+                if (c < nch) acc[ci] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, xs[k * xstride + 16 * c + m], acc[ci], 0, 0, 0);
+            }
+        }
+    }
+    // D layout: lane (m, kq) holds rows 4 kq + i of column 16 c + m
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci) {
+        const int c = w + kWsbWaves * ci;
+        if (c < nch) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hand[(4 * kq + i) * hstride + 16 * c + m] = acc[ci][i];
+        }
+    }
+    __syncthreads();
+    // residual entries: wave w takes the block's rows 4w .. 4w + 3
+    const SpLane<NV, 4> lp(G, 0);
+    const int r = 4 * w + (l >> 4);
+    const int node = row0 + r;
+    const int e0 = node < N ? A.rptr[node] : 0, e1 = node < N ? A.rptr[node + 1] : 0;
+    SpParams Q = P;
+    Q.indices = A.ridx;
+    Q.w = A.rw;
+    float y[NV];
+    sp_stream<T, U, 4>(Q, lp, e0, e1, y);
+    if (lp.g != 0 || !lp.act || node >= N) return;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) y[k] += hand[r * hstride + lp.col + k];
+    store_vec_nt<T>(P.Y, (int64_t)node * F + lp.col, VT::pack(y));
+}
+
+template <class T, bool TR>
+static int launch_wsb(gnn_plan_t plan, const SpParams &P, const WsbArgs &A, hipStream_t s) {
+    return launch(plan, TR ? K_SPMM_T_WSB : K_SPMM_WSB, k_spmm_wsb<T, 4, TR>, dim3((unsigned)A.n_blocks),
+                  dim3(kWsbWaves * kWave), wsb_lds(P.g.F), s, P, A);
+}
+
+template <class T, bool TR>
+static int run_spmm_tiled(gnn_plan_t plan, SpParams &P, const WsbArgs &A, hipStream_t s) {
+    GNN_TRY((run_spmm<T, TR>(plan, P, nullptr, nullptr, 0, s)));
+    return launch_wsb<T, TR>(plan, P, A, s);
+}
+
 }  // namespace gnn
 
 using namespace gnn;
@@ -369,6 +519,22 @@ int gnn_spmm_prepare(gnn_plan_t plan, gnn_norm_t norm, hipStream_t stream) {
                                    as<int2>(plan->spmm_crng));
         }
     }
+    if (plan->has_tiles) {
+        // a tiled plan's residual entries (their weights, in residual order)
+        const size_t rbytes = (size_t)std::max<int64_t>(plan->n_residual, 1) * 4;
+        if (plan->spmm_rw.bytes != rbytes) GNN_TRY(dev_alloc(plan->spmm_rw, rbytes));
+        if (n > 0)
+            hipLaunchKernelGGL(k_spmm_w_res, grid1d((int64_t)n * kWave), dim3(256), 0, stream, plan->indptr,
+                               as<int32_t>(plan->rindptr), as<int32_t>(plan->rindices), n, (int)norm, 1,
+                               as<float>(plan->spmm_rw));
+        if (plan->has_csc) {
+            if (plan->spmm_rcw.bytes != rbytes) GNN_TRY(dev_alloc(plan->spmm_rcw, rbytes));
+            if (n > 0)
+                hipLaunchKernelGGL(k_spmm_w_res, grid1d((int64_t)n * kWave), dim3(256), 0, stream, plan->indptr,
+                                   as<int32_t>(plan->rcindptr), as<int32_t>(plan->rcindices), n, (int)norm, 0,
+                                   as<float>(plan->spmm_rcw));
+        }
+    }
     GNN_HIP(hipGetLastError());
     plan->spmm_norm = (int32_t)norm;
     return GNN_OK;
@@ -408,6 +574,29 @@ int gnn_spmm(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int
         void *ws = nullptr;
         GNN_TRY(plan_workspace(plan, (size_t)P.n_groups * F * sizeof(float), stream, &ws));
         P.part = (float *)ws;
+    }
+    if (plan->has_tiles && wsb_supported(P.g)) {
+        // tiled blocks on the block kernel; the light rows outside them (one
+        // per wave) and the heavy rows on the CSR kernel
+        P.light = as<int32_t>(transpose ? plan->c_light_nt : plan->light_nt);
+        P.n_light = transpose ? plan->n_c_light_nt : plan->n_light_nt;
+        WsbArgs A{};
+        A.blocks = as<int32_t>(transpose ? plan->tcb : plan->trb);
+        A.n_blocks = transpose ? plan->n_tcb : plan->n_trb;
+        A.tile_ptr = as<int32_t>(transpose ? plan->ctile_ptr : plan->tile_ptr);
+        A.tile_ids = transpose ? as<int32_t>(plan->ctile) : nullptr;
+        A.tile_rc = as<int32_t>(plan->tile_rc);
+        A.tile_mask = as<uint64_t>(plan->tile_mask);
+        A.rptr = as<int32_t>(transpose ? plan->rcindptr : plan->rindptr);
+        A.ridx = as<int32_t>(transpose ? plan->rcindices : plan->rindices);
+        A.rw = as<float>(transpose ? plan->spmm_rcw : plan->spmm_rw);
+        A.indptr = indptr;
+        A.norm = plan->spmm_norm;
+        if (dtype == GNN_BF16)
+            return transpose ? run_spmm_tiled<bf16_tag, true>(plan, P, A, stream)
+                             : run_spmm_tiled<bf16_tag, false>(plan, P, A, stream);
+        return transpose ? run_spmm_tiled<float, true>(plan, P, A, stream)
+                         : run_spmm_tiled<float, false>(plan, P, A, stream);
     }
     const int32_t *by_degree = as<int32_t>(b.by_degree);
     const int2 *rng = as<int2>(transpose ? plan->spmm_crng : plan->spmm_rng);

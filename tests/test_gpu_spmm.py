@@ -131,6 +131,63 @@ def test_spmm_long_light_rows(g, dtype, F, threshold):
             assert np.array_equal(host(Y2), host(Y)), "not reproducible"
 
 
+def _tile_graph(kind):
+    """CSR arrays (rows sorted, repeated entries kept) for the tiled-plan tests."""
+    if kind == "blocks":
+        rng = np.random.default_rng(401)
+        n = 1000                                     # a ragged last block of 8 rows
+        a = rng.random((n, n)) < 0.01
+        for b0 in range(0, n - 15, 16):
+            if rng.random() < 0.6:
+                a[b0:b0 + 16, b0:b0 + 16] |= rng.random((16, 16)) < rng.uniform(0.6, 1.0)
+        a[:, 7] = True                               # a heavy source: its column block is never tiled
+        a[333, :] = True                             # a heavy row: its row block is never tiled
+        a[900:916, :] = False                        # empty rows inside a block
+        dst, src = np.nonzero(a)
+        dup = rng.choice(src.size, src.size // 20, replace=False)   # repeated entries, tiled and not
+        dst, src = np.concatenate([dst, dst[dup]]), np.concatenate([src, src[dup]])
+    else:
+        import workloads
+        wl = workloads.make(kind, 2048, features=False)
+        n, dst, src = wl.n_nodes, wl.dst.astype(np.int64), wl.src.astype(np.int64)
+    order = np.lexsort((src, dst))
+    dst, src = dst[order], src[order]
+    ip = np.concatenate([[0], np.cumsum(np.bincount(dst, minlength=n))]).astype(np.int32)
+    return ip, src.astype(np.int32), n
+
+
+@pytest.mark.parametrize("dtype,F", [("f32", 16), ("f32", 64), ("bf16", 16), ("bf16", 128), ("bf16", 256)])
+@pytest.mark.parametrize("kind,tau,T", [("spmm_comm16_n1m_deg27", 0.75, 512), ("blocks", 0.5, 60)])
+def test_spmm_tiled_plan(g, dtype, F, kind, tau, T):
+    """Plans with a tile census: tiled blocks run on the 16x16 block kernel
+    (MFMA tile products plus the blocks' residual entries), the other light
+    rows and the heavy rows on the CSR kernel; rows of more than 256 bytes
+    (bf16, F = 256) stay on the CSR kernel. Both products, three norms."""
+    rng = np.random.default_rng(F + int(100 * tau))
+    ip, ix, n = _tile_graph(kind)
+    ip_d, ix_d = dev_i32(ip), dev_i32(ix)
+    plan = g.gnn_plan_create(ip_d, ix_d, light_threshold=T, chunk=32, tile_density=tau, want_csc=True)
+    info = g.gnn_plan_export(plan)
+    say(f"{kind}: n={n} E={ip[-1]} tiles={info['n_tiles']} tiled row blocks={info['n_trb']} "
+        f"tiled column blocks={info['n_tcb']} residual={info['n_residual']}")
+    assert info["n_tiles"] > 0 and info["n_trb"] > 0 and info["n_tcb"] > 0
+    block_path = F * (2 if dtype == "bf16" else 4) <= 256
+    X = _feats(rng, n, F, dtype)
+    Xd = dev_feat(X, dtype)
+    for norm in ("gcn", "mean", "sum"):
+        g.gnn_spmm_prepare(plan, norm)
+        for tr in (False, True):
+            g.gnn_plan_set_timing(plan, True)
+            Y = g.gnn_spmm(plan, ip_d, ix_d, Xd, transpose=tr)
+            ran = g.gnn_plan_timing_read(plan)
+            g.gnn_plan_set_timing(plan, False)
+            assert (("spmm_t_wsb" if tr else "spmm_wsb") in ran) == block_path, ran
+            ref = oracle.spmm(ip, ix, X, norm, transpose=tr)
+            check(f"tiled spmm {kind} {dtype} F={F} {norm} transpose={tr}", host(Y), ref["Y"], ref["S"], dtype)
+            Y2 = g.gnn_spmm(plan, ip_d, ix_d, Xd, transpose=tr)
+            assert np.array_equal(host(Y2), host(Y)), "not reproducible"
+
+
 def test_spmm_errors_and_empty(g):
     import torch
     rng = np.random.default_rng(3)
