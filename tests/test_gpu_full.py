@@ -11,7 +11,8 @@ GPU outputs of each plan are compared with the same oracle rows. Properties
 that hold at any size are checked on the full GPU outputs.
 
 The reduction and SpMM workloads (ranked after the attention path) are
-compared in full on the graphs of up to 10M edges and on every heavy row plus
+compared in full on the graphs of up to 10M edges (SpMM: 30M, which takes in
+the clustered graph on its CSR and its tiled plan) and on every heavy row plus
 a seeded sample of light rows on the 64M-edge graph."""
 import time
 
@@ -314,21 +315,28 @@ def test_full_size_reduce(g, live, name):
     live(f"[full] {name}: {'every row' if small else f'{rows.size} rows'} compared ({time.time() - t0:.0f} s)")
 
 
-@pytest.mark.parametrize("name", ["spmm_chunglu25_n169k", "spmm_chunglu22_n2450k"])
-def test_full_size_spmm(g, live, name):
-    """GCN-normalised SpMM and its transpose at full size, default plan: every
-    row and source (169k-node graph) or every heavy row (source) and a seeded
-    sample of light ones (64M-edge graph)."""
+@pytest.mark.parametrize("name,tau", [("spmm_chunglu25_n169k", 0.0), ("spmm_chunglu22_n2450k", 0.0),
+                                      ("spmm_comm16_n1m_deg27", 0.0), ("spmm_comm16_n1m_deg27", 0.75)])
+def test_full_size_spmm(g, live, name, tau):
+    """GCN-normalised SpMM and its transpose at full size, on the default plan
+    and (clustered graph) on the tiled plan the benchmark times, whose tiled
+    blocks run on the 16x16 block kernel: every row and source (graphs up to
+    30M edges) or every heavy row (source) and a seeded sample of light ones
+    (64M-edge graph)."""
     import torch
-    say("full-size spmm", name)
+    say("full-size spmm", name, "tile density", tau)
     t0 = time.time()
     wl = workloads.make(name, backward=True)
     n, F = wl.n_nodes, wl.heads * wl.dim
     ip, ix = g.gnn_csr_build(torch.from_numpy(wl.src).cuda(), torch.from_numpy(wl.dst).cuda(), n)
     rp, rx = oracle.csr_build(wl.src, wl.dst, n)
     assert np.array_equal(ip.cpu().numpy(), rp) and np.array_equal(ix.cpu().numpy(), rx)
-    small = rx.size <= 10_000_000
-    plan = g.gnn_plan_create(ip, ix, want_csc=True)
+    small = rx.size <= 30_000_000
+    plan = g.gnn_plan_create(ip, ix, want_csc=True, tile_density=tau)
+    if tau > 0:
+        info = g.gnn_plan_export(plan)
+        say(f"  tiles {info['n_tiles']}, tiled row blocks {info['n_trb']}, column blocks {info['n_tcb']}")
+        assert info["n_trb"] > 0 and info["n_tcb"] > 0
     g.gnn_spmm_prepare(plan, "gcn")
     rng = np.random.default_rng(80)
     cip, _ = oracle.csc(rp, rx, n)
