@@ -620,9 +620,15 @@ def host_cpu() -> str:
     return f"{model}, {len(os.sched_getaffinity(0))} of {os.cpu_count()} logical CPUs in this process's affinity"
 
 
-def cpu_baseline(wl, rp, rx, target_s, threads=None, op="max", msg="src", norm="gcn"):
+# parity bar of the outputs (condition-scaled error), by storage type
+PARITY_TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def cpu_baseline(wl, rp, rx, target_s, threads=None, op="max", msg="src", norm="gcn", gpu=None):
     """fp64 oracle on a seeded sample of destination rows (and the same nodes
-    as sources for the gradient), sized to about target_s seconds."""
+    as sources for the gradient), sized to about target_s seconds. With the
+    GPU's outputs of the measured steps (`gpu`, host arrays), the sampled
+    rows of the last timed pass are also compared with them."""
     import numpy as np
 
     import oracle
@@ -631,12 +637,55 @@ def cpu_baseline(wl, rp, rx, target_s, threads=None, op="max", msg="src", norm="
     if threads:
         oracle.set_threads(threads)
     try:
-        return _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg, norm)
+        return _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg, norm, gpu)
     finally:
         oracle.set_threads(all_threads)
 
 
-def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg, norm):
+def _parity(oracle, wl, rows, res, gpu, op, msg):
+    """Condition-scaled and normwise errors of the GPU outputs on the sampled
+    rows (sources for the gradients) against the oracle's results."""
+    import numpy as np
+    tol = PARITY_TOL[wl.dtype]
+    out = {"rows": int(rows.size), "tolerance": tol, "max_scaled_error": {}, "normwise_error": {}}
+
+    def add(name, x, ref, scale, t=tol):
+        e = float(oracle.scaled_error(x, ref, scale))
+        out["max_scaled_error"][name] = float(f"{e:.3e}")
+        out["normwise_error"][name] = float(f"{float(oracle.normwise_error(x, ref)):.3e}")
+        return e <= t
+
+    ok = True
+    if wl.kind == "spmm":
+        ok &= add("Y", gpu["Y"][rows], res["f"]["Y"], res["f"]["S"])
+        if "b" in res:
+            ok &= add("dX", gpu["dX"][rows], res["b"]["Y"], res["b"]["S"])
+    elif wl.kind == "reduce":
+        ref = res["f"]
+        ro = oracle.round_bf16(ref["out"]) if (wl.dtype == "bf16" and msg == "diff") else ref["out"]
+        arg_eq = bool(np.array_equal(gpu["arg"][rows], ref["arg"]))
+        val_eq = bool(np.array_equal(gpu["out"][rows].astype(np.float32).view(np.uint32),
+                                     np.asarray(ro, np.float32).view(np.uint32)))
+        out.update(winners_bit_exact=arg_eq, values_bit_exact=val_eq,
+                   note="forward only: a sample of rows does not give its sources' whole gradient")
+        ok &= arg_eq and val_eq
+    else:
+        ok &= add("O", gpu["O"][rows], res["f"]["O"], res["f"]["SO"])
+        ok &= add("LSE", gpu["LSE"][rows], res["f"]["LSE"], res["f"]["SL"], PARITY_TOL["f32"])
+        if "b" in res:
+            b = res["b"]
+            if wl.kind == "gatv2":
+                ok &= add("dXD", gpu["dQ"][rows], b["dXD"], b["SdXD"])
+                ok &= add("dXS", gpu["dK"][rows], b["dXS"], b["SdXS"])
+            else:
+                ok &= add("dQ", gpu["dQ"][rows], b["dQ"], b["SdQ"])
+                ok &= add("dK", gpu["dK"][rows], b["dK"], b["SdK"])
+                ok &= add("dV", gpu["dV"][rows], b["dV"], b["SdV"])
+    out["within_tolerance"] = bool(ok)
+    return out
+
+
+def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg, norm, gpu=None):
     import numpy as np
 
     n = wl.n_nodes
@@ -656,28 +705,33 @@ def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg, norm):
         dO = np.asarray(wl.feats["dO"], np.float64) if wl.backward else None
     csc = oracle.csc(rp, rx, n) if wl.backward and wl.kind != "reduce" else None
 
+    last = {}
+
     def run(edges):
         k = int(np.searchsorted(csum, edges)) + 1
         rows = np.sort(order[:min(k, n)])
+        res = {}
         t0 = time.perf_counter()
         if wl.kind == "spmm":
-            oracle.spmm(rp, rx, X, norm, rows=rows)
+            res["f"] = oracle.spmm(rp, rx, X, norm, rows=rows)
             if wl.backward:
-                oracle.spmm(rp, rx, dO, norm, transpose=True, rows=rows)
+                res["b"] = oracle.spmm(rp, rx, dO, norm, transpose=True, rows=rows)
         elif wl.kind == "reduce":
-            arg = oracle.segment_reduce(rp, rx, X, op, msg, rows=rows)["arg"]
+            res["f"] = oracle.segment_reduce(rp, rx, X, op, msg, rows=rows)
             if wl.backward:
-                oracle.segment_reduce_bwd(rp, rx, dO[rows], arg, msg, n_nodes=n, rows=rows)
+                oracle.segment_reduce_bwd(rp, rx, dO[rows], res["f"]["arg"], msg, n_nodes=n, rows=rows)
         elif wl.kind == "gatv2":
-            oracle.gatv2_fwd(rp, rx, XD, XS, wl.att, slope=0.2, rows=rows)
+            res["f"] = oracle.gatv2_fwd(rp, rx, XD, XS, wl.att, slope=0.2, rows=rows)
             if wl.backward:
-                oracle.gatv2_bwd(rp, rx, XD, XS, wl.att, dO, slope=0.2, rows=rows, srcs=rows, csc_arrays=csc,
-                                 want_da=False)
+                res["b"] = oracle.gatv2_bwd(rp, rx, XD, XS, wl.att, dO, slope=0.2, rows=rows, srcs=rows,
+                                            csc_arrays=csc, want_da=False)
         else:
-            oracle.gt_fwd(rp, rx, Q, K, V, rows=rows)
+            res["f"] = oracle.gt_fwd(rp, rx, Q, K, V, rows=rows)
             if wl.backward:
-                oracle.gt_bwd(rp, rx, Q, K, V, dO, rows=rows, srcs=rows, csc_arrays=csc)
-        return time.perf_counter() - t0, int(deg[rows].sum()), rows.size
+                res["b"] = oracle.gt_bwd(rp, rx, Q, K, V, dO, rows=rows, srcs=rows, csc_arrays=csc)
+        t = time.perf_counter() - t0
+        last.update(rows=rows, res=res)
+        return t, int(deg[rows].sum()), rows.size
 
     e_try = min(int(csum[-1]), 200_000)
     t, e, r = run(e_try)
@@ -691,10 +745,13 @@ def _cpu_baseline(oracle, wl, rp, rx, target_s, op, msg, norm):
         reps += 1
     t = tt / reps
     cores = 1 if wl.kind == "spmm" else oracle.num_threads()      # scipy's sparse product runs on one thread
-    return dict(value=round(e / t / 1e9, 6), unit="GEdges/s", cores=cores, kind="oracle", host=host_cpu(),
-                sample=f"{r} destination rows drawn uniformly (seed 12345) covering {e} of {int(csum[-1])} edges"
-                       + (" (forward + backward, the same nodes as sources)" if wl.backward else " (forward)")
-                       + f", {t:.2f} s per pass, mean of {reps}")
+    rec = dict(value=round(e / t / 1e9, 6), unit="GEdges/s", cores=cores, kind="oracle", host=host_cpu(),
+               sample=f"{r} destination rows drawn uniformly (seed 12345) covering {e} of {int(csum[-1])} edges"
+                      + (" (forward + backward, the same nodes as sources)" if wl.backward else " (forward)")
+                      + f", {t:.2f} s per pass, mean of {reps}")
+    if gpu is not None:
+        rec["parity"] = _parity(oracle, wl, last["rows"], last["res"], gpu, op, msg)
+    return rec
 
 
 def bench(args) -> int:
@@ -855,9 +912,11 @@ def bench(args) -> int:
         import oracle
         rp = indptr.cpu().numpy()
         rx = indices.cpu().numpy()
-        log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        log(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s), checked against the measured outputs")
+        names = {"spmm": ("Y", "dX"), "reduce": ("out", "arg")}.get(wl.kind, ("O", "LSE", "dQ", "dK", "dV"))
+        gpu = {k: (T[k].float() if T[k].dtype == torch.bfloat16 else T[k]).cpu().numpy() for k in names if k in T}
         rec["cpu_baseline"] = cpu_baseline(wl, rp, rx, args.cpu_seconds, op=args.reduce_op, msg=args.msg,
-                                           norm=args.norm)
+                                           norm=args.norm, gpu=gpu)
         if E <= 10_000_000 and wl.kind != "spmm":
             rec["cpu_baseline_1core"] = cpu_baseline(wl, rp, rx, args.cpu_seconds / 2, threads=1,
                                                      op=args.reduce_op, msg=args.msg)

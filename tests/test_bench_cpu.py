@@ -160,3 +160,44 @@ def test_roofline_context_labels_the_cache_state():
     # a model rate above the HBM peak is flagged as no bound
     c = bench.roofline_context("gt_bwd_src_main", 8, 64, 2, 1_000_000, 10164.0, 30.34e9, 6020.0)
     assert not c["model_is_bound"] and "not a bound" in c["note"]
+
+
+@pytest.mark.parametrize("name", ["gt_uniform_n2708", "gatv2_zipf21_n100k", "spmm_chunglu25_n169k",
+                                  "maxpool_zipf21_n100k"])
+def test_cpu_baseline_checks_the_measured_outputs(name):
+    """The baseline leg compares the GPU's outputs on its sampled rows with
+    the oracle: the oracle's own outputs pass, a planted error fails."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    wl = workloads.make(name, 600, backward=name != "maxpool_zipf21_n100k")
+    n = wl.n_nodes
+    rp, rx = oracle.csr_build(wl.src, wl.dst, n)
+    f = {k: np.asarray(v) for k, v in wl.feats.items()}
+    if wl.kind == "spmm":
+        F = wl.heads * wl.dim
+        gpu = {"Y": oracle.spmm(rp, rx, f["X"].reshape(n, F))["Y"],
+               "dX": oracle.spmm(rp, rx, f["dO"].reshape(n, F), transpose=True)["Y"]}
+        key = "Y"
+    elif wl.kind == "reduce":
+        r = oracle.segment_reduce(rp, rx, f["X"].reshape(n, -1), "max", "src")
+        gpu = {"out": np.asarray(r["out"], np.float32), "arg": r["arg"]}
+        key = "out"
+    elif wl.kind == "gatv2":
+        r = oracle.gatv2_fwd(rp, rx, f["XD"], f["XS"], wl.att, slope=0.2)
+        b = oracle.gatv2_bwd(rp, rx, f["XD"], f["XS"], wl.att, f["dO"], slope=0.2, want_da=False)
+        gpu = {"O": r["O"], "LSE": r["LSE"], "dQ": b["dXD"], "dK": b["dXS"]}
+        key = "O"
+    else:
+        r = oracle.gt_fwd(rp, rx, f["Q"], f["K"], f["V"])
+        b = oracle.gt_bwd(rp, rx, f["Q"], f["K"], f["V"], f["dO"])
+        gpu = {"O": r["O"], "LSE": r["LSE"], "dQ": b["dQ"], "dK": b["dK"], "dV": b["dV"]}
+        key = "O"
+    rec = bench.cpu_baseline(wl, rp, rx, 0.05, gpu=gpu)
+    par = rec["parity"]
+    assert par["within_tolerance"] and par["rows"] > 0, par
+    bad = dict(gpu)
+    bad[key] = np.array(gpu[key], dtype=np.float64 if key != "out" else np.float32, copy=True)
+    bad[key][...] += 0.5 * (np.abs(bad[key]).max() + 1.0)
+    assert not bench.cpu_baseline(wl, rp, rx, 0.05, gpu=bad)["parity"]["within_tolerance"]
