@@ -620,6 +620,24 @@ def host_cpu() -> str:
     return f"{model}, {len(os.sched_getaffinity(0))} of {os.cpu_count()} logical CPUs in this process's affinity"
 
 
+def memory_record(g, plan, T, indptr, indices, wl, E):
+    """Device memory of the measured run: what the library holds (the plan's
+    structures and its workspace, grown to the largest request) and what the
+    caller holds (graph, features and outputs). No per-edge buffer exists; for
+    scale, the bytes of one fp32 score per edge and head, the smallest
+    intermediate a materialising implementation keeps."""
+    info = g.gnn_plan_export(plan)
+    tensors = sum(t.numel() * t.element_size() for t in T.values())
+    graph = indptr.numel() * indptr.element_size() + indices.numel() * indices.element_size()
+    lib = int(info["structure_bytes"]) + int(info["workspace_bytes"])
+    rec = {"library_bytes": lib, "plan_structure_bytes": int(info["structure_bytes"]),
+           "plan_workspace_bytes": int(info["workspace_bytes"]), "caller_graph_bytes": int(graph),
+           "caller_feature_and_output_bytes": int(tensors)}
+    if wl.kind in ("gt", "gatv2"):
+        rec["per_edge_score_bytes_not_materialised"] = int(E) * wl.heads * 4
+    return rec
+
+
 # parity bar of the outputs (condition-scaled error), by storage type
 PARITY_TOL = {"f32": 1e-4, "bf16": 2e-2}
 
@@ -905,6 +923,7 @@ def bench(args) -> int:
         },
         "kernels": kernels,
         "kernel_source_sha256": kernel_source_hash(dom),
+        "memory": memory_record(g, plan, T, indptr, indices, wl, E),
         "preprocess": prep,
         "wall_s_timed": round(wall, 4),
     }

@@ -326,6 +326,20 @@ int gnn_plan_timing_read(gnn_plan_t plan, int32_t cap, const char **names /*host
                          int32_t *launches /*host [cap]*/, double *total_ms /*host [cap]*/,
                          int32_t *n_out /*host*/);
 
+/*
+ * 1 when this library is the checked build (compiled with GNN_CHECKED, the
+ * debugging variant), else 0. In the checked build every compute call also
+ * validates its indptr / indices as gnn_plan_create does (after the argument
+ * checks; the allocation-free forward skips this, as the check allocates), and
+ * its kernels check every graph index before using it as a node-table row: an
+ * index outside [0, N) is replaced by row 0, so no access leaves the tables,
+ * and the call returns GNN_ERR_BAD_GRAPH after its kernels (it synchronises
+ * the stream to read the kernels' flags). Results of good graphs are the same
+ * as the normal build's.
+ * For: debugging callers' graph arrays and the library itself; not for speed.
+ */
+int gnn_build_checked(void);
+
 /* Human-readable text for a status code (includes the last HIP error for GNN_ERR_HIP). */
 const char *gnn_status_string(int status);
 

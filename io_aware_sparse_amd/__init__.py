@@ -11,7 +11,7 @@ fallback path, and calls fail loudly when the library is missing.
 Function names match the C ABI: gnn_csr_build, gnn_plan_create,
 gnn_plan_export, gnn_plan_destroy, gnn_attn_fwd, gnn_attn_fwd_noalloc, gnn_attn_bwd,
 gatv2_attn_fwd, gatv2_attn_bwd, gnn_plan_set_timing, gnn_plan_timing_read,
-gnn_status_string.
+gnn_build_checked, gnn_status_string.
 """
 from __future__ import annotations
 
@@ -20,7 +20,9 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgnn_attn.so")
+# GNN_CHECKED=1 selects the checked build (graph validation in every call and
+# device-side index checks; for debugging, not for speed)
+LIB_PATH = os.path.join(_PKG, "libgnn_attn_checked.so" if os.environ.get("GNN_CHECKED") == "1" else "libgnn_attn.so")
 
 GNN_F32, GNN_BF16 = 0, 1
 GNN_OK = 0
@@ -31,7 +33,7 @@ STATUS = {0: "GNN_OK", -1: "GNN_ERR_INVALID_ARG", -2: "GNN_ERR_UNSUPPORTED", -3:
 EXPORTS = ["gnn_plan_opts_default", "gnn_csr_build", "gnn_plan_create", "gnn_plan_export", "gnn_plan_destroy",
            "gnn_attn_fwd", "gnn_attn_fwd_noalloc", "gnn_attn_bwd", "gatv2_attn_fwd", "gatv2_attn_bwd", "gnn_plan_set_timing",
            "gnn_plan_timing_read", "gnn_status_string", "gnn_reduce_fwd", "gnn_reduce_bwd", "gnn_reorder",
-           "gnn_permute_graph", "gnn_permute_rows", "gnn_spmm_prepare", "gnn_spmm"]
+           "gnn_permute_graph", "gnn_permute_rows", "gnn_spmm_prepare", "gnn_spmm", "gnn_build_checked"]
 ORDERS = {"degree": 0, "rcm": 1}      # gnn_order_t
 NORMS = {"sum": 0, "mean": 1, "gcn": 2}   # gnn_norm_t
 REDUCE_OPS = {"max": 0, "min": 1}     # gnn_reduce_op_t
@@ -111,6 +113,7 @@ def lib():
         L.gnn_plan_set_timing.argtypes = [V, I32]
         L.gnn_plan_timing_read.argtypes = [V, I32, C.POINTER(C.c_char_p), C.POINTER(C.c_int32),
                                            C.POINTER(C.c_double), C.POINTER(C.c_int32)]
+        L.gnn_build_checked.argtypes = []
         L.gnn_status_string.argtypes = [C.c_int]
         L.gnn_status_string.restype = C.c_char_p
         for name in EXPORTS:
@@ -414,6 +417,11 @@ def gatv2_attn_bwd(plan: Plan, indptr, indices, XD, XS, att, dO, LSE, V=None, ne
                                 _ptr(dXD), _ptr(dXS), _ptr(dV), _ptr(d_att), _dtype_code(XD), _stream(stream)),
            "gatv2_attn_bwd")
     return dXD, dXS, dV, d_att
+
+
+def gnn_build_checked() -> bool:
+    """True when the loaded library is the checked build."""
+    return bool(lib().gnn_build_checked())
 
 
 def gnn_plan_set_timing(plan: Plan, enable: bool = True):

@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgnn_attn.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
+# the checked build (GNN_CHECKED: graph validation in every call, device-side index checks)
+LIB_CHECKED = os.path.join(PKG, "libgnn_attn_checked.so")
+OBJ_DIR_CHECKED = os.path.join(ROOT, "_build", "obj_checked")
 SOURCES = ["prep.hip", "tiles.hip", "attn.hip", "attn_tile.hip", "attn_gat.hip", "reduce.hip", "reorder.hip",
            "spmm.hip"]
 HEADERS = ["device.h", "internal.h", "attn_core.h"]
@@ -55,14 +58,16 @@ def _filtered(stderr: str) -> str:
     return "\n".join(l for l in stderr.splitlines() if "packed-fp32-ops" not in l)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into the package's shared library (always rebuilds)."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(verbose: bool = False, checked: bool = False) -> str:
+    """Compile every HIP source into the package's shared library (always
+    rebuilds); checked=True builds the checked variant instead."""
+    obj_dir, lib = (OBJ_DIR_CHECKED, LIB_CHECKED) if checked else (OBJ_DIR, LIB)
+    os.makedirs(obj_dir, exist_ok=True)
     cc = hipcc()
-    inc = ["-I", os.path.join(ROOT, "include")]
+    inc = ["-I", os.path.join(ROOT, "include")] + (["-DGNN_CHECKED"] if checked else [])
 
     def compile_one(src):
-        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
         cmd = [cc, *COMPILE_FLAGS, *inc, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         return src, obj, cmd, r
@@ -82,7 +87,7 @@ def build(verbose: bool = False) -> str:
             objs.append(obj)
     if failed:
         raise RuntimeError("hipcc failed")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [cc, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -90,9 +95,10 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc link failed")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build(verbose=True, checked=True))

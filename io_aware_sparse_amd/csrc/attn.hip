@@ -377,6 +377,7 @@ static int fwd_common(gnn_plan_t plan, const int32_t *indptr, const int32_t *ind
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return GNN_ERR_ALIGNMENT;
     if (mode != M_GT && !aligned16(att)) return GNN_ERR_ALIGNMENT;
     if (N == 0) return GNN_OK;
+    if (!fixed_ws) GNN_TRY(checked_graph(indptr, indices, N, E, s));   // the allocation-free path skips it
     FwdParams P{};
     const int LH = lanes_per_head(dtype, D);
     P.g = make_geom(N, H, D, LH);
@@ -495,6 +496,9 @@ static int scratch_on_current_device(float **out) {
     return GNN_OK;
 }
 
+// this file's kernels' index flag (checked builds)
+GNN_INDEX_FAULT_READER(index_fault_attn)
+
 }  // namespace gnn
 
 using namespace gnn;
@@ -505,8 +509,9 @@ int gnn_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices,
                  int32_t D, const void *Q, const void *K, const void *V, void *O, float *LSE, float scale,
                  gnn_dtype_t dtype, hipStream_t stream) {
     const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)std::max(D, 1)));
-    return fwd_common(plan, indptr, indices, N, E, H, D, Q, K, V, O, LSE, nullptr, 0.f, sc * kLog2e, M_GT, dtype,
-                      stream);
+    return finish_call(fwd_common(plan, indptr, indices, N, E, H, D, Q, K, V, O, LSE, nullptr, 0.f, sc * kLog2e, M_GT,
+                                  dtype, stream),
+                       stream);
 }
 
 int gnn_attn_fwd_noalloc(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
@@ -521,19 +526,21 @@ int gnn_attn_fwd_noalloc(gnn_plan_t plan, const int32_t *indptr, const int32_t *
     float *buf = nullptr;
     GNN_TRY(scratch_on_current_device(&buf));
     const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)std::max(D, 1)));
-    return fwd_common(plan, indptr, indices, N, E, H, D, Q, K, V, O, LSE, nullptr, 0.f, sc * kLog2e, M_GT, dtype,
-                      stream, buf, GNN_NOALLOC_SCRATCH_BYTES);
+    return finish_call(fwd_common(plan, indptr, indices, N, E, H, D, Q, K, V, O, LSE, nullptr, 0.f, sc * kLog2e, M_GT,
+                                  dtype, stream, buf, GNN_NOALLOC_SCRATCH_BYTES),
+                       stream);
 }
 
 int gatv2_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
                    int32_t H, int32_t D, const void *Q, const void *K, const void *V, const float *att,
                    float negative_slope, void *O, float *LSE, gnn_dtype_t dtype, hipStream_t stream) {
     const int mode = (V == K) ? M_GAT_ALIAS : M_GAT_SEPV;
-    return fwd_common(plan, indptr, indices, N, E, H, D, Q, K, V, O, LSE, att, negative_slope, 1.f, mode, dtype,
-                      stream);
+    return finish_call(fwd_common(plan, indptr, indices, N, E, H, D, Q, K, V, O, LSE, att, negative_slope, 1.f, mode,
+                                  dtype, stream),
+                       stream);
 }
 
-int gnn_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t H,
+static int attn_bwd_impl(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t H,
                  int32_t D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
                  const float *LSE, void *dQ, void *dK, void *dV, float scale, gnn_dtype_t dtype,
                  hipStream_t stream) {
@@ -544,6 +551,7 @@ int gnn_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices,
     for (const void *p : {Q, K, V, dO, (const void *)dQ, (const void *)dK, (const void *)dV})
         if (!aligned16(p)) return GNN_ERR_ALIGNMENT;
     if (N == 0) return GNN_OK;
+    GNN_TRY(checked_graph(indptr, indices, N, E, stream));
     const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
     BwdParams P{};
     fill_bwd_params(plan, P, indptr, indices, N, H, D, Q, K, V, dO, LSE, dQ, dK, dV, sc, dtype);
@@ -578,6 +586,13 @@ int gnn_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices,
         }
     }
     return GNN_ERR_UNSUPPORTED;
+}
+
+int gnn_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t H,
+                 int32_t D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                 const float *LSE, void *dQ, void *dK, void *dV, float scale, gnn_dtype_t dtype,
+                 hipStream_t stream) {
+    return finish_call(attn_bwd_impl(plan, indptr, indices, N, E, H, D, Q, K, V, O, dO, LSE, dQ, dK, dV, scale, dtype, stream), stream);
 }
 
 }  // extern "C"

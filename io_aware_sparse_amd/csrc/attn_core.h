@@ -134,14 +134,14 @@ __device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp
     const int S = min(kWave / RPW, GR * U);         // edges per step of this row
     const int UE = S / GR;                          // steps per group actually used
     const int li = lp.lane - lp.rg0;
-    int jn = (li < S && e0 + li < e1) ? P.indices[e0 + li] : -1;
+    int jn = (li < S && e0 + li < e1) ? checked_index(P.indices[e0 + li], G.N) : -1;
     // steps until every row of the wave has used up its edges (one row: until base >= e1)
     for (int base = e0; RPW == 1 ? base < e1 : __any(base < e1); base += S) {
         const int jc = jn;
         if (RPW == 1) {
-            if (base + S < e1) jn = (li < S && base + S + li < e1) ? P.indices[base + S + li] : -1;
+            if (base + S < e1) jn = (li < S && base + S + li < e1) ? checked_index(P.indices[base + S + li], G.N) : -1;
         } else {
-            jn = (li < S && base + S + li < e1) ? P.indices[base + S + li] : -1;
+            jn = (li < S && base + S + li < e1) ? checked_index(P.indices[base + S + li], G.N) : -1;
         }
         int j[U];
 #pragma unroll
@@ -274,10 +274,10 @@ __device__ __forceinline__ void bwd_dst_stream(const BwdParams &P, const LanePos
     }
     const int S = min(kWave, G.G * U);
     const int UE = S / G.G;
-    int jn = (lp.lane < S && e0 + lp.lane < e1) ? P.indices[e0 + lp.lane] : -1;
+    int jn = (lp.lane < S && e0 + lp.lane < e1) ? checked_index(P.indices[e0 + lp.lane], G.N) : -1;
     for (int base = e0; base < e1; base += S) {
         const int jc = jn;
-        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? P.indices[base + S + lp.lane] : -1;
+        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? checked_index(P.indices[base + S + lp.lane], G.N) : -1;
         int j[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) j[u] = (u < UE) ? __shfl(jc, u * G.G + lp.g, kWave) : -1;
@@ -330,10 +330,10 @@ __device__ __forceinline__ void bwd_src_stream(const BwdParams &P, const LanePos
     }
     const int S = min(kWave, G.G * U);
     const int UE = S / G.G;
-    int jn = (lp.lane < S && e0 + lp.lane < e1) ? P.cindices[e0 + lp.lane] : -1;
+    int jn = (lp.lane < S && e0 + lp.lane < e1) ? checked_index(P.cindices[e0 + lp.lane], G.N) : -1;
     for (int base = e0; base < e1; base += S) {
         const int jc = jn;
-        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? P.cindices[base + S + lp.lane] : -1;
+        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? checked_index(P.cindices[base + S + lp.lane], G.N) : -1;
         int i[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) i[u] = (u < UE) ? __shfl(jc, u * G.G + lp.g, kWave) : -1;

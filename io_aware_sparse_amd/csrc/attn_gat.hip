@@ -62,10 +62,10 @@ __device__ __forceinline__ void gat_dst_stream(const GatBwdParams &GP, const Lan
     const float slope = GP.slope;
     const int S = min(kWave, G.G * U);
     const int UE = S / G.G;
-    int jn = (lp.lane < S && e0 + lp.lane < e1) ? P.indices[e0 + lp.lane] : -1;
+    int jn = (lp.lane < S && e0 + lp.lane < e1) ? checked_index(P.indices[e0 + lp.lane], G.N) : -1;
     for (int base = e0; base < e1; base += S) {
         const int jc = jn;
-        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? P.indices[base + S + lp.lane] : -1;
+        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? checked_index(P.indices[base + S + lp.lane], G.N) : -1;
         int j[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) j[u] = (u < UE) ? __shfl(jc, u * G.G + lp.g, kWave) : -1;
@@ -229,10 +229,10 @@ __device__ __forceinline__ void gat_src_stream(const GatBwdParams &GP, const Lan
     const float slope = GP.slope;
     const int S = min(kWave, G.G * U);
     const int UE = S / G.G;
-    int jn = (lp.lane < S && e0 + lp.lane < e1) ? P.cindices[e0 + lp.lane] : -1;
+    int jn = (lp.lane < S && e0 + lp.lane < e1) ? checked_index(P.cindices[e0 + lp.lane], G.N) : -1;
     for (int base = e0; base < e1; base += S) {
         const int jc = jn;
-        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? P.cindices[base + S + lp.lane] : -1;
+        if (base + S < e1) jn = (lp.lane < S && base + S + lp.lane < e1) ? checked_index(P.cindices[base + S + lp.lane], G.N) : -1;
         int i[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) i[u] = (u < UE) ? __shfl(jc, u * G.G + lp.g, kWave) : -1;
@@ -447,11 +447,16 @@ static int dispatch_gat_bwd(gnn_plan_t plan, GatBwdParams &GP, gnn_dtype_t dt, i
     return GNN_ERR_UNSUPPORTED;
 }
 
+// this file's kernels' index flag (checked builds)
+GNN_INDEX_FAULT_READER(index_fault_gat)
+
 }  // namespace gnn
 
 using namespace gnn;
 
-extern "C" int gatv2_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
+extern "C" {
+
+static int gat_bwd_impl(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
                               int32_t H, int32_t D, const void *Q, const void *K, const void *V, const float *att,
                               float negative_slope, const void *dO, const float *LSE, void *dQ, void *dK, void *dV,
                               float *d_att, gnn_dtype_t dtype, hipStream_t stream) {
@@ -465,6 +470,7 @@ extern "C" int gatv2_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int3
         if (!aligned16(p)) return GNN_ERR_ALIGNMENT;
     if (sepv && !aligned16(dV)) return GNN_ERR_ALIGNMENT;
     if (N == 0) return GNN_OK;
+    GNN_TRY(checked_graph(indptr, indices, N, E, stream));
     GatBwdParams GP{};
     BwdParams &P = GP.b;
     fill_bwd_params(plan, P, indptr, indices, N, H, D, Q, K, V, dO, LSE, dQ, dK, sepv ? dV : nullptr, 1.f, dtype);
@@ -486,3 +492,12 @@ extern "C" int gatv2_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int3
     return sepv ? dispatch_gat_bwd<true>(plan, GP, dtype, D, stream)
                 : dispatch_gat_bwd<false>(plan, GP, dtype, D, stream);
 }
+
+int gatv2_attn_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E,
+                              int32_t H, int32_t D, const void *Q, const void *K, const void *V, const float *att,
+                              float negative_slope, const void *dO, const float *LSE, void *dQ, void *dK, void *dV,
+                              float *d_att, gnn_dtype_t dtype, hipStream_t stream) {
+    return finish_call(gat_bwd_impl(plan, indptr, indices, N, E, H, D, Q, K, V, att, negative_slope, dO, LSE, dQ, dK, dV, d_att, dtype, stream), stream);
+}
+
+}  // extern "C"

@@ -618,4 +618,7 @@ int launch_tile_bwd_src(gnn_plan_t plan, const BwdParams &P, int D, hipStream_t 
     return GNN_ERR_UNSUPPORTED;
 }
 
+// this file's kernels' index flag (checked builds)
+GNN_INDEX_FAULT_READER(index_fault_tile)
+
 }  // namespace gnn

@@ -151,4 +151,48 @@ __device__ __forceinline__ void store_vec_nt(void *base, int64_t elem_off, const
     __builtin_nontemporal_store(x, reinterpret_cast<u4 *>(reinterpret_cast<char *>(base) + elem_off * Vec<T>::bytes));
 }
 
+// Checked builds (compiled with GNN_CHECKED): a kernel passes each graph index
+// it is about to use as a node-table row through checked_index, which marks an
+// index outside [0, n) in this source file's flag and uses row 0 instead, so
+// the access stays in bounds; the entry points read and clear the flags and
+// return GNN_ERR_BAD_GRAPH. Other builds use the index as it is.
+#ifdef GNN_CHECKED
+static __device__ int g_index_fault;
+#endif
+
+__device__ __forceinline__ int checked_index(int j, int n) {
+#ifdef GNN_CHECKED
+    if ((unsigned)j >= (unsigned)n) {
+        atomicOr(&g_index_fault, 1);
+        return 0;
+    }
+#endif
+    return j;
+}
+
+// Defines `int NAME(hipStream_t s)` for one source file: in checked builds it
+// reads and clears that file's index flag (1: a kernel met a bad index; -1: a
+// HIP call failed), in other builds it returns 0.
+#ifdef GNN_CHECKED
+#define GNN_INDEX_FAULT_READER(NAME)                                                                      \
+    int NAME(hipStream_t s) {                                                                             \
+        int h = 0;                                                                                        \
+        if (hipMemcpyFromSymbolAsync(&h, HIP_SYMBOL(g_index_fault), sizeof(int), 0, hipMemcpyDeviceToHost, \
+                                     s) != hipSuccess ||                                                  \
+            hipStreamSynchronize(s) != hipSuccess)                                                        \
+            return -1;                                                                                    \
+        if (h) {                                                                                          \
+            const int z = 0;                                                                              \
+            if (hipMemcpyToSymbolAsync(HIP_SYMBOL(g_index_fault), &z, sizeof(int), 0, hipMemcpyHostToDevice, \
+                                       s) != hipSuccess ||                                                \
+                hipStreamSynchronize(s) != hipSuccess)                                                    \
+                return -1;                                                                                \
+        }                                                                                                 \
+        return h;                                                                                         \
+    }
+#else
+#define GNN_INDEX_FAULT_READER(NAME) \
+    int NAME(hipStream_t) { return 0; }
+#endif
+
 }  // namespace gnn

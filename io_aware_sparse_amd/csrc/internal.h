@@ -186,4 +186,33 @@ int build_buckets(const int32_t *indptr, int32_t n, int32_t T, int32_t C, int32_
                   Buckets &b, hipStream_t s, bool by_degree = false);
 // 16x16 tile census of the plan's graph (fills the plan's tile arrays)
 int build_tiles(gnn_plan_s *p, int32_t min_nnz, hipStream_t s);
+
+// Checked builds (GNN_CHECKED): each compute entry point validates its graph
+// after the argument checks (checked_graph) and, after its kernels, reads and
+// clears every source file's index flag (finish_call): GNN_ERR_BAD_GRAPH when
+// a kernel met an index outside [0, N). Other builds: no-ops.
+int index_fault_attn(hipStream_t s);
+int index_fault_gat(hipStream_t s);
+int index_fault_tile(hipStream_t s);
+int index_fault_reduce(hipStream_t s);
+int index_fault_spmm(hipStream_t s);
+int take_index_faults(hipStream_t s);
+
+inline int checked_graph(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, hipStream_t s) {
+#ifdef GNN_CHECKED
+    return n > 0 ? validate_csr(indptr, indices, n, e, s) : GNN_OK;
+#else
+    (void)indptr, (void)indices, (void)n, (void)e, (void)s;
+    return GNN_OK;
+#endif
+}
+
+inline int finish_call(int rc, hipStream_t s) {
+#ifdef GNN_CHECKED
+    return rc != GNN_OK ? rc : take_index_faults(s);
+#else
+    (void)s;
+    return rc;
+#endif
+}
 }  // namespace gnn

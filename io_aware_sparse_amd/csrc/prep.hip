@@ -688,6 +688,20 @@ int64_t gnn_plan_s::structure_bytes() {
 }
 
 namespace gnn {
+int take_index_faults(hipStream_t s) {
+    int bad = 0;
+    for (auto f : {index_fault_attn, index_fault_gat, index_fault_tile, index_fault_reduce, index_fault_spmm}) {
+        const int r = f(s);
+        if (r < 0) {
+            set_hip_error(hipGetLastError(), "index check");
+            return GNN_ERR_HIP;
+        }
+        bad |= r;
+    }
+    if (bad) return GNN_ERR_BAD_GRAPH;
+    return GNN_OK;
+}
+
 int plan_workspace(gnn_plan_s *p, size_t bytes, hipStream_t s, void **out) {
     if (bytes <= p->ws.bytes) {
         *out = p->ws.p;
@@ -890,6 +904,14 @@ int gnn_plan_destroy(gnn_plan_t p) {
     dev_free(p->ws);
     delete p;
     return GNN_OK;
+}
+
+int gnn_build_checked(void) {
+#ifdef GNN_CHECKED
+    return 1;
+#else
+    return 0;
+#endif
 }
 
 int gnn_plan_set_timing(gnn_plan_t p, int32_t enable) {

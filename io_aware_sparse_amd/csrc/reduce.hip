@@ -133,14 +133,14 @@ __device__ __forceinline__ void red_stream(const RedParams &P, const RLane &lp, 
     const int S = min(kLanesRG, GR * U);      // edges per step of this row
     const int UE = S / GR;
     const int li = lp.lane - lp.rg0;
-    int jn = (li < S && e0 + li < e1) ? P.indices[e0 + li] : -1;
+    int jn = (li < S && e0 + li < e1) ? checked_index(P.indices[e0 + li], G.N) : -1;
     // steps until every row group of the wave has used up its edges (one row: until base >= e1)
     for (int base = e0; RPW == 1 ? base < e1 : __any(base < e1); base += S) {
         const int jc = jn;
         if (RPW == 1) {
-            if (base + S < e1) jn = (li < S && base + S + li < e1) ? P.indices[base + S + li] : -1;
+            if (base + S < e1) jn = (li < S && base + S + li < e1) ? checked_index(P.indices[base + S + li], G.N) : -1;
         } else {
-            jn = (li < S && base + S + li < e1) ? P.indices[base + S + li] : -1;
+            jn = (li < S && base + S + li < e1) ? checked_index(P.indices[base + S + li], G.N) : -1;
         }
         int j[U];
 #pragma unroll
@@ -174,7 +174,7 @@ __device__ __forceinline__ void red_stream(const RedParams &P, const RLane &lp, 
         // a group whose messages all equal the worst value (an infinity) took none of them: its first
         // edge wins; a group without edges stays empty with value 0
         const int e_first = e0 + lp.g;
-        const int j_first = e_first < e1 ? P.indices[e_first] : -1;
+        const int j_first = e_first < e1 ? checked_index(P.indices[e_first], G.N) : -1;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             if (bj[k] < 0) {
@@ -358,7 +358,7 @@ __device__ __forceinline__ void red_bwd_stream(const RedParams &P, const RLane &
     // entry e is skipped when it repeats entry e-1 of the same transposed row
     auto fetch = [&](int e) -> int {
         if (e >= e1) return -1;
-        const int i = P.indices[e];
+        const int i = checked_index(P.indices[e], G.N);
         return (e > row0 && P.indices[e - 1] == i) ? -1 : i;
     };
     int jn = lp.lane < S ? fetch(e0 + lp.lane) : -1;
@@ -575,13 +575,16 @@ static int dispatch_red_fwd(gnn_plan_t plan, RedParams &P, int op, int msg, hipS
                               : run_red_fwd<T, GNN_REDUCE_MIN, GNN_MSG_DIFF>(plan, P, s);
 }
 
+// this file's kernels' index flag (checked builds)
+GNN_INDEX_FAULT_READER(index_fault_reduce)
+
 }  // namespace gnn
 
 using namespace gnn;
 
 extern "C" {
 
-int gnn_reduce_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
+static int reduce_fwd_impl(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
                    const void *X, void *out, int32_t *arg, gnn_reduce_op_t op, gnn_msg_t msg, gnn_dtype_t dtype,
                    hipStream_t stream) {
     GNN_TRY(red_check(plan, indptr, indices, N, E, F, dtype));
@@ -590,6 +593,7 @@ int gnn_reduce_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indice
     if (N > 0 && (!X || !out)) return GNN_ERR_INVALID_ARG;
     if (!aligned16(X) || !aligned16(out) || !aligned16(arg)) return GNN_ERR_ALIGNMENT;
     if (N == 0) return GNN_OK;
+    GNN_TRY(checked_graph(indptr, indices, N, E, stream));
     RedParams P{};
     P.g = red_geom(N, F, dtype);
     P.indptr = indptr;
@@ -622,7 +626,13 @@ int gnn_reduce_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indice
     return dispatch_red_fwd<float>(plan, P, op, msg, stream);
 }
 
-int gnn_reduce_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
+int gnn_reduce_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
+                   const void *X, void *out, int32_t *arg, gnn_reduce_op_t op, gnn_msg_t msg, gnn_dtype_t dtype,
+                   hipStream_t stream) {
+    return finish_call(reduce_fwd_impl(plan, indptr, indices, N, E, F, X, out, arg, op, msg, dtype, stream), stream);
+}
+
+static int reduce_bwd_impl(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
                    const void *dOut, const int32_t *arg, void *dX, gnn_msg_t msg, gnn_dtype_t dtype,
                    hipStream_t stream) {
     if (!plan) return GNN_ERR_INVALID_ARG;
@@ -632,6 +642,7 @@ int gnn_reduce_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indice
     if (N > 0 && (!dOut || !arg || !dX)) return GNN_ERR_INVALID_ARG;
     if (!aligned16(dOut) || !aligned16(arg) || !aligned16(dX)) return GNN_ERR_ALIGNMENT;
     if (N == 0) return GNN_OK;
+    GNN_TRY(checked_graph(indptr, indices, N, E, stream));
     RedParams P{};
     P.g = red_geom(N, F, dtype);
     P.indptr = as<int32_t>(plan->cindptr);
@@ -659,6 +670,12 @@ int gnn_reduce_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indice
                                   : run_red_bwd<bf16_tag, GNN_MSG_DIFF>(plan, P, stream);
     return msg == GNN_MSG_SRC ? run_red_bwd<float, GNN_MSG_SRC>(plan, P, stream)
                               : run_red_bwd<float, GNN_MSG_DIFF>(plan, P, stream);
+}
+
+int gnn_reduce_bwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
+                   const void *dOut, const int32_t *arg, void *dX, gnn_msg_t msg, gnn_dtype_t dtype,
+                   hipStream_t stream) {
+    return finish_call(reduce_bwd_impl(plan, indptr, indices, N, E, F, dOut, arg, dX, msg, dtype, stream), stream);
 }
 
 }  // extern "C"

@@ -57,7 +57,7 @@ __global__ void k_spmm_w_rows(const int32_t *indptr, const int32_t *indices, int
     const int32_t e0 = indptr[i], e1 = indptr[i + 1];
     const float di = (float)(e1 - e0);
     for (int32_t e = e0 + lane; e < e1; e += kWave)
-        w[e] = spmm_weight(norm, di, norm == GNN_NORM_GCN ? in_degree(indptr, indices[e]) : 0.f);
+        w[e] = spmm_weight(norm, di, norm == GNN_NORM_GCN ? in_degree(indptr, checked_index(indices[e], n)) : 0.f);
 }
 
 // weights in transposed order: the entries of source j name destinations i
@@ -68,7 +68,7 @@ __global__ void k_spmm_w_cols(const int32_t *indptr, const int32_t *cindptr, con
     if (j >= n) return;
     const float dj = in_degree(indptr, (int32_t)j);
     for (int32_t e = cindptr[j] + lane; e < cindptr[j + 1]; e += kWave)
-        cw[e] = spmm_weight(norm, in_degree(indptr, cindices[e]), dj);
+        cw[e] = spmm_weight(norm, in_degree(indptr, checked_index(cindices[e], n)), dj);
 }
 
 // weights of a tiled plan's residual entries, in the order of a residual
@@ -81,7 +81,7 @@ __global__ void k_spmm_w_res(const int32_t *indptr, const int32_t *rptr, const i
     if (r >= n) return;
     const float dr = in_degree(indptr, (int32_t)r);
     for (int32_t e = rptr[r] + lane; e < rptr[r + 1]; e += kWave) {
-        const float dother = in_degree(indptr, ridx[e]);
+        const float dother = in_degree(indptr, checked_index(ridx[e], n));
         w[e] = rows_are_dst ? spmm_weight(norm, dr, dother) : spmm_weight(norm, dother, dr);
     }
 }
@@ -152,7 +152,7 @@ __device__ __forceinline__ void sp_stream(const SpParams &P, const SpLane<Vec<T>
     int jn = -1;
     float wn = 0.f;
     if (li < S && e0 + li < e1) {
-        jn = P.indices[e0 + li];
+        jn = checked_index(P.indices[e0 + li], G.N);
         wn = P.w[e0 + li];
     }
     for (int base = e0; RPW == 1 ? base < e1 : __any(base < e1); base += S) {
@@ -161,7 +161,7 @@ __device__ __forceinline__ void sp_stream(const SpParams &P, const SpLane<Vec<T>
         jn = -1;
         wn = 0.f;
         if (li < S && base + S + li < e1) {
-            jn = P.indices[base + S + li];
+            jn = checked_index(P.indices[base + S + li], G.N);
             wn = P.w[base + S + li];
         }
         int j[U];
@@ -478,6 +478,9 @@ static int run_spmm_tiled(gnn_plan_t plan, SpParams &P, const WsbArgs &A, hipStr
     return launch_wsb<T, TR>(plan, P, A, s);
 }
 
+// this file's kernels' index flag (checked builds)
+GNN_INDEX_FAULT_READER(index_fault_spmm)
+
 }  // namespace gnn
 
 using namespace gnn;
@@ -540,7 +543,7 @@ int gnn_spmm_prepare(gnn_plan_t plan, gnn_norm_t norm, hipStream_t stream) {
     return GNN_OK;
 }
 
-int gnn_spmm(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
+static int spmm_impl(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
              const void *X, void *Y, int32_t transpose, gnn_dtype_t dtype, hipStream_t stream) {
     if (!plan || N < 0 || E < 0 || F < 1 || !indptr || (E > 0 && !indices)) return GNN_ERR_INVALID_ARG;
     if (plan->n_nodes != N || plan->n_edges != E || plan->indptr != indptr || plan->indices != indices)
@@ -553,6 +556,7 @@ int gnn_spmm(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int
     if (N > 0 && (!X || !Y)) return GNN_ERR_INVALID_ARG;
     if (!aligned16(X) || !aligned16(Y)) return GNN_ERR_ALIGNMENT;
     if (N == 0) return GNN_OK;
+    GNN_TRY(checked_graph(indptr, indices, N, E, stream));
     SpParams P{};
     P.g = sp_geom(N, F, dtype);
     P.X = X;
@@ -605,6 +609,11 @@ int gnn_spmm(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int
                          : run_spmm<bf16_tag, false>(plan, P, by_degree, rng, b.n_long, stream);
     return transpose ? run_spmm<float, true>(plan, P, by_degree, rng, b.n_long, stream)
                      : run_spmm<float, false>(plan, P, by_degree, rng, b.n_long, stream);
+}
+
+int gnn_spmm(gnn_plan_t plan, const int32_t *indptr, const int32_t *indices, int32_t N, int64_t E, int32_t F,
+             const void *X, void *Y, int32_t transpose, gnn_dtype_t dtype, hipStream_t stream) {
+    return finish_call(spmm_impl(plan, indptr, indices, N, E, F, X, Y, transpose, dtype, stream), stream);
 }
 
 }  // extern "C"

@@ -201,3 +201,22 @@ def test_cpu_baseline_checks_the_measured_outputs(name):
     bad[key] = np.array(gpu[key], dtype=np.float64 if key != "out" else np.float32, copy=True)
     bad[key][...] += 0.5 * (np.abs(bad[key]).max() + 1.0)
     assert not bench.cpu_baseline(wl, rp, rx, 0.05, gpu=bad)["parity"]["within_tolerance"]
+
+
+def test_memory_record_adds_up():
+    """The bench line's memory object: library bytes are the plan's structures
+    plus workspace; caller bytes count the graph and every tensor of the step."""
+    import numpy as np
+    import torch
+
+    class Plan:
+        pass
+
+    g = types.SimpleNamespace(gnn_plan_export=lambda plan: {"structure_bytes": 1000, "workspace_bytes": 24})
+    T = {"Q": torch.zeros(10, 2, 4), "LSE": torch.zeros(10, 2)}
+    ip, ix = torch.zeros(11, dtype=torch.int32), torch.zeros(30, dtype=torch.int32)
+    wl = types.SimpleNamespace(kind="gt", heads=2)
+    rec = bench.memory_record(g, Plan(), T, ip, ix, wl, 30)
+    assert rec["library_bytes"] == 1024 and rec["caller_graph_bytes"] == 4 * 41
+    assert rec["caller_feature_and_output_bytes"] == 4 * (80 + 20)
+    assert rec["per_edge_score_bytes_not_materialised"] == 30 * 2 * 4
