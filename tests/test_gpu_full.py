@@ -11,9 +11,9 @@ GPU outputs of each plan are compared with the same oracle rows. Properties
 that hold at any size are checked on the full GPU outputs.
 
 The reduction and SpMM workloads (ranked after the attention path) are
-compared in full on the graphs of up to 10M edges (SpMM: 30M, which takes in
-the clustered graph on its CSR and its tiled plan) and on every heavy row plus
-a seeded sample of light rows on the 64M-edge graph."""
+compared on every row, the SpMM on the clustered graph also on its tiled
+plan; the reduction's gradient on every source up to 10M edges and, on the
+64M-edge graph, on sampled sources and through a column-sum identity."""
 import time
 
 import numpy as np
@@ -29,7 +29,7 @@ FULL = ["gt_uniform_n2708", "gt_chunglu25_n169k", "gatv2_zipf21_n100k", "gt_chun
         "gt_comm16_n1m_deg27", "gt_comm16_n1m_deg100"]
 TILED = {"gt_comm16_n1m_deg27", "gt_comm16_n1m_deg100"}
 CHUNK_EDGES = 6_000_000          # oracle edges per call
-N_SAMPLE = 20000                 # sampled rows on the 64M-edge reduction / SpMM graph
+N_SAMPLE = 20000                 # sampled sources of the reduction gradient on the 64M-edge graph
 
 
 @pytest.fixture(scope="module")
@@ -265,10 +265,12 @@ def _bits32(x):
 @pytest.mark.parametrize("name", ["maxpool_zipf21_n100k", "maxpool_chunglu22_n2450k"])
 def test_full_size_reduce(g, live, name):
     """Max / min reduction at full size, default plan: values and winners bit
-    for bit on every row (Zipf graph) or on every heavy row and a seeded
-    sample of light rows (64M-edge graph); the gradient against the oracle on
-    every source (Zipf graph) or through its column-sum identity (every
-    non-empty row's dOut lands exactly once)."""
+    for bit on every row; the gradient against the oracle on every source
+    (Zipf graph) or, on the 64M-edge graph, on every heavy source and a
+    seeded sample of light ones (max of sources: the oracle given only the
+    winners that fall in the sample, so that its scatter stays small) and
+    through its column-sum identity (every non-empty row's dOut lands exactly
+    once)."""
     import torch
     say("full-size reduce", name)
     t0 = time.time()
@@ -280,19 +282,21 @@ def test_full_size_reduce(g, live, name):
     small = rx.size <= 10_000_000
     plan = g.gnn_plan_create(ip, ix, want_csc=True)
     heavy = oracle.bucketing(rp, 512, 512, 4)["heavy"]
+    cip, _ = oracle.csc(rp, rx, n)
     rng = np.random.default_rng(79)
-    rows = np.arange(n) if small else _sample(rng, n, heavy, N_SAMPLE)
+    rows = np.arange(n)
+    srcs = None if small else _sample(rng, n, oracle.bucketing(cip, 512, 512, 4)["heavy"], N_SAMPLE)
     X = wl.feats["X"].reshape(n, F)
     Xd = _dev(wl, "X").reshape(n, F)
     gO = _dev(wl, "dO").reshape(n, F)
     for op, msg in (("max", "src"), ("min", "diff")):
         out, arg = g.gnn_reduce_fwd(plan, ip, ix, Xd, op, msg)
         torch.cuda.synchronize()
-        ref = oracle.segment_reduce(rp, rx, X, op, msg, rows=None if small else rows)
+        ref = oracle.segment_reduce(rp, rx, X, op, msg)
         ro = oracle.round_bf16(ref["out"]) if (wl.dtype == "bf16" and msg == "diff") else ref["out"]
         ga = arg.cpu().numpy()[rows]
         go = out.float().cpu().numpy()[rows]
-        say(f"  {op} {msg}: {rows.size} rows ({heavy.size} heavy), winners equal "
+        say(f"  {op} {msg}: every row ({heavy.size} heavy), winners equal "
             f"{np.mean(ga == ref['arg']):.6f}, values equal {np.mean(_bits32(go) == _bits32(ro)):.6f}")
         assert np.array_equal(ga, ref["arg"]) and np.array_equal(_bits32(go), _bits32(ro)), (op, msg)
         dX = g.gnn_reduce_bwd(plan, ip, ix, gO, arg, msg)
@@ -302,6 +306,12 @@ def test_full_size_reduce(g, live, name):
                                                want_scale=True)
             _check(f"dX {op} {msg}", _host(dX), rdX, S, wl.dtype)
         else:
+            if msg == "src":
+                # every term that lands on a sampled source: the winners outside the sample dropped
+                keep = np.where(np.isin(ref["arg"], srcs), ref["arg"], -1)
+                rdX, S = oracle.segment_reduce_bwd(rp, rx, wl.feats["dO"].reshape(n, F), keep, msg,
+                                                   want_scale=True)
+                _check(f"dX {op} {msg} (sampled sources)", _host(dX)[srcs], rdX[srcs], S[srcs], wl.dtype)
             nonempty = np.diff(rp) > 0
             col = dX.double().sum(0).cpu().numpy()
             want = wl.feats["dO"].reshape(n, F)[nonempty].astype(np.float64).sum(0)
@@ -312,7 +322,8 @@ def test_full_size_reduce(g, live, name):
             say(f"  dX column sums: max |sum - expected| / sum|dOut| = {err:.2e}")
             assert err <= (1e-6 if wl.dtype == "f32" else 1e-2), err
         del out, arg, dX
-    live(f"[full] {name}: {'every row' if small else f'{rows.size} rows'} compared ({time.time() - t0:.0f} s)")
+    live(f"[full] {name}: every row compared{'' if small else f', {srcs.size} sources of the gradient'} "
+         f"({time.time() - t0:.0f} s)")
 
 
 @pytest.mark.parametrize("name,tau", [("spmm_chunglu25_n169k", 0.0), ("spmm_chunglu22_n2450k", 0.0),
@@ -320,9 +331,7 @@ def test_full_size_reduce(g, live, name):
 def test_full_size_spmm(g, live, name, tau):
     """GCN-normalised SpMM and its transpose at full size, on the default plan
     and (clustered graph) on the tiled plan the benchmark times, whose tiled
-    blocks run on the 16x16 block kernel: every row and source (graphs up to
-    30M edges) or every heavy row (source) and a seeded sample of light ones
-    (64M-edge graph)."""
+    blocks run on the 16x16 block kernel: every row and every source."""
     import torch
     say("full-size spmm", name, "tile density", tau)
     t0 = time.time()
@@ -331,17 +340,13 @@ def test_full_size_spmm(g, live, name, tau):
     ip, ix = g.gnn_csr_build(torch.from_numpy(wl.src).cuda(), torch.from_numpy(wl.dst).cuda(), n)
     rp, rx = oracle.csr_build(wl.src, wl.dst, n)
     assert np.array_equal(ip.cpu().numpy(), rp) and np.array_equal(ix.cpu().numpy(), rx)
-    small = rx.size <= 30_000_000
     plan = g.gnn_plan_create(ip, ix, want_csc=True, tile_density=tau)
     if tau > 0:
         info = g.gnn_plan_export(plan)
         say(f"  tiles {info['n_tiles']}, tiled row blocks {info['n_trb']}, column blocks {info['n_tcb']}")
         assert info["n_trb"] > 0 and info["n_tcb"] > 0
     g.gnn_spmm_prepare(plan, "gcn")
-    rng = np.random.default_rng(80)
-    cip, _ = oracle.csc(rp, rx, n)
-    rows = np.arange(n) if small else _sample(rng, n, oracle.bucketing(rp, 512, 512, 4)["heavy"], N_SAMPLE)
-    srcs = np.arange(n) if small else _sample(rng, n, oracle.bucketing(cip, 512, 512, 4)["heavy"], N_SAMPLE)
+    rows = srcs = np.arange(n)
     X = wl.feats["X"].reshape(n, F)
     dO = wl.feats["dO"].reshape(n, F)
     Y = g.gnn_spmm(plan, ip, ix, _dev(wl, "X").reshape(n, F))
@@ -351,4 +356,4 @@ def test_full_size_spmm(g, live, name, tau):
     _check("Y", _host(Y)[rows], ref["Y"], ref["S"], wl.dtype)
     ref = oracle.spmm(rp, rx, dO, "gcn", transpose=True, rows=srcs)
     _check("dX", _host(dX)[srcs], ref["Y"], ref["S"], wl.dtype)
-    live(f"[full] {name}: {'every row' if small else f'{rows.size} rows'} compared ({time.time() - t0:.0f} s)")
+    live(f"[full] {name}: every row and source compared ({time.time() - t0:.0f} s)")
