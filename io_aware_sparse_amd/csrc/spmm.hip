@@ -14,20 +14,22 @@
 // has the transposed adjacency, in its order too.
 //
 // The product uses the degree-aware layout of the other kernels: a lane holds
-// one 16-byte slice of a feature row; light rows run from the
-// packed-order list 4 per wave when a row spans at most 16 lanes
-// (256 bytes), 2 per wave with 10 edges per step in fp32 (8 in bf16) when it
-// spans 17-32 lanes (512 bytes), else one per wave; the packed waves read each row's entry
-// range from a record cached by gnn_spmm_prepare, alongside the row id
-// (rows are short: one dependent load fewer before the gathers). The light
-// rows of more than 128 entries, which head the packed list, get a wave each
-// in the same launch (all its edge groups on one row), so the longest light
-// rows take half or a quarter of the steps they would take packed; heavy
-// rows run as the plan's chunk groups, their W waves
-// summed in LDS and the groups summed in ascending order by a second pass.
-// fp32 accumulation, output rounded to the storage type; no atomics, so the
-// result is bitwise reproducible. The transposed product (dX = A_w^T dY) is
-// the same kernel over the transposed adjacency and its buckets.
+// one 16-byte slice of a feature row; light rows run from the packed-order
+// list 4 per wave when a row spans at most 16 lanes (256 bytes), 2 per wave
+// with 10 edges per step in fp32 (8 in bf16) when it spans 17-32 lanes (512
+// bytes), else one per wave; the packed waves read each row's entry range
+// from a record cached by gnn_spmm_prepare, alongside the row id (rows are
+// short: one dependent load fewer before the gathers). The light rows of more
+// than 128 entries, which head the packed list, get a wave each in the same
+// launch (all its edge groups on one row), so the longest light rows take
+// half or a quarter of the steps they would take packed; heavy rows run as
+// the plan's chunk groups, their W waves summed in LDS and the groups summed
+// in ascending order by a second pass. On a plan with a tile census the
+// tiled 16-row blocks run on the block kernel further down (the Weighted
+// Block Sparse option: tile products on the matrix cores, then the blocks'
+// residual entries). fp32 accumulation, output rounded to the storage type;
+// no atomics, so the result is bitwise reproducible. The transposed product
+// (dX = A_w^T dY) is the same kernels over the transposed structures.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
