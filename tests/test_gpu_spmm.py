@@ -140,6 +140,9 @@ def _tile_graph(kind):
         for b0 in range(0, n - 15, 16):
             if rng.random() < 0.6:
                 a[b0:b0 + 16, b0:b0 + 16] |= rng.random((16, 16)) < rng.uniform(0.6, 1.0)
+            if rng.random() < 0.3:                   # dense off-diagonal blocks: several tiles per row
+                c0 = 16 * int(rng.integers(1, n // 16))          # and per column block
+                a[b0:b0 + 16, c0:c0 + 16] |= rng.random((16, 16)) < rng.uniform(0.6, 1.0)
         a[:, 7] = True                               # a heavy source: its column block is never tiled
         a[333, :] = True                             # a heavy row: its row block is never tiled
         a[900:916, :] = False                        # empty rows inside a block
@@ -171,6 +174,9 @@ def test_spmm_tiled_plan(g, dtype, F, kind, tau, T):
     say(f"{kind}: n={n} E={ip[-1]} tiles={info['n_tiles']} tiled row blocks={info['n_trb']} "
         f"tiled column blocks={info['n_tcb']} residual={info['n_residual']}")
     assert info["n_tiles"] > 0 and info["n_trb"] > 0 and info["n_tcb"] > 0
+    if kind == "blocks":                              # blocks with several tiles, both ways
+        d = g.gnn_plan_export(plan, arrays=True)
+        assert np.diff(d["tile_ptr"]).max() >= 2 and np.diff(d["ctile_ptr"]).max() >= 2
     block_path = F * (2 if dtype == "bf16" else 4) <= 256
     X = _feats(rng, n, F, dtype)
     Xd = dev_feat(X, dtype)

@@ -32,6 +32,9 @@ def _graph(g, kind):
         for b0 in range(0, n - 15, 16):
             if rng.random() < 0.6:
                 a[b0:b0 + 16, b0:b0 + 16] |= rng.random((16, 16)) < rng.uniform(0.6, 1.0)
+            if rng.random() < 0.3:                   # dense off-diagonal blocks: several tiles per row
+                c0 = 16 * int(rng.integers(1, n // 16))          # and per column block
+                a[b0:b0 + 16, c0:c0 + 16] |= rng.random((16, 16)) < rng.uniform(0.6, 1.0)
         a[:, 7] = True
         a[333, :] = True
         dst, src = np.nonzero(a)
@@ -61,6 +64,9 @@ def test_tile_fwd_bwd_parity(g, D, H, kind, tau, T):
     plan = g.gnn_plan_create(ip, ix, light_threshold=T, chunk=32, waves_per_group=4, tile_density=tau, want_csc=True)
     info = g.gnn_plan_export(plan)
     assert info["n_tiles"] > 0
+    if kind == "blocks":                              # blocks with several tiles, both ways
+        d = g.gnn_plan_export(plan, arrays=True)
+        assert np.diff(d["tile_ptr"]).max() >= 2 and np.diff(d["ctile_ptr"]).max() >= 2
     rng = np.random.default_rng(D + 3 * H)
     Q, K, V, dO = rand_feats(rng, n, H, D, "bf16", k=4)
     q, k, v, go = (dev_feat(x, "bf16") for x in (Q, K, V, dO))
