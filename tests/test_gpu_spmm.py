@@ -159,7 +159,8 @@ def _tile_graph(kind):
     return ip, src.astype(np.int32), n
 
 
-@pytest.mark.parametrize("dtype,F", [("f32", 16), ("f32", 64), ("bf16", 16), ("bf16", 128), ("bf16", 256)])
+@pytest.mark.parametrize("dtype,F", [("f32", 16), ("f32", 32), ("f32", 64), ("bf16", 16), ("bf16", 48), ("bf16", 128),
+                                     ("bf16", 256)])
 @pytest.mark.parametrize("kind,tau,T", [("spmm_comm16_n1m_deg27", 0.75, 512), ("blocks", 0.5, 60)])
 def test_spmm_tiled_plan(g, dtype, F, kind, tau, T):
     """Plans with a tile census: tiled blocks run on the 16x16 block kernel
