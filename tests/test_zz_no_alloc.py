@@ -6,7 +6,8 @@ shape), each with heavy rows whose partial states go to the fixed scratch:
 outputs bitwise equal to gnn_attn_fwd's on an identical plan and within the
 oracle's bar; the plan's workspace never grows and device free memory does
 not change across a call. Also a tiled plan, the scratch-size error (nothing
-launched) and the timing guard."""
+launched), the timing guard, and the call recorded into a HIP graph whose
+replays (eager work on the shared scratch in between) equal the eager call."""
 import numpy as np
 import pytest
 
@@ -132,3 +133,45 @@ def test_noalloc_scratch_limit_and_timing_guard(g):
         g.gnn_attn_fwd_noalloc(plan2, ip, ix, q, q, q, O)
     assert e.value.status == -2
     g.gnn_plan_set_timing(plan2, False)
+
+
+def test_noalloc_under_graph_capture(g):
+    """The allocation-free forward recorded into a HIP graph and replayed: each
+    replay, after eager work that overwrites the outputs and the shared scratch
+    (another allocation-free call on another graph with heavy rows), equals the
+    eager result bit for bit."""
+    import torch
+    rp, rx = _graph("gt_chunglu25_n169k", 6000)
+    rp2, rx2 = _graph("gatv2_zipf21_n100k", 1500)
+    n, n2, H, D = rp.size - 1, rp2.size - 1, 4, 32
+    ip, ix, ip2, ix2 = dev_i32(rp), dev_i32(rx), dev_i32(rp2), dev_i32(rx2)
+    opts = dict(light_threshold=24, chunk=16, waves_per_group=4)
+    plan, plan2 = g.gnn_plan_create(ip, ix, **opts), g.gnn_plan_create(ip2, ix2, **opts)
+    assert g.gnn_plan_export(plan)["n_groups"] > 0 and g.gnn_plan_export(plan2)["n_groups"] > 0
+    q, k, v = (torch.from_numpy(x).cuda() for x in rand_feats(np.random.default_rng(21), n, H, D, "f32"))
+    q2, k2, v2 = (torch.from_numpy(x).cuda() for x in rand_feats(np.random.default_rng(22), n2, H, D, "f32"))
+    O_ref, L_ref = torch.empty_like(q), torch.empty((n, H), device="cuda")
+    g.gnn_attn_fwd_noalloc(plan, ip, ix, q, k, v, O_ref, L_ref)          # eager reference
+    O, L = torch.empty_like(q), torch.empty((n, H), device="cuda")
+    O2, L2 = torch.empty_like(q2), torch.empty((n2, H), device="cuda")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g.gnn_attn_fwd_noalloc(plan, ip, ix, q, k, v, O, L)             # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        g.gnn_attn_fwd_noalloc(plan, ip, ix, q, k, v, O, L)
+    torch.cuda.synchronize()
+    for r in range(4):
+        O.fill_(7.0)
+        L.fill_(7.0)
+        g.gnn_attn_fwd_noalloc(plan2, ip2, ix2, q2, k2, v2, O2, L2)      # eager work on the shared scratch
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O.view(torch.int32), O_ref.view(torch.int32)), f"replay {r}: O differs"
+        assert torch.equal(L.view(torch.int32), L_ref.view(torch.int32)), f"replay {r}: LSE differs"
+    say("noalloc: graph capture, 4 replays bitwise equal to the eager call")
