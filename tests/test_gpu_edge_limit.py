@@ -22,6 +22,7 @@ import pytest
 
 import oracle
 from _gpu import check, say
+from _helpers import stride_dests, stride_rows
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -33,14 +34,11 @@ assert E == (1 << 31) - (1 << 21)
 
 
 def _rows_of(ids):
-    """Sorted entry lists of rows `ids` (closed form), [len(ids), DEG] int32."""
-    ids = np.asarray(ids, np.int64)
-    return np.sort((ids[:, None] + STEP * np.arange(DEG)[None, :]) % N, axis=1).astype(np.int32)
+    return stride_rows(ids, N, STEP, DEG)
 
 
 def _dests_of(j):
-    """Every destination row that lists source j."""
-    return (j - STEP * np.arange(DEG)) % N
+    return stride_dests(j, N, STEP, DEG)
 
 
 @pytest.fixture(scope="module")

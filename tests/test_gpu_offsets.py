@@ -22,6 +22,7 @@ import pytest
 
 import oracle
 from _gpu import check, say
+from _helpers import dependency_subgraph
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -72,21 +73,7 @@ def graph(g):
 
 
 def _subgraph(G):
-    """Relabelled subgraph holding every input the sampled outputs depend on:
-    U (sorted global ids), its CSR (full rows for `need`, other rows empty)
-    and the local ids of rows, sources and need."""
-    rp, rx, cip, cix, rows, srcs = (G[k] for k in ("rp", "rx", "cip", "cix", "rows", "srcs"))
-    need = np.unique(np.concatenate([rows, srcs] + [cix[cip[s]:cip[s + 1]] for s in srcs]).astype(np.int64))
-    U = np.unique(np.concatenate([need] + [rx[rp[i]:rp[i + 1]] for i in need]).astype(np.int64))
-    loc = np.searchsorted(U, need)
-    deg = np.zeros(U.size, np.int64)
-    deg[loc] = rp[need + 1] - rp[need]
-    sp = np.concatenate([[0], np.cumsum(deg)])
-    sx = np.empty(int(sp[-1]), np.int32)
-    for i, li in zip(need, loc):
-        sx[sp[li]:sp[li + 1]] = np.searchsorted(U, rx[rp[i]:rp[i + 1]])
-    return dict(U=U, sp=sp, sx=sx, rows=np.searchsorted(U, rows), srcs=np.searchsorted(U, srcs),
-                need=loc)
+    return dependency_subgraph(*(G[k] for k in ("rp", "rx", "cip", "cix", "rows", "srcs")))
 
 
 def _take(x, U):
