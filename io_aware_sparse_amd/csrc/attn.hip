@@ -320,12 +320,13 @@ static int launch_fwd_main(gnn_plan_t plan, const FwdParams &P, hipStream_t s) {
 }
 
 // Light rows of 257-512 bytes (two edge groups per wave) on a plan run from
-// the packed-order list, 2 per wave with 8 edges per step, so each row
-// keeps the edges per step it would have alone and a wave has twice the
-// rows in flight; the rows of more than 128 edges at the head of that list
-// take a wave each (both edge groups, 16 edges per step), so the longest
-// light rows do not set the kernel's duration. Otherwise one (row, head
-// group) per wave, 4 edges per group and step.
+// the packed-order list, 2 per wave with 8 edges per step (GATv2) or 7 (GT:
+// 88 instead of 97 VGPRs for fp32, five waves per SIMD instead of four), so
+// each row keeps about the edges per step it would have alone and a wave has
+// twice the rows in flight; the rows of more than 128 edges at the head of
+// that list take a wave each (both edge groups, 16 or 14 edges per step), so
+// the longest light rows do not set the kernel's duration. Otherwise one
+// (row, head group) per wave, 4 edges per group and step.
 template <class T, int LH, int MODE>
 static int run_fwd(gnn_plan_t plan, FwdParams &P, const int32_t *by_degree, hipStream_t s) {
     const int kind_merge = MODE == M_GT ? K_FWD_MERGE : K_GAT_MERGE;
@@ -333,7 +334,7 @@ static int run_fwd(gnn_plan_t plan, FwdParams &P, const int32_t *by_degree, hipS
         FwdParams Q = P;
         Q.light = by_degree;
         Q.n_long = plan->fwd.n_long;
-        GNN_TRY((launch_fwd_main<T, LH, MODE, 8, 2>(plan, Q, s)));
+        GNN_TRY((launch_fwd_main<T, LH, MODE, MODE == M_GT ? 7 : 8, 2>(plan, Q, s)));
     } else {
         GNN_TRY((launch_fwd_main<T, LH, MODE, 4, 1>(plan, P, s)));
     }

@@ -105,7 +105,8 @@ __device__ __forceinline__ void merge_groups(SoftState<NV> &st, int lr_shift) {
 // stays inside the row group; the wave steps until every row is done.
 template <class T, int LH, int MODE, int U, int RPW = 1>
 __device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp, int node, int e0, int e1,
-                                           SoftState<Vec<T>::N> &st, bool reset = true) {
+                                           SoftState<Vec<T>::N> &st, bool reset = true,
+                                           const typename Vec<T>::raw *qown_p = nullptr) {
     using VT = Vec<T>;
     constexpr int NV = VT::N;
     const Geom &G = P.g;
@@ -116,7 +117,7 @@ __device__ __forceinline__ void fwd_stream(const FwdParams &P, const LanePos &lp
 #pragma unroll
     for (int k = 0; k < NV; ++k) q[k] = a[k] = 0.f;
     if (lp.act) {
-        qraw = load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col);
+        qraw = qown_p ? *qown_p : load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col);
         if (MODE != M_GT) {
             VT::unpack(qraw, q);
 #pragma unroll
@@ -255,7 +256,9 @@ __device__ __forceinline__ void store_scaled(void *base, int64_t off, const floa
 template <class T, int LH, int U>
 __device__ __forceinline__ void bwd_dst_stream(const BwdParams &P, const LanePos &lp, int node, int e0, int e1,
                                                float (&A)[Vec<T>::N], float (&B)[Vec<T>::N], float &dsum,
-                                               float &lse2, bool reset = true) {
+                                               float &lse2, bool reset = true,
+                                               const typename Vec<T>::raw *qown_p = nullptr,
+                                               const typename Vec<T>::raw *down_p = nullptr) {
     using VT = Vec<T>;
     constexpr int NV = VT::N;
     const Geom &G = P.g;
@@ -268,8 +271,13 @@ __device__ __forceinline__ void bwd_dst_stream(const BwdParams &P, const LanePos
     }
     lse2 = kNegInf;
     if (lp.act) {
-        q = load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col);
-        dof = load_vec<T>(P.dO, (int64_t)node * rowlen + lp.col);
+        if (qown_p) {
+            q = *qown_p;
+            dof = *down_p;
+        } else {
+            q = load_vec<T>(P.Q, (int64_t)node * rowlen + lp.col);
+            dof = load_vec<T>(P.dO, (int64_t)node * rowlen + lp.col);
+        }
         lse2 = P.LSE[(int64_t)node * G.H + lp.h] * kLog2e;
     }
     const int S = min(kWave, G.G * U);
@@ -314,7 +322,9 @@ __device__ __forceinline__ void bwd_dst_stream(const BwdParams &P, const LanePos
 template <class T, int LH, int U>
 __device__ __forceinline__ void bwd_src_stream(const BwdParams &P, const LanePos &lp, int node, int e0, int e1,
                                                float (&dk)[Vec<T>::N], float (&dv)[Vec<T>::N],
-                                               bool reset = true) {
+                                               bool reset = true,
+                                               const typename Vec<T>::raw *kown_p = nullptr,
+                                               const typename Vec<T>::raw *vown_p = nullptr) {
     using VT = Vec<T>;
     constexpr int NV = VT::N;
     const Geom &G = P.g;
@@ -325,8 +335,13 @@ __device__ __forceinline__ void bwd_src_stream(const BwdParams &P, const LanePos
         for (int k = 0; k < NV; ++k) dk[k] = dv[k] = 0.f;
     }
     if (lp.act) {
-        kown = load_vec<T>(P.K, (int64_t)node * rowlen + lp.col);
-        vown = load_vec<T>(P.V, (int64_t)node * rowlen + lp.col);
+        if (kown_p) {
+            kown = *kown_p;
+            vown = *vown_p;
+        } else {
+            kown = load_vec<T>(P.K, (int64_t)node * rowlen + lp.col);
+            vown = load_vec<T>(P.V, (int64_t)node * rowlen + lp.col);
+        }
     }
     const int S = min(kWave, G.G * U);
     const int UE = S / G.G;

@@ -22,12 +22,15 @@
 // for all heads of the group. Phase 2 hands the per-row state through LDS to
 // the CSR lane geometry and streams the residual (non-tile) edges of the 16
 // rows with the same code as the light path, continuing the same state, so
-// no cross-kernel merge is needed. P and dS enter the second products as
-// bf16 (rounding 2^-9 relative per term).
+// no cross-kernel merge is needed. The block's own rows that phase 2 needs
+// (Q; Q and dO; K and V) are copied to LDS by direct global-to-LDS loads
+// issued before the first tile, so phase 2 does not fetch them again. P and
+// dS enter the second products as bf16 (rounding 2^-9 relative per term).
 //
 // Occupancy. The state hand-off buffer overlays the staging rows (it is
 // written only after the last tile's products have read them), so a
-// workgroup's LDS is the larger of the two, not their sum. When the head
+// workgroup's LDS is the larger of the two, not their sum, plus the own-row
+// copy (about 50 KB at most: three workgroups per CU). When the head
 // group has fewer heads than the workgroup has waves (the backward passes at
 // D = 64 and 128), SPLIT waves share a head, each accumulating its own share
 // of the D output columns (the score products are recomputed by each): every
@@ -97,6 +100,28 @@ __device__ __forceinline__ void stage_rows(uint16_t *dst, const void *src, int r
     }
 }
 
+// Copy rows r0..r0+15 (head-group columns) of a [N, H*D] bf16 table into LDS
+// as [16][width] (unpadded: only read row-contiguously, one 16-byte slice per
+// lane) with direct global-to-LDS loads, which need no registers and complete
+// alongside the wave's other loads. Wave w moves the 64-vector chunks w,
+// w + 8, ... (16 * width / 8 vectors, a multiple of 64 for width >= 32); lanes
+// past the table (rows >= N, heads >= H) load element 0 instead, into slots
+// that are never read.
+__device__ __forceinline__ void dma_rows(uint16_t *dst, const void *src, int r0, int N, int64_t rowlen, int64_t c0,
+                                         int width, int64_t valid_width, int w) {
+    const int vpr = width / 8;
+    const int nchunk = 16 * vpr / kWave;
+    const int lane = lane_id();
+    for (int c = w; c < nchunk; c += kTileWaves) {
+        const int v = c * kWave + lane;
+        const int r = v / vpr, e = (v % vpr) * 8;
+        const bool ok = (r0 + r < N) && (e < valid_width);
+        const uint16_t *g = reinterpret_cast<const uint16_t *>(src) + (ok ? (int64_t)(r0 + r) * rowlen + c0 + e : 0);
+        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(dst + c * kWave * 8), 16, 0,
+                                         0);
+    }
+}
+
 __device__ __forceinline__ float sum4x(float x) {
     x += xor_lane(x, 16);
     x += xor_lane(x, 32);
@@ -130,6 +155,9 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
     const int SW = D + 3;
     float *state = lds;                                   // written after the last tile, over the staged rows
     uint16_t *vst = reinterpret_cast<uint16_t *>(lds);   // [16][stride]
+    // the block's own Q rows for phase 2, [16][width], past the state / staging
+    // region (the staged table takes 8 * stride floats)
+    uint16_t *qown = reinterpret_cast<uint16_t *>(lds + std::max(16 * HW * SW, 8 * stride));
     const int row0 = rb * 16;
     const int m = l & 15, q4 = l >> 4;
 
@@ -152,7 +180,11 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
 #pragma unroll
         for (int c = 0; c < DC; ++c) acc[s][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    for (int t = A.tile_ptr[rb]; t < A.tile_ptr[rb + 1]; ++t) {
+    // the tile range is read before the own-row copy is issued, so that waiting
+    // for it does not wait for the copy
+    const int t0 = A.tile_ptr[rb], t1 = A.tile_ptr[rb + 1];
+    dma_rows(qown, P.Q, row0, N, rowlen, c0, width, valid, w);
+    for (int t = t0; t < t1; ++t) {
         const int col0 = A.tile_rc[2 * t + 1] * 16;
         stage_rows(vst, P.V, col0, N, rowlen, c0, width, stride, valid);
         __syncthreads();
@@ -234,7 +266,8 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_fwd(FwdParams P, TileArgs
 #pragma unroll
             for (int k = 0; k < NV; ++k) st.acc[k] = row[lp.dv * NV + k];
         }
-        fwd_stream<bf16_tag, LH, M_GT, 4>(R, lp, node, A.rptr[node], A.rptr[node + 1], st, false);
+        fwd_stream<bf16_tag, LH, M_GT, 4>(R, lp, node, A.rptr[node], A.rptr[node + 1], st, false,
+                                          reinterpret_cast<const uint4 *>(qown + r * width + (lp.col - c0)));
         write_out<bf16_tag, NV>(P, lp, node, st);
     }
 }
@@ -260,6 +293,10 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(WP
     float *state = lds;                                   // [16][HW][2D+1]: A, B, Delta (after the last tile)
     uint16_t *kst = reinterpret_cast<uint16_t *>(lds);   // [16][stride]
     uint16_t *vst = kst + 16 * stride;
+    // the block's own Q and dO rows for phase 2, [16][width] each, past the
+    // state / staging region (two staged tables: 16 * stride floats)
+    uint16_t *qown = reinterpret_cast<uint16_t *>(lds + std::max(16 * HW * SW, 16 * stride));
+    uint16_t *gown = qown + 16 * width;
     const int row0 = rb * 16;
     const int m = l & 15, q4 = l >> 4;
     const int part = w % SPLIT, c0w = part * DCW;        // this wave's output column chunks
@@ -286,7 +323,10 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
         for (int c = 0; c < DCW; ++c) Aa[s][c] = Ba[s][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    for (int t = A.tile_ptr[rb]; t < A.tile_ptr[rb + 1]; ++t) {
+    const int t0 = A.tile_ptr[rb], t1 = A.tile_ptr[rb + 1];
+    dma_rows(qown, P.Q, row0, N, rowlen, c0, width, valid, w);
+    dma_rows(gown, P.dO, row0, N, rowlen, c0, width, valid, w);
+    for (int t = t0; t < t1; ++t) {
         const int col0 = A.tile_rc[2 * t + 1] * 16;
         stage_rows(kst, P.K, col0, N, rowlen, c0, width, stride, valid);
         stage_rows(vst, P.V, col0, N, rowlen, c0, width, stride, valid);
@@ -357,7 +397,10 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(WP
             }
             dsum = row[2 * D];
         }
-        bwd_dst_stream<bf16_tag, LH, 2>(R, lp, node, A.rptr[node], A.rptr[node + 1], Av, Bv, dsum, l2, false);
+        const int own = r * width + (int)(lp.col - c0);
+        bwd_dst_stream<bf16_tag, LH, 2>(R, lp, node, A.rptr[node], A.rptr[node + 1], Av, Bv, dsum, l2, false,
+                                        reinterpret_cast<const uint4 *>(qown + own),
+                                        reinterpret_cast<const uint4 *>(gown + own));
         if (lp.g == 0 && lp.act) store_dq<bf16_tag, NV>(P, lp, node, Av, Bv, dsum, l2);
     }
 }
@@ -382,6 +425,10 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(WP
     float *state = lds;                                   // [16][HW][SW]: dK, dV (after the last tile)
     uint16_t *qst = reinterpret_cast<uint16_t *>(lds);   // [16][stride]
     uint16_t *gst = qst + 16 * stride;
+    // the block's own K and V rows for phase 2, [16][width] each, past the
+    // state / staging region
+    uint16_t *kown = reinterpret_cast<uint16_t *>(lds + std::max(16 * HW * SW, 16 * stride));
+    uint16_t *vown = kown + 16 * width;
     const int col0 = cb * 16;
     const int n = l & 15, q4 = l >> 4;
     const int part = w % SPLIT, c0w = part * DCW;        // this wave's output column chunks
@@ -405,7 +452,10 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
         for (int c = 0; c < DCW; ++c) dKa[s][c] = dVa[s][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    for (int x = A.tile_ptr[cb]; x < A.tile_ptr[cb + 1]; ++x) {
+    const int x0 = A.tile_ptr[cb], x1 = A.tile_ptr[cb + 1];
+    dma_rows(kown, P.K, col0, N, rowlen, c0, width, valid, w);
+    dma_rows(vown, P.V, col0, N, rowlen, c0, width, valid, w);
+    for (int x = x0; x < x1; ++x) {
         const int t = A.tile_ids[x];
         const int row0 = A.tile_rc[2 * t] * 16;
         stage_rows(qst, P.Q, row0, N, rowlen, c0, width, stride, valid);
@@ -479,7 +529,10 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(WP
                 dv[k] = row[D + lp.dv * NV + k];
             }
         }
-        bwd_src_stream<bf16_tag, LH, 2>(R, lp, node, A.rptr[node], A.rptr[node + 1], dk, dv, false);
+        const int own = r * width + (int)(lp.col - c0);
+        bwd_src_stream<bf16_tag, LH, 2>(R, lp, node, A.rptr[node], A.rptr[node + 1], dk, dv, false,
+                                        reinterpret_cast<const uint4 *>(kown + own),
+                                        reinterpret_cast<const uint4 *>(vown + own));
         if (lp.g != 0 || !lp.act) continue;
         const int64_t off = (int64_t)node * rowlen + lp.col;
         store_scaled<bf16_tag, NV>(P.dK, off, dk, P.scale);
@@ -491,11 +544,13 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(WP
 
 bool tile_supported(gnn_dtype_t dt, int D) { return dt == GNN_BF16 && (D == 32 || D == 64 || D == 128); }
 
-// LDS of a tile workgroup: the state hand-off buffer overlays the staged rows
+// LDS of a tile workgroup: the state hand-off buffer overlays the staged rows;
+// the own-row copy comes after both
 static size_t tile_lds(int kind, int HW, int D) {
     const size_t stage = (size_t)16 * (HW * D + kRowPad) * 2;
-    if (kind == 0) return std::max((size_t)16 * HW * (D + 3) * 4, stage);
-    return std::max((size_t)16 * HW * (2 * D + 1) * 4, 2 * stage);
+    const size_t own = (size_t)16 * HW * D * 2;   // one table of the block's own rows, unpadded
+    if (kind == 0) return std::max((size_t)16 * HW * (D + 3) * 4, stage) + own;
+    return std::max((size_t)16 * HW * (2 * D + 1) * 4, 2 * stage) + 2 * own;
 }
 
 // waves per head in the backward tile kernels: 8 / HW when that divides the
