@@ -50,7 +50,7 @@ def _case(seed):
     return n, ip, ix, dtype, H, D, opts, rng
 
 
-@pytest.mark.parametrize("seed", range(120))
+@pytest.mark.parametrize("seed", range(400))
 def test_random_configuration(g, seed):
     import torch
     n, ip, ix, dtype, H, D, opts, rng = _case(seed)
