@@ -3,7 +3,8 @@ checked against the oracle: multigraphs from 1 to 3,000 nodes with skewed
 in- and out-degrees, hubs (heavy rows and sources), empty rows and repeated
 entries; fp32 or bf16; H in {1, 2, 3, 4, 8}, D in {16, 32, 64, 128}; no plan,
 or a plan with a random light threshold, chunk, waves per group, launch
-order and tile density. Every case runs the GT forward, the GATv2 forward,
+order and tile density, and in some graphs 16x16 block pairs filled to
+60-100 % (so tiled plans have tiles). Every case runs the GT forward, the GATv2 forward,
 the max reduction and, with a plan, the GT and GATv2 backward, the
 reduction's gradient and both SpMM products."""
 import numpy as np
@@ -36,7 +37,17 @@ def _case(seed):
         src = rng.integers(0, n, d)
         pick = rng.random(d) < 0.3
         src[pick] = popular[rng.integers(0, popular.size, int(pick.sum()))]
-        rows.append(np.sort(src))
+        rows.append(src)
+    if n >= 32 and rng.random() < 0.6:
+        # locally dense spots: 16x16 block pairs filled to 60-100 % (tiles)
+        nb = n // 16
+        for _ in range(int(rng.integers(1, 8))):
+            rb, cb = rng.integers(0, nb, 2)
+            fill = rng.random((16, 16)) < rng.uniform(0.6, 1.0)
+            for a in range(16):
+                rows[rb * 16 + a] = np.concatenate([rows[rb * 16 + a], cb * 16 + np.nonzero(fill[a])[0]])
+    rows = [np.sort(r) for r in rows]
+    deg = np.array([r.size for r in rows], np.int64)
     ip = np.concatenate([[0], np.cumsum(deg)]).astype(np.int32)
     ix = np.concatenate(rows + [np.zeros(0, np.int64)]).astype(np.int32)
     dtype = str(rng.choice(["f32", "bf16"]))
@@ -46,7 +57,7 @@ def _case(seed):
     if rng.random() >= 0.15:
         opts = dict(light_threshold=int(rng.choice([0, 3, 16, 64, 512])), chunk=int(rng.choice([1, 7, 64, 512])),
                     waves_per_group=int(rng.choice([1, 2, 4, 8])), sched_order=int(rng.integers(0, 3)),
-                    tile_density=float(rng.choice([0.0, 0.0, 0.5])), want_csc=True)
+                    tile_density=float(rng.choice([0.0, 0.5, 0.75])), want_csc=True)
     return n, ip, ix, dtype, H, D, opts, rng
 
 
@@ -57,6 +68,8 @@ def test_random_configuration(g, seed):
     say(f"random {seed}: N={n} E={ix.size} max deg={np.diff(ip).max() if n else 0} {dtype} H={H} D={D} plan={opts}")
     ipd, ixd = dev_i32(ip), dev_i32(ix)
     plan = g.gnn_plan_create(ipd, ixd, **opts) if opts else None
+    if plan is not None and opts["tile_density"] > 0:
+        say(f"  tiles {g.gnn_plan_export(plan)['n_tiles']}")
     Q, K, V, dO = rand_feats(rng, n, H, D, dtype, k=4)
     q, k, v, go = (dev_feat(x, dtype) for x in (Q, K, V, dO))
     # GT forward (and backward on a plan)
