@@ -334,8 +334,9 @@ int gnn_plan_timing_read(gnn_plan_t plan, int32_t cap, const char **names /*host
  * its kernels check every graph index before using it as a node-table row: an
  * index outside [0, N) is replaced by row 0, so no access leaves the tables,
  * and the call returns GNN_ERR_BAD_GRAPH after its kernels (it synchronises
- * the stream to read the kernels' flags). Results of good graphs are the same
- * as the normal build's.
+ * the stream to read the kernels' flags, so no call of the checked build can
+ * be captured into a HIP graph). Results of good graphs are the same as the
+ * normal build's.
  * For: debugging callers' graph arrays and the library itself; not for speed.
  */
 int gnn_build_checked(void);

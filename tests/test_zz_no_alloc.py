@@ -141,6 +141,9 @@ def test_noalloc_under_graph_capture(g):
     (another allocation-free call on another graph with heavy rows), equals the
     eager result bit for bit."""
     import torch
+    if g.gnn_build_checked():
+        pytest.skip("the checked build reads its index-check flags after every call (a synchronising copy), "
+                    "which a capturing stream does not allow")
     rp, rx = _graph("gt_chunglu25_n169k", 6000)
     rp2, rx2 = _graph("gatv2_zipf21_n100k", 1500)
     n, n2, H, D = rp.size - 1, rp2.size - 1, 4, 32
