@@ -66,9 +66,11 @@ int gnn_permute_graph(const int32_t *indptr, const int32_t *indices, int32_t N, 
 /*
  * Feature rows in the new order: dst[r] = src[perm[r]] (back = 0), or back to
  * the old order: dst[perm[r]] = src[r] (back = 1). Rows of row_bytes bytes
- * (a multiple of 16, else GNN_ERR_UNSUPPORTED); src and dst distinct and
- * 16-byte aligned (GNN_ERR_ALIGNMENT). perm is checked to name every node
- * once (GNN_ERR_INVALID_ARG); the copy itself is asynchronous on `stream`.
+ * (a multiple of 16, else GNN_ERR_UNSUPPORTED); src and dst distinct (when
+ * N > 0 and row_bytes > 0; empty tables may both be null) and 16-byte aligned
+ * (GNN_ERR_ALIGNMENT). perm is checked to name every node once
+ * (GNN_ERR_INVALID_ARG); the copy itself is asynchronous on `stream`. N == 0
+ * or row_bytes == 0: nothing to do, GNN_OK.
  * Source: as gnn_reorder (applying a reordering to the node features).
  */
 int gnn_permute_rows(const void *src, void *dst, int32_t N, int64_t row_bytes, const int32_t *perm, int32_t back,

@@ -486,7 +486,10 @@ int gnn_permute_graph(const int32_t *indptr, const int32_t *indices, int32_t N, 
 
 int gnn_permute_rows(const void *src, void *dst, int32_t N, int64_t row_bytes, const int32_t *perm, int32_t back,
                      hipStream_t stream) {
-    if (N < 0 || row_bytes < 0 || (N > 0 && (!src || !dst || !perm)) || src == dst) return GNN_ERR_INVALID_ARG;
+    // src == dst is rejected only when there is something to copy: empty
+    // tables (N == 0 or row_bytes == 0) may both be null
+    if (N < 0 || row_bytes < 0 || (N > 0 && (!src || !dst || !perm))) return GNN_ERR_INVALID_ARG;
+    if (N > 0 && row_bytes > 0 && src == dst) return GNN_ERR_INVALID_ARG;
     if (row_bytes % 16) return GNN_ERR_UNSUPPORTED;
     if (!aligned16(src) || !aligned16(dst)) return GNN_ERR_ALIGNMENT;
     if (N == 0 || row_bytes == 0) return GNN_OK;

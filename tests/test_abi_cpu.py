@@ -91,6 +91,7 @@ def test_host_validation(g):
     assert L.gnn_permute_rows(A, A + 8, 10, 32, A, 0, None) == -3
     assert L.gnn_permute_rows(A, A, 10, 32, A, 0, None) == -1                             # src == dst
     assert L.gnn_permute_rows(A, A + 16, 0, 32, A, 0, None) == 0
+    assert L.gnn_permute_rows(None, None, 0, 32, None, 0, None) == 0                      # empty table: no-op
     # SpMM needs a plan, prepared
     assert L.gnn_spmm_prepare(None, 2, None) == -1
     assert L.gnn_spmm(None, A, A, 10, 20, 8, A, A, 0, 0, None) == -1
