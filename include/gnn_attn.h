@@ -299,7 +299,8 @@ int gatv2_attn_fwd(gnn_plan_t plan, const int32_t *indptr, const int32_t *indice
  *   dK_j   = sum_i ds_ij att * phi'(z_ij)           (source projection XS)
  *            + sum_i p_ij dO_i  when V is the same buffer as K
  *   dV_j   = sum_i p_ij dO_i    when V is a separate buffer (dV may be NULL otherwise)
- *   d_att  = sum over all edges of ds_ij phi(z_ij)  (fp32 [H, D], overwritten)
+ *   d_att  = sum over all edges of ds_ij phi(z_ij)  (fp32 [H, D], overwritten;
+ *            zero for a graph without edges, N == 0 included)
  * phi'(z) = 1 for z >= 0 and negative_slope otherwise (the forward's branch).
  * The plan must have been created with want_csc. No atomics: d_att is a
  * fixed-order sum and every output is bitwise reproducible. The plan

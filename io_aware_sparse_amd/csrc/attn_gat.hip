@@ -469,7 +469,13 @@ static int gat_bwd_impl(gnn_plan_t plan, const int32_t *indptr, const int32_t *i
     for (const void *p : {Q, K, V, dO, (const void *)dQ, (const void *)dK})
         if (!aligned16(p)) return GNN_ERR_ALIGNMENT;
     if (sepv && !aligned16(dV)) return GNN_ERR_ALIGNMENT;
-    if (N == 0) return GNN_OK;
+    if (N == 0) {
+        // no edges: d_att, their sum, is zero (the column sum over no chunks)
+        if (d_att)
+            GNN_TRY(launch(plan, K_GAT_DATT, k_col_final, dim3((unsigned)((int64_t)H * D)), dim3(256), 0, stream,
+                           (const float *)nullptr, (int64_t)0, (int64_t)H * D, d_att));
+        return GNN_OK;
+    }
     GNN_TRY(checked_graph(indptr, indices, N, E, stream));
     GatBwdParams GP{};
     BwdParams &P = GP.b;
