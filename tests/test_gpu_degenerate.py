@@ -24,41 +24,47 @@ def g():
 
 
 def _all_calls(g, plan, ip, ix, n, dtype):
-    """Run every compute entry point; returns their outputs (torch tensors)."""
+    """Run every compute entry point; returns their outputs (torch tensors).
+    Every output buffer starts filled with NaN (indices with a sentinel), so
+    an element a call leaves unwritten cannot pass for a zero."""
     import torch
     H, D = 2, 32
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     gen = torch.Generator(device="cuda").manual_seed(3)
     q, k, v, go = (torch.randn((n, H, D), generator=gen, device="cuda", dtype=tdt) for _ in range(4))
     att = torch.randn((H, D), generator=gen, device="cuda")
+    nan = lambda shape, dt=tdt: torch.full(shape, float("nan"), dtype=dt, device="cuda")   # noqa: E731
+    feat, stat, rows = (n, H, D), (n, H), (n, H * D)
     out = {}
-    out["O"], out["L"] = g.gnn_attn_fwd(plan, ip, ix, q, k, v)
+    out["O"], out["L"] = g.gnn_attn_fwd(plan, ip, ix, q, k, v, O=nan(feat), LSE=nan(stat, torch.float32))
     if plan is not None:
-        out["dQ"], out["dK"], out["dV"] = g.gnn_attn_bwd(plan, ip, ix, q, k, v, out["O"], go, out["L"])
-        O2 = torch.empty_like(q)
-        L2 = torch.empty((n, H), dtype=torch.float32, device="cuda")
+        out["dQ"], out["dK"], out["dV"] = g.gnn_attn_bwd(plan, ip, ix, q, k, v, out["O"], go, out["L"],
+                                                         dQ=nan(feat), dK=nan(feat), dV=nan(feat))
+        O2, L2 = nan(feat), nan(stat, torch.float32)
         g.gnn_attn_fwd_noalloc(plan, ip, ix, q, k, v, O2, L2)
         out["O_noalloc"], out["L_noalloc"] = O2, L2
-    out["GO"], out["GL"] = g.gatv2_attn_fwd(plan, ip, ix, q, k, att)
+    out["GO"], out["GL"] = g.gatv2_attn_fwd(plan, ip, ix, q, k, att, O=nan(feat), LSE=nan(stat, torch.float32))
     if plan is not None:
-        out["dXD"], out["dXS"], _, out["d_att"] = g.gatv2_attn_bwd(plan, ip, ix, q, k, att, go, out["GL"])
-    X = q.reshape(n, H * D)
+        out["dXD"], out["dXS"], _, out["d_att"] = g.gatv2_attn_bwd(
+            plan, ip, ix, q, k, att, go, out["GL"], dXD=nan(feat), dXS=nan(feat), d_att=nan((H, D), torch.float32))
+    X = q.reshape(rows)
     out["X"] = X
     for op, msg in (("max", "src"), ("min", "diff")):
-        r, a = g.gnn_reduce_fwd(plan, ip, ix, X, op, msg)
+        r, a = g.gnn_reduce_fwd(plan, ip, ix, X, op, msg, out=nan(rows),
+                                arg=torch.full(rows, 12345, dtype=torch.int32, device="cuda"))
         out[f"red_{op}"], out[f"arg_{op}"] = r, a
         if plan is not None:
-            out[f"dX_{op}"] = g.gnn_reduce_bwd(plan, ip, ix, go.reshape(n, H * D), a, msg)
+            out[f"dX_{op}"] = g.gnn_reduce_bwd(plan, ip, ix, go.reshape(rows), a, msg, dX=nan(rows))
     if plan is not None:
         g.gnn_spmm_prepare(plan, "gcn")
-        out["Y"] = g.gnn_spmm(plan, ip, ix, X)
-        out["YT"] = g.gnn_spmm(plan, ip, ix, X, transpose=True)
+        out["Y"] = g.gnn_spmm(plan, ip, ix, X, Y=nan(rows))
+        out["YT"] = g.gnn_spmm(plan, ip, ix, X, transpose=True, Y=nan(rows))
     for method in ("degree", "rcm"):
         perm = g.gnn_reorder(ip, ix, method)
         out[f"perm_{method}"] = perm
         pip, pix = g.gnn_permute_graph(ip, ix, perm)
         out[f"pip_{method}"] = pip
-        out[f"rows_{method}"] = g.gnn_permute_rows(X, perm)
+        out[f"rows_{method}"] = g.gnn_permute_rows(X, perm, dst=nan(rows))
     torch.cuda.synchronize()
     return out
 
