@@ -72,24 +72,28 @@ def test_random_configuration(g, seed):
         say(f"  tiles {g.gnn_plan_export(plan)['n_tiles']}")
     Q, K, V, dO = rand_feats(rng, n, H, D, dtype, k=4)
     q, k, v, go = (dev_feat(x, dtype) for x in (Q, K, V, dO))
+    # every output buffer starts as NaN: an element a kernel leaves unwritten fails the comparison
+    nan = lambda shape, dt=q.dtype: torch.full(shape, float("nan"), dtype=dt, device="cuda")   # noqa: E731
+    feat, stat = (n, H, D), (n, H)
     # GT forward (and backward on a plan)
-    O, L = g.gnn_attn_fwd(plan, ipd, ixd, q, k, v)
+    O, L = g.gnn_attn_fwd(plan, ipd, ixd, q, k, v, O=nan(feat), LSE=nan(stat, torch.float32))
     ref = oracle.gt_fwd(ip, ix, Q, K, V)
     check("GT O", host(O), ref["O"], ref["SO"], dtype)
     check("GT LSE", host(L), ref["LSE"], ref["SL"], "f32")
     if plan is not None:
-        dq, dk, dv = g.gnn_attn_bwd(plan, ipd, ixd, q, k, v, O, go, L)
+        dq, dk, dv = g.gnn_attn_bwd(plan, ipd, ixd, q, k, v, O, go, L, dQ=nan(feat), dK=nan(feat), dV=nan(feat))
         rb = oracle.gt_bwd(ip, ix, Q, K, V, dO)
         for nm, x in (("dQ", dq), ("dK", dk), ("dV", dv)):
             check(f"GT {nm}", host(x), rb[nm], rb["S" + nm], dtype)
     # GATv2 forward (and backward on a plan), values aliasing XS
     att = (rng.standard_normal((H, D)) / np.sqrt(D)).astype(np.float32)
     a = torch.from_numpy(att).cuda()
-    GO, GL = g.gatv2_attn_fwd(plan, ipd, ixd, q, k, a)
+    GO, GL = g.gatv2_attn_fwd(plan, ipd, ixd, q, k, a, O=nan(feat), LSE=nan(stat, torch.float32))
     rg = oracle.gatv2_fwd(ip, ix, Q, K, att, slope=0.2)
     check("GATv2 O", host(GO), rg["O"], rg["SO"], dtype)
     if plan is not None:
-        gxd, gxs, _, gda = g.gatv2_attn_bwd(plan, ipd, ixd, q, k, a, go, GL)
+        gxd, gxs, _, gda = g.gatv2_attn_bwd(plan, ipd, ixd, q, k, a, go, GL, dXD=nan(feat), dXS=nan(feat),
+                                            d_att=nan((H, D), torch.float32))
         rgb = oracle.gatv2_bwd(ip, ix, Q, K, att, dO, slope=0.2)
         check("GATv2 dXD", host(gxd), rgb["dXD"], rgb["SdXD"], dtype)
         check("GATv2 dXS", host(gxs), rgb["dXS"], rgb["SdXS"], dtype)
@@ -97,18 +101,19 @@ def test_random_configuration(g, seed):
     # max reduction: values and winners bit for bit (and the gradient on a plan)
     F = H * D
     X = q.reshape(n, F)
-    out, arg = g.gnn_reduce_fwd(plan, ipd, ixd, X, "max", "src")
+    out, arg = g.gnn_reduce_fwd(plan, ipd, ixd, X, "max", "src", out=nan((n, F)),
+                                arg=torch.full((n, F), 12345, dtype=torch.int32, device="cuda"))
     rr = oracle.segment_reduce(ip, ix, Q.reshape(n, F), "max", "src")
     torch.cuda.synchronize()
     assert np.array_equal(arg.cpu().numpy(), rr["arg"]), "winners differ"
     assert np.array_equal(out.float().cpu().numpy(), rr["out"]), "values differ"
     if plan is not None:
-        dX = g.gnn_reduce_bwd(plan, ipd, ixd, go.reshape(n, F), arg, "src")
+        dX = g.gnn_reduce_bwd(plan, ipd, ixd, go.reshape(n, F), arg, "src", dX=nan((n, F)))
         rdx, S = oracle.segment_reduce_bwd(ip, ix, dO.reshape(n, F), rr["arg"], "src", want_scale=True)
         check("max dX", host(dX), rdx, S, dtype)
         # SpMM, both products
         g.gnn_spmm_prepare(plan, "gcn")
         for tr in (False, True):
-            Y = g.gnn_spmm(plan, ipd, ixd, X, transpose=tr)
+            Y = g.gnn_spmm(plan, ipd, ixd, X, transpose=tr, Y=nan((n, F)))
             rs = oracle.spmm(ip, ix, Q.reshape(n, F), "gcn", transpose=tr)
             check(f"SpMM transpose={tr}", host(Y), rs["Y"], rs["S"], dtype)
