@@ -147,6 +147,18 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
+def _fresh(t, stream=None):
+    """An output buffer this binding allocated. They start uninitialised;
+    with GNN_POISON_OUTPUTS=1 (a debugging aid) they start as NaN (integer
+    outputs as INT32_MAX), filled on the call's stream, so that an element the
+    library fails to write cannot pass for a plausible value."""
+    if os.environ.get("GNN_POISON_OUTPUTS") == "1" and t.numel():
+        torch = _torch()
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+            t.fill_(float("nan") if t.is_floating_point() else 2 ** 31 - 1)
+    return t
+
+
 def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.float32:
@@ -190,8 +202,8 @@ def gnn_csr_build(src, dst, n_nodes: int, add_self_loops: bool = True, stream=No
     if int(dst.numel()) != m:
         raise ValueError("src and dst differ in length")
     cap = m + (n_nodes if add_self_loops else 0)
-    indptr = torch.empty(n_nodes + 1, dtype=torch.int32, device=src.device)
-    indices = torch.empty(max(cap, 1), dtype=torch.int32, device=src.device)
+    indptr = _fresh(torch.empty(n_nodes + 1, dtype=torch.int32, device=src.device), stream)
+    indices = _fresh(torch.empty(max(cap, 1), dtype=torch.int32, device=src.device), stream)
     e = C.c_int64(0)
     _check(lib().gnn_csr_build(_ptr(src), _ptr(dst), m, int(n_nodes), int(bool(add_self_loops)), _ptr(indptr),
                                _ptr(indices), cap, C.byref(e), _stream(stream)), "gnn_csr_build")
@@ -313,9 +325,9 @@ def gnn_attn_fwd(plan: Optional[Plan], indptr, indices, Q, K, V, O=None, LSE=Non
         raise ValueError("Q rows differ from the graph's node count")
     _feat(K, "K", Q.shape, Q.dtype)
     _feat(V, "V", Q.shape, Q.dtype)
-    O = torch.empty_like(Q) if O is None else _feat(O, "O", Q.shape, Q.dtype)
+    O = _fresh(torch.empty_like(Q), stream) if O is None else _feat(O, "O", Q.shape, Q.dtype)
     if LSE is None and want_lse:
-        LSE = torch.empty((N, H), dtype=torch.float32, device=Q.device)
+        LSE = _fresh(torch.empty((N, H), dtype=torch.float32, device=Q.device), stream)
     _check(lib().gnn_attn_fwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
                               _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), float(scale), _dtype_code(Q),
                               _stream(stream)), "gnn_attn_fwd")
@@ -358,9 +370,9 @@ def gatv2_attn_fwd(plan: Optional[Plan], indptr, indices, XD, XS, att, V=None, n
     V = XS if V is None else _feat(V, "V", XD.shape, XD.dtype)
     if not (att.is_cuda and att.dtype == torch.float32 and att.is_contiguous() and tuple(att.shape) == (H, D)):
         raise TypeError("att must be a contiguous float32 [H, D] device tensor")
-    O = torch.empty_like(XD) if O is None else _feat(O, "O", XD.shape, XD.dtype)
+    O = _fresh(torch.empty_like(XD), stream) if O is None else _feat(O, "O", XD.shape, XD.dtype)
     if LSE is None and want_lse:
-        LSE = torch.empty((N, H), dtype=torch.float32, device=XD.device)
+        LSE = _fresh(torch.empty((N, H), dtype=torch.float32, device=XD.device), stream)
     _check(lib().gatv2_attn_fwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
                                 _ptr(XD), _ptr(XS), _ptr(V), _ptr(att), float(negative_slope), _ptr(O), _ptr(LSE),
                                 _dtype_code(XD), _stream(stream)), "gatv2_attn_fwd")
@@ -380,9 +392,9 @@ def gnn_attn_bwd(plan: Plan, indptr, indices, Q, K, V, O, dO, LSE, dQ=None, dK=N
         _feat(O, "O", Q.shape, Q.dtype)
     if not (LSE.is_cuda and LSE.dtype == torch.float32 and tuple(LSE.shape) == (N, H) and LSE.is_contiguous()):
         raise TypeError("LSE must be a contiguous float32 [N, H] device tensor")
-    dQ = torch.empty_like(Q) if dQ is None else _feat(dQ, "dQ", Q.shape, Q.dtype)
-    dK = torch.empty_like(Q) if dK is None else _feat(dK, "dK", Q.shape, Q.dtype)
-    dV = torch.empty_like(Q) if dV is None else _feat(dV, "dV", Q.shape, Q.dtype)
+    dQ = _fresh(torch.empty_like(Q), stream) if dQ is None else _feat(dQ, "dQ", Q.shape, Q.dtype)
+    dK = _fresh(torch.empty_like(Q), stream) if dK is None else _feat(dK, "dK", Q.shape, Q.dtype)
+    dV = _fresh(torch.empty_like(Q), stream) if dV is None else _feat(dV, "dV", Q.shape, Q.dtype)
     _check(lib().gnn_attn_bwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
                               _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
                               float(scale), _dtype_code(Q), _stream(stream)), "gnn_attn_bwd")
@@ -405,13 +417,13 @@ def gatv2_attn_bwd(plan: Plan, indptr, indices, XD, XS, att, dO, LSE, V=None, ne
         raise TypeError("att must be a contiguous float32 [H, D] device tensor")
     if not (LSE.is_cuda and LSE.dtype == torch.float32 and tuple(LSE.shape) == (N, H) and LSE.is_contiguous()):
         raise TypeError("LSE must be a contiguous float32 [N, H] device tensor")
-    dXD = torch.empty_like(XD) if dXD is None else _feat(dXD, "dXD", XD.shape, XD.dtype)
-    dXS = torch.empty_like(XD) if dXS is None else _feat(dXS, "dXS", XD.shape, XD.dtype)
+    dXD = _fresh(torch.empty_like(XD), stream) if dXD is None else _feat(dXD, "dXD", XD.shape, XD.dtype)
+    dXS = _fresh(torch.empty_like(XD), stream) if dXS is None else _feat(dXS, "dXS", XD.shape, XD.dtype)
     if sep:
-        dV = torch.empty_like(XD) if dV is None else _feat(dV, "dV", XD.shape, XD.dtype)
+        dV = _fresh(torch.empty_like(XD), stream) if dV is None else _feat(dV, "dV", XD.shape, XD.dtype)
     else:
         dV = None
-    d_att = torch.empty((H, D), dtype=torch.float32, device=XD.device) if d_att is None else d_att
+    d_att = _fresh(torch.empty((H, D), dtype=torch.float32, device=XD.device), stream) if d_att is None else d_att
     _check(lib().gatv2_attn_bwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, H, D,
                                 _ptr(XD), _ptr(XS), _ptr(Vt), _ptr(att), float(negative_slope), _ptr(dO), _ptr(LSE),
                                 _ptr(dXD), _ptr(dXS), _ptr(dV), _ptr(d_att), _dtype_code(XD), _stream(stream)),
@@ -453,9 +465,9 @@ def gnn_reduce_fwd(plan: Optional[Plan], indptr, indices, X, op: str = "max", ms
     N, F = X.shape
     if N != n:
         raise ValueError("X rows differ from the graph's node count")
-    out = torch.empty_like(X) if out is None else _rows2d(out, "out", X.shape, X.dtype)
+    out = _fresh(torch.empty_like(X), stream) if out is None else _rows2d(out, "out", X.shape, X.dtype)
     if arg is None and want_arg:
-        arg = torch.empty((N, F), dtype=torch.int32, device=X.device)
+        arg = _fresh(torch.empty((N, F), dtype=torch.int32, device=X.device), stream)
     elif arg is not None:
         _rows2d(arg, "arg", X.shape, torch.int32)
     _check(lib().gnn_reduce_fwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, F, _ptr(X),
@@ -474,7 +486,7 @@ def gnn_reduce_bwd(plan: Plan, indptr, indices, dOut, arg, msg: str = "src", dX=
     if N != n:
         raise ValueError("dOut rows differ from the graph's node count")
     _rows2d(arg, "arg", dOut.shape, torch.int32)
-    dX = torch.empty_like(dOut) if dX is None else _rows2d(dX, "dX", dOut.shape, dOut.dtype)
+    dX = _fresh(torch.empty_like(dOut), stream) if dX is None else _rows2d(dX, "dX", dOut.shape, dOut.dtype)
     _check(lib().gnn_reduce_bwd(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, F, _ptr(dOut),
                                 _ptr(arg), _ptr(dX), REDUCE_MSGS[msg], _dtype_code(dOut), _stream(stream)),
            "gnn_reduce_bwd")
@@ -495,7 +507,7 @@ def gnn_spmm(plan: Plan, indptr, indices, X, transpose: bool = False, Y=None, st
     N, F = X.shape
     if N != n:
         raise ValueError("X rows differ from the graph's node count")
-    Y = torch.empty_like(X) if Y is None else _rows2d(Y, "Y", X.shape, X.dtype)
+    Y = _fresh(torch.empty_like(X), stream) if Y is None else _rows2d(Y, "Y", X.shape, X.dtype)
     _check(lib().gnn_spmm(_plan_handle(plan), _ptr(indptr), _ptr(indices) if e else None, N, e, F, _ptr(X), _ptr(Y),
                           int(bool(transpose)), _dtype_code(X), _stream(stream)), "gnn_spmm")
     return Y
@@ -505,7 +517,7 @@ def gnn_reorder(indptr, indices, method: str = "rcm", stream=None):
     """Node order for relabelling (perm[new] = old, int32 device tensor)."""
     torch = _torch()
     n, e = _graph(indptr, indices)
-    perm = torch.empty(max(n, 0), dtype=torch.int32, device=indptr.device)
+    perm = _fresh(torch.empty(max(n, 0), dtype=torch.int32, device=indptr.device), stream)
     _check(lib().gnn_reorder(_ptr(indptr), _ptr(indices) if e else None, n, e, ORDERS[method], _ptr(perm),
                              _stream(stream)), "gnn_reorder")
     return perm
@@ -517,8 +529,8 @@ def gnn_permute_graph(indptr, indices, perm, stream=None):
     n, e = _graph(indptr, indices)
     if perm.dtype != torch.int32 or not perm.is_cuda or perm.numel() != n or not perm.is_contiguous():
         raise TypeError("perm must be a contiguous int32 device tensor of N entries")
-    nip = torch.empty_like(indptr)
-    nix = torch.empty_like(indices)
+    nip = _fresh(torch.empty_like(indptr), stream)
+    nix = _fresh(torch.empty_like(indices), stream)
     _check(lib().gnn_permute_graph(_ptr(indptr), _ptr(indices) if e else None, n, e, _ptr(perm), _ptr(nip),
                                    _ptr(nix) if e else None, _stream(stream)), "gnn_permute_graph")
     return nip, nix
@@ -533,7 +545,7 @@ def gnn_permute_rows(src, perm, back: bool = False, dst=None, stream=None):
     n = src.shape[0]
     if perm.dtype != torch.int32 or perm.numel() != n or not perm.is_contiguous():
         raise TypeError("perm must be a contiguous int32 tensor of src.shape[0] entries")
-    dst = torch.empty_like(src) if dst is None else dst
+    dst = _fresh(torch.empty_like(src), stream) if dst is None else dst
     row_bytes = src[0].numel() * src.element_size() if n else 0
     _check(lib().gnn_permute_rows(_ptr(src), _ptr(dst), n, row_bytes, _ptr(perm), int(bool(back)), _stream(stream)),
            "gnn_permute_rows")
