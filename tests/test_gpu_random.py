@@ -6,7 +6,8 @@ or a plan with a random light threshold, chunk, waves per group, launch
 order and tile density, and in some graphs 16x16 block pairs filled to
 60-100 % (so tiled plans have tiles). Every case runs the GT forward, the GATv2 forward,
 the max reduction and, with a plan, the GT and GATv2 backward, the
-reduction's gradient and both SpMM products."""
+reduction's gradient and both SpMM products, with guard bands around every
+output and a check that no input changed."""
 import numpy as np
 import pytest
 
@@ -72,9 +73,22 @@ def test_random_configuration(g, seed):
         say(f"  tiles {g.gnn_plan_export(plan)['n_tiles']}")
     Q, K, V, dO = rand_feats(rng, n, H, D, dtype, k=4)
     q, k, v, go = (dev_feat(x, dtype) for x in (Q, K, V, dO))
-    # every output buffer starts as NaN: an element a kernel leaves unwritten fails the comparison
-    nan = lambda shape, dt=q.dtype: torch.full(shape, float("nan"), dtype=dt, device="cuda")   # noqa: E731
+    # Every output buffer starts as NaN (an element a kernel leaves unwritten
+    # fails the comparison) and sits between two guard bands of 64 NaN
+    # elements that must stay untouched (a write past either end of an output
+    # shows up there); the inputs must be left as they were.
+    guards, G = [], 64
+
+    def guarded(shape, dt, fill):
+        size = int(np.prod(shape))
+        b = torch.full((size + 2 * G,), fill, dtype=dt, device="cuda")
+        guards.append((b, size, fill))
+        return b[G:G + size].view(shape)
+
+    nan = lambda shape, dt=q.dtype: guarded(shape, dt, float("nan"))                    # noqa: E731
     feat, stat = (n, H, D), (n, H)
+    inputs = {"indptr": ipd, "indices": ixd, "Q": q, "K": k, "V": v, "dO": go}
+    before = {nm: t.clone() for nm, t in inputs.items()}
     # GT forward (and backward on a plan)
     O, L = g.gnn_attn_fwd(plan, ipd, ixd, q, k, v, O=nan(feat), LSE=nan(stat, torch.float32))
     ref = oracle.gt_fwd(ip, ix, Q, K, V)
@@ -102,7 +116,7 @@ def test_random_configuration(g, seed):
     F = H * D
     X = q.reshape(n, F)
     out, arg = g.gnn_reduce_fwd(plan, ipd, ixd, X, "max", "src", out=nan((n, F)),
-                                arg=torch.full((n, F), 12345, dtype=torch.int32, device="cuda"))
+                                arg=guarded((n, F), torch.int32, 12345))
     rr = oracle.segment_reduce(ip, ix, Q.reshape(n, F), "max", "src")
     torch.cuda.synchronize()
     assert np.array_equal(arg.cpu().numpy(), rr["arg"]), "winners differ"
@@ -117,3 +131,10 @@ def test_random_configuration(g, seed):
             Y = g.gnn_spmm(plan, ipd, ixd, X, transpose=tr, Y=nan((n, F)))
             rs = oracle.spmm(ip, ix, Q.reshape(n, F), "gcn", transpose=tr)
             check(f"SpMM transpose={tr}", host(Y), rs["Y"], rs["S"], dtype)
+    torch.cuda.synchronize()
+    for b, size, fill in guards:
+        band = torch.cat([b[:G], b[G + size:]])
+        ok = torch.isnan(band).all() if b.is_floating_point() else (band == fill).all()
+        assert ok.item(), "a write landed outside an output"
+    for nm, t in inputs.items():
+        assert torch.equal(t, before[nm]), f"input {nm} was modified"
