@@ -95,6 +95,14 @@ typedef struct {
                                 of degree > max(1, light_threshold/4) first, by descending
                                 floor(log2(degree)), then the rest by id. Outputs do not
                                 depend on it                                                   */
+    int32_t xcd_split;       /* 1 (default): also cut the heavy rows at the boundaries of 8
+                                equal source-id ranges into groups of at most C*W entries,
+                                each reading one range, and launch them so that the 8 XCDs
+                                each take one range (their L2s then hold what they gather);
+                                the forward uses them when a node's gathered rows (K, plus V
+                                unless it aliases K) over N/8 nodes take at most 12 MiB and
+                                all heads fit one head group; results differ from the plain
+                                groups by rounding only. 0: not built. Needs sorted rows    */
 } gnn_plan_opts;
 
 /* Fill *opts with the defaults above. Returns GNN_ERR_INVALID_ARG if opts is NULL. */
@@ -197,6 +205,16 @@ typedef struct {
                                    light_by_degree, each given a wave of its own by the packed
                                    SpMM and attention-forward launches */
     int32_t c_n_long_light;     /* the same over out-degrees and c_light_by_degree (want_csc) */
+    /* source-range split of the heavy rows (xcd_split; n_xsplit_groups = 0: none) */
+    int32_t n_xsplit_groups, n_xsplit_slots;
+    const int32_t *xsplit_groups;      /* [n_xsplit_groups][3] (node, e0, e1): for each heavy node
+                                          in heavy_ids order, its entries of each source range r
+                                          (sources in [r*ceil(N/8), (r+1)*ceil(N/8)), r = 0..7, in
+                                          order) cut into ceil(len / (C*W)) near-equal groups,
+                                          group j = [a + len*j/k, a + len*(j+1)/k)              */
+    const int32_t *xsplit_partial_ofs; /* [n_heavy+1] group range of each heavy node             */
+    const int32_t *xsplit_order;       /* [n_xsplit_slots] launch slot i*8 + r: the i-th group of
+                                          range r, or -1; n_xsplit_slots = 8 * the largest count */
 } gnn_plan_info;
 
 int gnn_plan_export(gnn_plan_t plan, gnn_plan_info *info /*host*/);

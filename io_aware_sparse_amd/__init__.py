@@ -48,7 +48,8 @@ class GnnError(RuntimeError):
 
 class PlanOpts(C.Structure):
     _fields_ = [("light_threshold", C.c_int32), ("chunk", C.c_int32), ("waves_per_group", C.c_int32),
-                ("tile_density", C.c_float), ("want_csc", C.c_int32), ("sched_order", C.c_int32)]
+                ("tile_density", C.c_float), ("want_csc", C.c_int32), ("sched_order", C.c_int32),
+                ("xcd_split", C.c_int32)]
 
 
 _P32 = C.POINTER(C.c_int32)
@@ -75,7 +76,9 @@ class PlanInfo(C.Structure):
                 ("largest_workspace_alloc", C.c_int64), ("rows_sorted", C.c_int32),
                 ("light_by_degree", C.c_void_p), ("c_light_by_degree", C.c_void_p), ("spmm_norm", C.c_int32),
                 ("spmm_w", C.c_void_p), ("spmm_cw", C.c_void_p),
-                ("n_long_light", C.c_int32), ("c_n_long_light", C.c_int32)]
+                ("n_long_light", C.c_int32), ("c_n_long_light", C.c_int32),
+                ("n_xsplit_groups", C.c_int32), ("n_xsplit_slots", C.c_int32), ("xsplit_groups", C.c_void_p),
+                ("xsplit_partial_ofs", C.c_void_p), ("xsplit_order", C.c_void_p)]
 
 
 _lib = None
@@ -232,12 +235,14 @@ class Plan:
 
 
 def gnn_plan_create(indptr, indices, light_threshold: int = 512, chunk: int = 512, waves_per_group: int = 4,
-                    tile_density: float = 0.0, want_csc: bool = False, sched_order: int = 2, stream=None) -> Plan:
+                    tile_density: float = 0.0, want_csc: bool = False, sched_order: int = 2, xcd_split: bool = True,
+                    stream=None) -> Plan:
     n, e = _graph(indptr, indices)
     o = PlanOpts()
     lib().gnn_plan_opts_default(C.byref(o))
     o.light_threshold, o.chunk, o.waves_per_group = int(light_threshold), int(chunk), int(waves_per_group)
     o.tile_density, o.want_csc, o.sched_order = float(tile_density), int(bool(want_csc)), int(sched_order)
+    o.xcd_split = int(bool(xcd_split))
     h = C.c_void_p()
     _check(lib().gnn_plan_create(_ptr(indptr), _ptr(indices) if e else None, n, e, C.byref(o), _stream(stream),
                                  C.byref(h)), "gnn_plan_create")
@@ -288,6 +293,10 @@ def gnn_plan_export(plan: Plan, arrays: bool = False) -> dict:
             d["c_partial_ofs"] = _copy_dev(info.c_partial_ofs, info.c_n_heavy + 1, np.int32)
             d["c_light_sched"] = _copy_dev(info.c_light_sched, info.c_n_light, np.int32)
             d["c_light_by_degree"] = _copy_dev(info.c_light_by_degree, info.c_n_light, np.int32)
+        if info.n_xsplit_groups:
+            d["xsplit_groups"] = _copy_dev(info.xsplit_groups, 3 * info.n_xsplit_groups, np.int32).reshape(-1, 3)
+            d["xsplit_partial_ofs"] = _copy_dev(info.xsplit_partial_ofs, info.n_heavy + 1, np.int32)
+            d["xsplit_order"] = _copy_dev(info.xsplit_order, info.n_xsplit_slots, np.int32)
         if info.spmm_w:
             d["spmm_w"] = _copy_dev(info.spmm_w, info.n_edges, np.float32)
         if info.spmm_cw:

@@ -38,11 +38,18 @@ __global__ __launch_bounds__(512) void k_fwd_main(FwdParams P) {
     constexpr int NV = VT::N;
     extern __shared__ float lds[];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int heavy_blocks = P.n_groups * P.g.NHG;
+    const int heavy_blocks = P.n_slots * P.g.NHG;
     if ((int)blockIdx.x < heavy_blocks) {
-        const int grp = blockIdx.x / P.g.NHG, hg = blockIdx.x % P.g.NHG;
+        int grp = blockIdx.x / P.g.NHG;
+        const int hg = blockIdx.x % P.g.NHG;
+        if (P.gperm) {
+            grp = P.gperm[grp];
+            if (grp < 0) return;              // an empty slot: the whole workgroup leaves
+        }
         const int node = P.groups[3 * grp], g0 = P.groups[3 * grp + 1], g1 = P.groups[3 * grp + 2];
-        const int e0 = min(g1, g0 + w * P.C), e1 = min(g1, e0 + P.C);
+        // XCD-ordered groups split their span evenly over the W waves
+        const int cw = P.gperm ? (g1 - g0 + P.W - 1) / P.W : P.C;
+        const int e0 = min(g1, g0 + w * cw), e1 = min(g1, e0 + cw);
         const LanePos lp = lane_pos<LH, NV>(P.g, hg);
         SoftState<NV> st;
         fwd_stream<T, LH, MODE, U>(P, lp, node, e0, e1, st);
@@ -312,7 +319,7 @@ static int launch_fwd_main(gnn_plan_t plan, const FwdParams &P, hipStream_t s) {
     const int kind_main = MODE == M_GT ? K_FWD_MAIN : K_GAT_MAIN;
     const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NHG
                                          : P.n_long + ((int64_t)P.n_light - P.n_long + RPW - 1) / RPW;
-    const int64_t blocks = (int64_t)P.n_groups * P.g.NHG + (light_waves + P.W - 1) / P.W;
+    const int64_t blocks = (int64_t)P.n_slots * P.g.NHG + (light_waves + P.W - 1) / P.W;
     if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
     const size_t lds = P.n_groups ? (size_t)P.W * (1 << P.g.lr_shift) * (NV + 2) * sizeof(float) : 0;
     return launch(plan, kind_main, k_fwd_main<T, LH, MODE, U, RPW>, dim3((unsigned)blocks), dim3(64 * P.W), lds, s,
@@ -400,6 +407,21 @@ static int fwd_common(gnn_plan_t plan, const int32_t *indptr, const int32_t *ind
         P.heavy = as<int32_t>(plan->fwd.heavy);
         P.partial_ofs = as<int32_t>(plan->fwd.partial_ofs);
         P.n_heavy = plan->fwd.n_heavy;
+        P.gperm = nullptr;
+        P.n_slots = P.n_groups;
+        // heavy rows split at source ranges, XCD-ordered: worth it when one
+        // range's gathered rows come near an XCD's L2 (a 6.4 MiB range of a
+        // 51 MiB table gathers about twice as fast as the whole table; 22 MiB
+        // ranges gain nothing), and only with one head group, whose blocks
+        // are the launch slots themselves
+        const int64_t gathered = (int64_t)N * H * D * (dtype == GNN_BF16 ? 2 : 4) * (mode == M_GAT_ALIAS ? 1 : 2);
+        if (plan->xsplit.n_groups && P.g.NHG == 1 && (gathered + 7) / 8 <= kXsplitMaxRangeBytes) {
+            P.groups = as<int32_t>(plan->xsplit.groups);
+            P.n_groups = plan->xsplit.n_groups;
+            P.partial_ofs = as<int32_t>(plan->xsplit.partial_ofs);
+            P.gperm = as<int32_t>(plan->xsplit.order);
+            P.n_slots = plan->xsplit.n_slots;
+        }
         P.C = plan->opts.chunk;
         P.W = plan->opts.waves_per_group;
         if (P.n_groups) {

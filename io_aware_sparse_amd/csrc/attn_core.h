@@ -41,6 +41,10 @@ struct FwdParams {
     int32_t n_heavy;
     float *ws_acc, *ws_ml;
     int32_t W;
+    // XCD-ordered heavy groups: launch slot -> group (-1: an empty slot), and
+    // the number of slots (a multiple of 8); null: slot i runs group i
+    const int32_t *gperm;
+    int32_t n_slots;
 };
 
 // per-lane position inside the wave's (node, head group) slice

@@ -62,6 +62,20 @@ struct Buckets {
     int32_t n_long = 0;
 };
 
+// The forward's heavy rows cut at the boundaries of 8 equal source-id ranges
+// and then into groups of at most C*W entries: every group reads sources of
+// one range only. Launch slot i*8 + r holds the i-th group of range r (-1
+// when range r has fewer), so with one block per slot and blocks dealt to the
+// 8 XCDs round-robin, each XCD gathers from one eighth of the table and its
+// L2 holds much more of what it reads. Partial slots stay per node and
+// contiguous (partial_ofs), so the merge is unchanged.
+struct XSplit {
+    int32_t n_groups = 0, n_slots = 0;
+    DevBuf groups, partial_ofs, order;
+};
+// the forward uses the split groups when one range's gathered rows take at most this
+constexpr int64_t kXsplitMaxRangeBytes = 12ll << 20;
+
 // A light row longer than this gets a wave of its own in the packed SpMM and
 // attention-forward launches rather than a share of one (a packed row steps
 // through its entries a few at a time, so the longest rows would set the
@@ -125,6 +139,7 @@ struct gnn_plan_s {
     bool rows_sorted = false;  // every row's sources in non-decreasing order (checked at creation)
     gnn_plan_opts opts{};
     gnn::Buckets fwd;          // in-degree buckets over the CSR
+    gnn::XSplit xsplit;        // the forward's heavy rows split at source ranges (see XSplit)
     bool has_csc = false;
     gnn::DevBuf cindptr, cindices;
     gnn::Buckets bwd;          // out-degree buckets over the transposed adjacency

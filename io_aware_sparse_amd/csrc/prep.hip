@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <vector>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -624,6 +625,83 @@ static int check_rows_sorted(const int32_t *indptr, const int32_t *indices, int3
     return rc;
 }
 
+// pos[9k + b]: the first entry of heavy row k whose source is >= b * R (b = 0..7),
+// pos[9k + 8] the row's end (the row's sources ascend)
+__global__ void k_range_bounds(const int32_t *indptr, const int32_t *indices, const int32_t *heavy, int32_t n_heavy,
+                               int32_t R, int32_t *pos) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)n_heavy * 9) return;
+    const int32_t k = (int32_t)(t / 9), b = (int32_t)(t % 9);
+    const int32_t node = heavy[k];
+    int32_t lo = indptr[node], hi = indptr[node + 1];
+    if (b == 8) {
+        pos[t] = hi;
+        return;
+    }
+    const int64_t key = (int64_t)b * R;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo) / 2;
+        if (indices[mid] < key) lo = mid + 1;
+        else hi = mid;
+    }
+    pos[t] = lo;
+}
+
+// The XSplit structure of a plan (see internal.h); nothing when there are no
+// heavy rows or the rows are not sorted.
+static int build_xsplit(gnn_plan_s *p, hipStream_t s) {
+    const Buckets &b = p->fwd;
+    XSplit &x = p->xsplit;
+    if (b.n_heavy == 0 || !p->rows_sorted) return GNN_OK;
+    const int32_t R = (int32_t)((p->n_nodes + 7) / 8);
+    const int64_t span = (int64_t)p->opts.chunk * p->opts.waves_per_group;
+    DevBuf pos;
+    GNN_TRY(dev_alloc(pos, (size_t)b.n_heavy * 9 * 4));
+    hipLaunchKernelGGL(k_range_bounds, grid1d((int64_t)b.n_heavy * 9), dim3(256), 0, s, p->indptr, p->indices,
+                       as<int32_t>(b.heavy), b.n_heavy, R, as<int32_t>(pos));
+    std::vector<int32_t> hpos((size_t)b.n_heavy * 9), hheavy((size_t)b.n_heavy);
+    if (hipMemcpyAsync(hpos.data(), pos.p, hpos.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(hheavy.data(), b.heavy.p, hheavy.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+        set_hip_error(hipGetLastError(), "source-range split");
+        dev_free(pos);
+        return GNN_ERR_HIP;
+    }
+    dev_free(pos);
+    std::vector<int32_t> groups, pofs((size_t)b.n_heavy + 1), lists[8];
+    int32_t ng = 0;
+    for (int32_t k = 0; k < b.n_heavy; ++k) {
+        pofs[k] = ng;
+        for (int r = 0; r < 8; ++r) {
+            const int64_t a = hpos[(size_t)k * 9 + r], len = hpos[(size_t)k * 9 + r + 1] - a;
+            if (len <= 0) continue;
+            const int64_t cnt = (len + span - 1) / span;
+            for (int64_t j = 0; j < cnt; ++j) {
+                groups.push_back(hheavy[k]);
+                groups.push_back((int32_t)(a + len * j / cnt));
+                groups.push_back((int32_t)(a + len * (j + 1) / cnt));
+                lists[r].push_back(ng++);
+            }
+        }
+    }
+    pofs[b.n_heavy] = ng;
+    size_t most = 0;
+    for (const auto &l : lists) most = std::max(most, l.size());
+    std::vector<int32_t> order(8 * most, -1);
+    for (int r = 0; r < 8; ++r)
+        for (size_t i = 0; i < lists[r].size(); ++i) order[i * 8 + r] = lists[r][i];
+    GNN_TRY(dev_alloc(x.groups, std::max<size_t>(groups.size(), 1) * 4));
+    GNN_TRY(dev_alloc(x.partial_ofs, pofs.size() * 4));
+    GNN_TRY(dev_alloc(x.order, std::max<size_t>(order.size(), 1) * 4));
+    GNN_HIP(hipMemcpyAsync(x.groups.p, groups.data(), groups.size() * 4, hipMemcpyHostToDevice, s));
+    GNN_HIP(hipMemcpyAsync(x.partial_ofs.p, pofs.data(), pofs.size() * 4, hipMemcpyHostToDevice, s));
+    GNN_HIP(hipMemcpyAsync(x.order.p, order.data(), order.size() * 4, hipMemcpyHostToDevice, s));
+    GNN_HIP(hipStreamSynchronize(s));
+    x.n_groups = ng;
+    x.n_slots = (int32_t)order.size();
+    return GNN_OK;
+}
+
 int validate_csr(const int32_t *indptr, const int32_t *indices, int32_t n, int64_t e, hipStream_t s) {
     DevBuf tmp;
     GNN_TRY(dev_alloc(tmp, 64));
@@ -675,7 +753,8 @@ int build_transpose(const int32_t *indptr, const int32_t *indices, int32_t n, in
 using namespace gnn;
 
 std::vector<DevBuf *> gnn_plan_s::structures() {
-    return {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &fwd.sched, &fwd.by_degree, &cindptr, &cindices,
+    return {&fwd.light, &fwd.heavy, &fwd.groups, &fwd.partial_ofs, &fwd.sched, &fwd.by_degree, &xsplit.groups,
+            &xsplit.partial_ofs, &xsplit.order, &cindptr, &cindices,
             &bwd.light, &bwd.heavy, &bwd.groups, &bwd.partial_ofs, &bwd.sched, &bwd.by_degree, &tile_rc, &tile_mask,
             &tile_ptr, &trb, &rindptr, &rindices, &light_nt, &ctile, &ctile_ptr, &tcb, &rcindptr, &rcindices,
             &c_light_nt, &spmm_w, &spmm_cw, &spmm_rng, &spmm_crng, &spmm_rw, &spmm_rcw};
@@ -743,6 +822,7 @@ int gnn_plan_opts_default(gnn_plan_opts *o) {
     o->tile_density = 0.0f;
     o->want_csc = 0;
     o->sched_order = 2;
+    o->xcd_split = 1;
     return GNN_OK;
 }
 
@@ -802,6 +882,7 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
         !(o.waves_per_group == 1 || o.waves_per_group == 2 || o.waves_per_group == 4 || o.waves_per_group == 8))
         return GNN_ERR_INVALID_ARG;
     if (o.tile_density > 1.0f || o.sched_order < 0 || o.sched_order > 2) return GNN_ERR_INVALID_ARG;
+    if (o.xcd_split != 0 && o.xcd_split != 1) return GNN_ERR_INVALID_ARG;
     if ((int64_t)o.chunk * o.waves_per_group > kMaxGroupSpan) return GNN_ERR_INVALID_ARG;
 
     gnn_plan_s *p = new (std::nothrow) gnn_plan_s();
@@ -816,6 +897,7 @@ int gnn_plan_create(const int32_t *indptr, const int32_t *indices, int32_t n_nod
     if (rc == GNN_OK)
         rc = build_buckets(indptr, n_nodes, o.light_threshold, o.chunk, o.waves_per_group, o.sched_order, p->fwd,
                            stream, true);
+    if (rc == GNN_OK && o.xcd_split) rc = build_xsplit(p, stream);
     if (rc == GNN_OK && o.want_csc) {
         rc = build_transpose(indptr, indices, n_nodes, n_edges, p->cindptr, p->cindices, stream);
         if (rc == GNN_OK) {
@@ -895,6 +977,11 @@ int gnn_plan_export(gnn_plan_t p, gnn_plan_info *info) {
     info->spmm_cw = as<float>(p->spmm_cw);
     info->n_long_light = p->fwd.n_long;
     info->c_n_long_light = p->bwd.n_long;
+    info->n_xsplit_groups = p->xsplit.n_groups;
+    info->n_xsplit_slots = p->xsplit.n_slots;
+    info->xsplit_groups = as<int32_t>(p->xsplit.groups);
+    info->xsplit_partial_ofs = as<int32_t>(p->xsplit.partial_ofs);
+    info->xsplit_order = as<int32_t>(p->xsplit.order);
     return GNN_OK;
 }
 

@@ -152,6 +152,47 @@ def bucketing(indptr, threshold: int, chunk: int, waves: int):
                 groups=groups.astype(np.int32), partial_ofs=partial_ofs.astype(np.int32))
 
 
+def xsplit(indptr, indices, heavy, n_nodes: int, chunk: int, waves: int):
+    """Source-range split of the heavy rows (plan option xcd_split).
+
+    The node ids split into 8 ranges of R = ceil(N / 8) ids (range r holds
+    sources r*R .. (r+1)*R - 1). For each heavy node in the given order, each
+    range's part of its (ascending) entries, a contiguous run of len entries
+    starting at position a, becomes k = ceil(len / (chunk * waves)) groups
+    (node, a + len*j // k, a + len*(j+1) // k), j = 0..k-1; empty parts give
+    none. partial_ofs[k] .. partial_ofs[k+1] are node k's groups. The launch
+    order puts the i-th group of range r at slot 8*i + r and -1 in the slots
+    a range has no group for, with 8 * (the largest per-range count) slots.
+
+    Returns dict groups int32 [G, 3], partial_ofs int32 [n_heavy + 1],
+    order int32 [S]."""
+    ip = np.asarray(indptr, np.int64)
+    ix = np.asarray(indices, np.int64)
+    R = -(-int(n_nodes) // 8)
+    span = int(chunk) * int(waves)
+    groups, pofs, per_range = [], [0], [[] for _ in range(8)]
+    for node in np.asarray(heavy, np.int64):
+        e0, e1 = int(ip[node]), int(ip[node + 1])
+        src = ix[e0:e1]
+        for r in range(8):
+            a = e0 + int(np.searchsorted(src, r * R, side="left"))
+            b = e1 if r == 7 else e0 + int(np.searchsorted(src, (r + 1) * R, side="left"))
+            n = b - a
+            if n <= 0:
+                continue
+            k = -(-n // span)
+            for j in range(k):
+                per_range[r].append(len(groups))
+                groups.append((int(node), a + n * j // k, a + n * (j + 1) // k))
+        pofs.append(len(groups))
+    most = max(len(l) for l in per_range)
+    order = np.full(8 * most, -1, np.int64)
+    for r, l in enumerate(per_range):
+        order[8 * np.arange(len(l), dtype=np.int64) + r] = l
+    g = np.asarray(groups, np.int64).reshape(-1, 3)
+    return dict(groups=g.astype(np.int32), partial_ofs=np.asarray(pofs, np.int32), order=order.astype(np.int32))
+
+
 def launch_order(indptr, light, order: int = 2, threshold: int = 512):
     """Launch order of the light nodes (kernel results do not depend on it).
 

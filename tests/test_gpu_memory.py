@@ -76,8 +76,17 @@ def _library_bytes(fn):
     return out, (free0 - free1) - (res1 - res0)
 
 
-def _ws_fwd(d, H, D):
-    return d["n_groups"] * (H * D + 2 * H) * 4
+def _ws_fwd(d, N, H, D, dtype="f32", gatv2=False):
+    """Forward workspace: one partial (acc, m, l) per heavy group. The forward
+    takes the source-range split groups when the plan has them, all heads fit
+    one head group and one eighth of the gathered tables is at most 12 MiB
+    (the rule the header states), else the plain groups."""
+    size = 2 if dtype == "bf16" else 4
+    lanes = D // (8 if dtype == "bf16" else 4)
+    one_group = H <= 64 // lanes
+    gathered = N * H * D * size * (1 if gatv2 else 2)
+    split = d["n_xsplit_groups"] > 0 and one_group and (gathered + 7) // 8 <= 12 << 20
+    return (d["n_xsplit_groups"] if split else d["n_groups"]) * (H * D + 2 * H) * 4
 
 
 def _ws_bwd(d, N, H, D, gat):
@@ -142,7 +151,7 @@ def test_memory_audit(g, name, tiles):
             def bwd():
                 O, L = holder["fwd"]
                 holder["bwd"] = g.gnn_attn_bwd(plan, ip, ix, q, k, v, O, go, L)
-    _audit(g, plan, wl, E, "forward", fwd, _ws_fwd(d, H, D))
+    _audit(g, plan, wl, E, "forward", fwd, _ws_fwd(d, N, H, D, wl.dtype, wl.kind == "gatv2"))
     if backward:
         _audit(g, plan, wl, E, "backward", bwd, _ws_bwd(d, N, H, D, wl.kind == "gatv2"))
 
@@ -181,14 +190,14 @@ def test_alloc_cap_fails_cleanly_midway(g, monkeypatch):
     H, D = 4, 32
     q = torch.randn(n, H, D, device="cuda")
     O = torch.full_like(q, 5.0)
-    monkeypatch.setenv("GNN_ALLOC_CAP_BYTES", str(_ws_fwd(d, H, D) - 1))
+    monkeypatch.setenv("GNN_ALLOC_CAP_BYTES", str(_ws_fwd(d, n, H, D) - 1))
     with pytest.raises(GnnError) as e:
         g.gnn_attn_fwd(plan, ip, ix, q, q, q, O=O)
     assert e.value.status == -4
     torch.cuda.synchronize()
     assert torch.all(O == 5.0) and g.gnn_plan_export(plan)["workspace_bytes"] == 0
-    monkeypatch.setenv("GNN_ALLOC_CAP_BYTES", str(_ws_fwd(d, H, D)))
+    monkeypatch.setenv("GNN_ALLOC_CAP_BYTES", str(_ws_fwd(d, n, H, D)))
     g.gnn_attn_fwd(plan, ip, ix, q, q, q, O=O)
     torch.cuda.synchronize()
-    assert g.gnn_plan_export(plan)["workspace_bytes"] == _ws_fwd(d, H, D)
+    assert g.gnn_plan_export(plan)["workspace_bytes"] == _ws_fwd(d, n, H, D)
     assert not torch.any(O == 5.0)

@@ -83,6 +83,44 @@ def test_buckets_and_csc(g, T, C, W, order):
     assert d["c_n_long_light"] == int((np.diff(cip)[cref["light"]] > 128).sum())
     assert np.array_equal(d["c_light_by_degree"], oracle.launch_order(cip, cref["light"], 3, T))
     assert d["n_light"] + d["n_heavy"] == n
+    # the source-range split of the heavy rows (built by default on sorted rows)
+    if ref["heavy"].size:
+        xref = oracle.xsplit(rp, rx, ref["heavy"], n, C, W)
+        for k in ("groups", "partial_ofs", "order"):
+            assert np.array_equal(d["xsplit_" + k], xref[k]), "xsplit_" + k
+    else:
+        assert d["n_xsplit_groups"] == 0
+
+
+@pytest.mark.parametrize("name,n", [("gt_chunglu25_n169k", 20000), ("gt_comm16_n1m_deg100", 4096),
+                                    ("gatv2_zipf21_n100k", 100000)])
+def test_xsplit(g, name, n):
+    """The source-range split bit for bit against the oracle on other graph
+    shapes (the full-size Zipf graph among them); none without the option or
+    on rows that are not sorted."""
+    wl = workloads.make(name, n, features=False)
+    n = wl.n_nodes
+    ip, ix, rp, rx = _csr_case(g, wl.src, wl.dst, n, True)
+    for T, C, W in ((512, 512, 4), (16, 8, 2)):
+        d = g.gnn_plan_export(g.gnn_plan_create(ip, ix, light_threshold=T, chunk=C, waves_per_group=W), arrays=True)
+        heavy = oracle.bucketing(rp, T, C, W)["heavy"]
+        say(f"xsplit {name} T={T}: {d['n_xsplit_groups']} groups for {heavy.size} heavy rows, "
+            f"{d['n_xsplit_slots']} slots")
+        if heavy.size == 0:
+            assert d["n_xsplit_groups"] == 0
+        else:
+            xref = oracle.xsplit(rp, rx, heavy, n, C, W)
+            for k in ("groups", "partial_ofs", "order"):
+                assert np.array_equal(d["xsplit_" + k], xref[k]), ("xsplit_" + k, T)
+        off = g.gnn_plan_export(g.gnn_plan_create(ip, ix, light_threshold=T, chunk=C, waves_per_group=W,
+                                                  xcd_split=False))
+        assert off["n_xsplit_groups"] == 0 and off["n_xsplit_slots"] == 0
+    # rows not sorted: the plan keeps the plain groups only
+    rx2 = rx.copy()
+    big = int(np.argmax(np.diff(rp)))
+    rx2[rp[big]:rp[big + 1]] = rx2[rp[big]:rp[big + 1]][::-1]
+    d = g.gnn_plan_export(g.gnn_plan_create(ip, dev_i32(rx2)))
+    assert d["rows_sorted"] == 0 and d["n_xsplit_groups"] == 0
 
 
 def test_plan_rejects_inconsistent_graph(g):
