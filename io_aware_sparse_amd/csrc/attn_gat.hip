@@ -33,6 +33,8 @@ struct GatBwdParams {
     float *da_part;       // [n_chunks][H*D] column-sum partials
     float *d_att;         // [H][D] output
     int32_t n_chunks;
+    const int32_t *a_gperm;   // nullable: destination-pass launch slot -> heavy group (-1: none)
+    int32_t a_n_slots;        // destination-pass heavy launch slots (b.a_n_groups without a_gperm)
 };
 
 template <class T, int LH, bool SEPV, int U>
@@ -135,12 +137,19 @@ __global__ __launch_bounds__(512) void k_gat_bwd_dst_main(GatBwdParams GP) {
     extern __shared__ float lds[];
     const BwdParams &P = GP.b;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int heavy_blocks = P.a_n_groups * P.g.NHG;
+    const int heavy_blocks = GP.a_n_slots * P.g.NHG;
     const int64_t rowlen = (int64_t)P.g.H * P.g.D;
     if ((int)blockIdx.x < heavy_blocks) {
-        const int grp = blockIdx.x / P.g.NHG, hg = blockIdx.x % P.g.NHG;
+        int grp = blockIdx.x / P.g.NHG;
+        const int hg = blockIdx.x % P.g.NHG;
+        if (GP.a_gperm) {
+            grp = GP.a_gperm[grp];
+            if (grp < 0) return;
+        }
         const int node = P.a_groups[3 * grp], g0 = P.a_groups[3 * grp + 1], g1 = P.a_groups[3 * grp + 2];
-        const int e0 = min(g1, g0 + w * P.C), e1 = min(g1, e0 + P.C);
+        // source-range groups spread their entries evenly over the W waves
+        const int cw = GP.a_gperm ? (g1 - g0 + P.W - 1) / P.W : P.C;
+        const int e0 = min(g1, g0 + w * cw), e1 = min(g1, e0 + cw);
         const LanePos lp = lane_pos<LH, NV>(P.g, hg);
         float x[5][NV];
         float lse2;
@@ -398,7 +407,7 @@ static int run_gat_bwd(gnn_plan_t plan, GatBwdParams &GP, hipStream_t s) {
     const int LR = 1 << P.g.lr_shift;
     {
         const int64_t lb = ((int64_t)P.a_n_light * P.g.NHG + P.W - 1) / P.W;
-        const int64_t blocks = (int64_t)P.a_n_groups * P.g.NHG + lb;
+        const int64_t blocks = (int64_t)GP.a_n_slots * P.g.NHG + lb;
         if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
         const size_t lds = P.a_n_groups ? (size_t)P.W * LR * 5 * NV * sizeof(float) : 0;
         GNN_TRY(launch(plan, K_GAT_BWD_DST_MAIN, k_gat_bwd_dst_main<T, LH, SEPV, U>, dim3((unsigned)blocks),
@@ -484,6 +493,19 @@ static int gat_bwd_impl(gnn_plan_t plan, const int32_t *indptr, const int32_t *i
     GP.slope = negative_slope;
     GP.d_att = d_att;
     GP.n_chunks = (int32_t)((N + kColChunk - 1) / kColChunk);
+    GP.a_gperm = nullptr;
+    GP.a_n_slots = P.a_n_groups;
+    // the destination pass takes the forward's source-range groups under the
+    // forward's rule (one head group, a range of the gathered tables near an
+    // XCD's L2); its partial slots merge in the same fixed order
+    const int64_t gathered = (int64_t)N * H * D * (dtype == GNN_BF16 ? 2 : 4) * (sepv ? 2 : 1);
+    if (plan->xsplit.n_groups && P.g.NHG == 1 && (gathered + 7) / 8 <= kXsplitMaxRangeBytes) {
+        P.a_groups = as<int32_t>(plan->xsplit.groups);
+        P.a_ofs = as<int32_t>(plan->xsplit.partial_ofs);
+        P.a_n_groups = plan->xsplit.n_groups;
+        GP.a_gperm = as<int32_t>(plan->xsplit.order);
+        GP.a_n_slots = plan->xsplit.n_slots;
+    }
     const size_t rowlen = (size_t)H * D;
     const size_t n_stat = (size_t)N * H * 2;
     const size_t n_a = (size_t)P.a_n_groups * (4 * rowlen + H), n_b = (size_t)P.b_n_groups * 2 * rowlen;
