@@ -151,3 +151,35 @@ def test_alloc_cap_forces_oom_before_any_hip_call(g, monkeypatch):
     with pytest.raises(g.GnnError) as err:
         g._check(L.gnn_plan_create(A, A, 10, 20, None, None, C.byref(h)), "gnn_plan_create")
     assert err.value.status == -4 and "GNN_ERR_OOM" in str(err.value)
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The binding's ctypes mirrors of gnn_plan_opts and gnn_plan_info have
+    the header's size and every field's offset (a C program built from the
+    header with the host compiler prints them)."""
+    import shutil
+    import subprocess
+    import io_aware_sparse_amd as g
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    lines = []
+    for cname, py in (("gnn_plan_opts", g.PlanOpts), ("gnn_plan_info", g.PlanInfo)):
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"gnn_attn.h\"\nint main(void) {\n"
+                   + "\n".join(lines) + "\nreturn 0;\n}\n")
+    exe = tmp_path / "layout"
+    r = subprocess.run([cc, "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+                        str(src), "-o", str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        s, f, v = line.split()
+        got[(s, f)] = int(v)
+    for cname, py in (("gnn_plan_opts", g.PlanOpts), ("gnn_plan_info", g.PlanInfo)):
+        assert got[(cname, "size")] == C.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)

@@ -76,22 +76,37 @@ def _library_bytes(fn):
     return out, (free0 - free1) - (res1 - res0)
 
 
+XSPLIT_MAX_RANGE = 12 << 20     # the header's bound on one eighth of the gathered tables
+
+
+def _one_head_group(H, D, dtype):
+    return H <= 64 // (D // (8 if dtype == "bf16" else 4))
+
+
 def _ws_fwd(d, N, H, D, dtype="f32", gatv2=False):
     """Forward workspace: one partial (acc, m, l) per heavy group. The forward
     takes the source-range split groups when the plan has them, all heads fit
     one head group and one eighth of the gathered tables is at most 12 MiB
     (the rule the header states), else the plain groups."""
     size = 2 if dtype == "bf16" else 4
-    lanes = D // (8 if dtype == "bf16" else 4)
-    one_group = H <= 64 // lanes
     gathered = N * H * D * size * (1 if gatv2 else 2)
-    split = d["n_xsplit_groups"] > 0 and one_group and (gathered + 7) // 8 <= 12 << 20
+    split = d["n_xsplit_groups"] > 0 and _one_head_group(H, D, dtype) and (gathered + 7) // 8 <= XSPLIT_MAX_RANGE
     return (d["n_xsplit_groups"] if split else d["n_groups"]) * (H * D + 2 * H) * 4
 
 
-def _ws_bwd(d, N, H, D, gat):
+def _ws_bwd(d, N, H, D, gat, dtype="f32"):
+    """Backward workspace: (LSE, Delta) per node and head, the destination
+    pass's partials per heavy group, the source pass's per heavy source group,
+    and for GATv2 the per-node d_att terms and their column-sum partials. The
+    GATv2 destination pass takes the split groups under the forward's rule
+    (gathered: the XS rows)."""
     rowlen = H * D
-    n = 2 * N * H + d["n_groups"] * ((4 if gat else 2) * rowlen + H) + d["c_n_groups"] * 2 * rowlen
+    size = 2 if dtype == "bf16" else 4
+    na = d["n_groups"]
+    if gat and _one_head_group(H, D, dtype) and d["n_xsplit_groups"] > 0 \
+            and (N * rowlen * size + 7) // 8 <= XSPLIT_MAX_RANGE:
+        na = d["n_xsplit_groups"]
+    n = 2 * N * H + na * ((4 if gat else 2) * rowlen + H) + d["c_n_groups"] * 2 * rowlen
     if gat:
         n += N * rowlen + ((N + 63) // 64) * rowlen
     return n * 4
@@ -153,7 +168,7 @@ def test_memory_audit(g, name, tiles):
                 holder["bwd"] = g.gnn_attn_bwd(plan, ip, ix, q, k, v, O, go, L)
     _audit(g, plan, wl, E, "forward", fwd, _ws_fwd(d, N, H, D, wl.dtype, wl.kind == "gatv2"))
     if backward:
-        _audit(g, plan, wl, E, "backward", bwd, _ws_bwd(d, N, H, D, wl.kind == "gatv2"))
+        _audit(g, plan, wl, E, "backward", bwd, _ws_bwd(d, N, H, D, wl.kind == "gatv2", wl.dtype))
 
 
 def test_alloc_cap_fails_cleanly_midway(g, monkeypatch):
