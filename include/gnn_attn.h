@@ -99,10 +99,11 @@ typedef struct {
                                 equal source-id ranges into groups of at most C*W entries,
                                 each reading one range, and launch them so that the 8 XCDs
                                 each take one range (their L2s then hold what they gather);
-                                the forward uses them when a node's gathered rows (K, plus V
-                                unless it aliases K) over N/8 nodes take at most 12 MiB and
-                                all heads fit one head group; results differ from the plain
-                                groups by rounding only. 0: not built. Needs sorted rows    */
+                                the forward and the GATv2 backward's destination pass use
+                                them when the gathered rows (K, plus V unless it aliases K)
+                                of N/8 nodes take at most 12 MiB and all heads fit one head
+                                group; results differ from the plain groups by rounding only.
+                                0: not built. Needs sorted rows                             */
 } gnn_plan_opts;
 
 /* Fill *opts with the defaults above. Returns GNN_ERR_INVALID_ARG if opts is NULL. */
