@@ -96,9 +96,10 @@ typedef struct {
                                 floor(log2(degree)), then the rest by id. Outputs do not
                                 depend on it                                                   */
     int32_t xcd_split;       /* 1 (default): also cut the heavy rows at the boundaries of 8
-                                equal source-id ranges into groups of at most C*W entries,
-                                each reading one range, and launch them so that the 8 XCDs
-                                each take one range (their L2s then hold what they gather);
+                                equal source-id ranges into groups of at most C entries,
+                                each reading one range and streamed by one wave, and launch
+                                them so that the 8 XCDs each take one range (their L2s then
+                                hold what they gather);
                                 the forward and the GATv2 backward's destination pass use
                                 them when the gathered rows (K, plus V unless it aliases K)
                                 of N/8 nodes take at most 12 MiB and all heads fit one head
@@ -211,7 +212,7 @@ typedef struct {
     const int32_t *xsplit_groups;      /* [n_xsplit_groups][3] (node, e0, e1): for each heavy node
                                           in heavy_ids order, its entries of each source range r
                                           (sources in [r*ceil(N/8), (r+1)*ceil(N/8)), r = 0..7, in
-                                          order) cut into ceil(len / (C*W)) near-equal groups,
+                                          order) cut into ceil(len / C) near-equal groups,
                                           group j = [a + len*j/k, a + len*(j+1)/k)              */
     const int32_t *xsplit_partial_ofs; /* [n_heavy+1] group range of each heavy node             */
     const int32_t *xsplit_order;       /* [n_xsplit_slots] launch slot i*8 + r: the i-th group of

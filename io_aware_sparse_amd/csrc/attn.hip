@@ -31,6 +31,25 @@
 
 namespace gnn {
 
+// Heavy blocks at the head of the forward launch: one per (chunk group, head
+// group), or, in XCD order, 8 per W rows of slots (n_slots is 8 times the
+// largest range's group count)
+__host__ __device__ inline int64_t fwd_heavy_blocks(const FwdParams &P) {
+    return P.gperm ? 8 * (((int64_t)P.n_slots / 8 + P.W - 1) / P.W) : (int64_t)P.n_slots * P.g.NHG;
+}
+
+// a heavy group's partial online-softmax state (acc; m and l per head)
+template <int NV>
+__device__ __forceinline__ void write_partial(const FwdParams &P, const LanePos &lp, int grp, const SoftState<NV> &st) {
+    const int64_t rowlen = (int64_t)P.g.H * P.g.D;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) P.ws_acc[(int64_t)grp * rowlen + lp.col + k] = st.acc[k];
+    if (lp.dv == 0) {
+        P.ws_ml[((int64_t)grp * P.g.H + lp.h) * 2 + 0] = st.m;
+        P.ws_ml[((int64_t)grp * P.g.H + lp.h) * 2 + 1] = st.l;
+    }
+}
+
 // RPW > 1: the light rows run RPW per wave (rows of at most 64/RPW lanes).
 template <class T, int LH, int MODE, int U, int RPW>
 __global__ __launch_bounds__(512) void k_fwd_main(FwdParams P) {
@@ -38,18 +57,25 @@ __global__ __launch_bounds__(512) void k_fwd_main(FwdParams P) {
     constexpr int NV = VT::N;
     extern __shared__ float lds[];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int heavy_blocks = P.n_slots * P.g.NHG;
+    const int heavy_blocks = (int)fwd_heavy_blocks(P);
     if ((int)blockIdx.x < heavy_blocks) {
-        int grp = blockIdx.x / P.g.NHG;
-        const int hg = blockIdx.x % P.g.NHG;
         if (P.gperm) {
-            grp = P.gperm[grp];
-            if (grp < 0) return;              // an empty slot: the whole workgroup leaves
+            // XCD-ordered source-range groups (one head group): the block that
+            // dispatch puts on XCD r = blockIdx % 8 takes the next W groups of
+            // range r, one per wave; a wave streams its whole group and writes
+            // its own partial state (no barrier on this path)
+            const int slot = ((int)(blockIdx.x / 8) * P.W + w) * 8 + (int)(blockIdx.x % 8);
+            const int grp = slot < P.n_slots ? P.gperm[slot] : -1;
+            if (grp < 0) return;
+            const LanePos lp = lane_pos<LH, NV>(P.g, 0);
+            SoftState<NV> st;
+            fwd_stream<T, LH, MODE, U>(P, lp, P.groups[3 * grp], P.groups[3 * grp + 1], P.groups[3 * grp + 2], st);
+            if (lp.lane < (1 << P.g.lr_shift) && lp.act) write_partial(P, lp, grp, st);
+            return;
         }
+        const int grp = blockIdx.x / P.g.NHG, hg = blockIdx.x % P.g.NHG;
         const int node = P.groups[3 * grp], g0 = P.groups[3 * grp + 1], g1 = P.groups[3 * grp + 2];
-        // XCD-ordered groups split their span evenly over the W waves
-        const int cw = P.gperm ? (g1 - g0 + P.W - 1) / P.W : P.C;
-        const int e0 = min(g1, g0 + w * cw), e1 = min(g1, e0 + cw);
+        const int e0 = min(g1, g0 + w * P.C), e1 = min(g1, e0 + P.C);
         const LanePos lp = lane_pos<LH, NV>(P.g, hg);
         SoftState<NV> st;
         fwd_stream<T, LH, MODE, U>(P, lp, node, e0, e1, st);
@@ -71,14 +97,7 @@ __global__ __launch_bounds__(512) void k_fwd_main(FwdParams P) {
             for (int k = 0; k < NV; ++k) a2[k] = o[2 + k];
             merge_state(st, o[0], o[1], a2);
         }
-        if (!lp.act) return;
-        const int64_t rowlen = (int64_t)P.g.H * P.g.D;
-#pragma unroll
-        for (int k = 0; k < NV; ++k) P.ws_acc[(int64_t)grp * rowlen + lp.col + k] = st.acc[k];
-        if (lp.dv == 0) {
-            P.ws_ml[((int64_t)grp * P.g.H + lp.h) * 2 + 0] = st.m;
-            P.ws_ml[((int64_t)grp * P.g.H + lp.h) * 2 + 1] = st.l;
-        }
+        if (lp.act) write_partial(P, lp, grp, st);
         return;
     }
     // the packed rows come from the descending-degree list, which has no id
@@ -319,7 +338,7 @@ static int launch_fwd_main(gnn_plan_t plan, const FwdParams &P, hipStream_t s) {
     const int kind_main = MODE == M_GT ? K_FWD_MAIN : K_GAT_MAIN;
     const int64_t light_waves = RPW == 1 ? (int64_t)P.n_light * P.g.NHG
                                          : P.n_long + ((int64_t)P.n_light - P.n_long + RPW - 1) / RPW;
-    const int64_t blocks = (int64_t)P.n_slots * P.g.NHG + (light_waves + P.W - 1) / P.W;
+    const int64_t blocks = fwd_heavy_blocks(P) + (light_waves + P.W - 1) / P.W;
     if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
     const size_t lds = P.n_groups ? (size_t)P.W * (1 << P.g.lr_shift) * (NV + 2) * sizeof(float) : 0;
     return launch(plan, kind_main, k_fwd_main<T, LH, MODE, U, RPW>, dim3((unsigned)blocks), dim3(64 * P.W), lds, s,

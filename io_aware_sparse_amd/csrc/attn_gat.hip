@@ -37,6 +37,13 @@ struct GatBwdParams {
     int32_t a_n_slots;        // destination-pass heavy launch slots (b.a_n_groups without a_gperm)
 };
 
+// heavy blocks at the head of the destination-pass launch (as in the forward:
+// one per (chunk group, head group), or 8 per W rows of XCD-ordered slots)
+__host__ __device__ inline int64_t gat_dst_heavy_blocks(const GatBwdParams &GP) {
+    return GP.a_gperm ? 8 * (((int64_t)GP.a_n_slots / 8 + GP.b.W - 1) / GP.b.W)
+                      : (int64_t)GP.a_n_slots * GP.b.g.NHG;
+}
+
 template <class T, int LH, bool SEPV, int U>
 __device__ __forceinline__ void gat_dst_stream(const GatBwdParams &GP, const LanePos &lp, int node, int e0, int e1,
                                                float (&A)[Vec<T>::N], float (&B)[Vec<T>::N], float (&Cc)[Vec<T>::N],
@@ -137,26 +144,36 @@ __global__ __launch_bounds__(512) void k_gat_bwd_dst_main(GatBwdParams GP) {
     extern __shared__ float lds[];
     const BwdParams &P = GP.b;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int heavy_blocks = GP.a_n_slots * P.g.NHG;
+    const int heavy_blocks = (int)gat_dst_heavy_blocks(GP);
     const int64_t rowlen = (int64_t)P.g.H * P.g.D;
     if ((int)blockIdx.x < heavy_blocks) {
-        int grp = blockIdx.x / P.g.NHG;
-        const int hg = blockIdx.x % P.g.NHG;
+        int grp, e0, e1, hg = 0;
         if (GP.a_gperm) {
-            grp = GP.a_gperm[grp];
+            // XCD-ordered source-range groups, one per wave (as in the forward)
+            const int slot = ((int)(blockIdx.x / 8) * P.W + w) * 8 + (int)(blockIdx.x % 8);
+            grp = slot < GP.a_n_slots ? GP.a_gperm[slot] : -1;
             if (grp < 0) return;
+            e0 = P.a_groups[3 * grp + 1];
+            e1 = P.a_groups[3 * grp + 2];
+        } else {
+            grp = blockIdx.x / P.g.NHG;
+            hg = blockIdx.x % P.g.NHG;
+            const int g0 = P.a_groups[3 * grp + 1], g1 = P.a_groups[3 * grp + 2];
+            e0 = min(g1, g0 + w * P.C);
+            e1 = min(g1, e0 + P.C);
         }
-        const int node = P.a_groups[3 * grp], g0 = P.a_groups[3 * grp + 1], g1 = P.a_groups[3 * grp + 2];
-        // source-range groups spread their entries evenly over the W waves
-        const int cw = GP.a_gperm ? (g1 - g0 + P.W - 1) / P.W : P.C;
-        const int e0 = min(g1, g0 + w * cw), e1 = min(g1, e0 + cw);
+        const int node = P.a_groups[3 * grp];
         const LanePos lp = lane_pos<LH, NV>(P.g, hg);
         float x[5][NV];
         float lse2;
         gat_dst_stream<T, LH, SEPV, U>(GP, lp, node, e0, e1, x[0], x[1], x[2], x[3], x[4][0], lse2);
 #pragma unroll
         for (int k = 1; k < NV; ++k) x[4][k] = 0.f;
-        if (!lds_sum_waves<NV, 5>(lds, w, P.W, lp.lane, 1 << P.g.lr_shift, x) || !lp.act) return;
+        if (GP.a_gperm) {
+            if (lp.lane >= (1 << P.g.lr_shift) || !lp.act) return;    // no barrier on this path
+        } else if (!lds_sum_waves<NV, 5>(lds, w, P.W, lp.lane, 1 << P.g.lr_shift, x) || !lp.act) {
+            return;
+        }
         float *slot = P.ws_a + (int64_t)grp * (4 * rowlen + P.g.H);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
@@ -182,37 +199,42 @@ template <class T, int LH>
 __global__ __launch_bounds__(256) void k_gat_bwd_dst_merge(GatBwdParams GP) {
     using VT = Vec<T>;
     constexpr int NV = VT::N;
+    extern __shared__ float lds[];
     const BwdParams &P = GP.b;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t item = (int64_t)blockIdx.x * (blockDim.x / kWave) + w;
-    if (item >= (int64_t)P.a_n_heavy * P.g.NHG) return;
+    const int nw = blockDim.x / kWave;
+    // one block per (heavy node, head group): wave w takes partials
+    // p0 + w*G + g, stepping nw*G, so a hub's long list is summed by nw
+    // waves at once; the waves are then summed in LDS in ascending order
+    const int64_t item = blockIdx.x;
+    if (item >= (int64_t)P.a_n_heavy * P.g.NHG) return;      // the whole block
     const int k = (int)(item / P.g.NHG), hg = (int)(item % P.g.NHG);
     const int node = P.a_heavy[k];
     const int p0 = P.a_ofs[k], p1 = P.a_ofs[k + 1];
     const LanePos lp = lane_pos<LH, NV>(P.g, hg);
     const int64_t rowlen = (int64_t)P.g.H * P.g.D;
-    float x[4][NV];
-    float dsum = 0.f, lse2 = -INFINITY;
+    float x[5][NV];                  // A, B, C, E and (Delta, 0, ...)
+    float lse2 = -INFINITY;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 5; ++a)
 #pragma unroll
         for (int q = 0; q < NV; ++q) x[a][q] = 0.f;
     if (lp.act) {
-        for (int p = p0 + lp.g; p < p1; p += P.g.G) {
+        for (int p = p0 + w * P.g.G + lp.g; p < p1; p += nw * P.g.G) {
             const float *slot = P.ws_a + (int64_t)p * (4 * rowlen + P.g.H);
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int q = 0; q < NV; ++q) x[a][q] += slot[a * rowlen + lp.col + q];
-            dsum += slot[4 * rowlen + lp.h];
+            x[4][0] += slot[4 * rowlen + lp.h];
         }
         lse2 = P.LSE[(int64_t)node * P.g.H + lp.h] * kLog2e;
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a) sum_groups(x[a], P.g.lr_shift);
-    for (int off = 1 << P.g.lr_shift; off < kWave; off <<= 1) dsum += xor_lane(dsum, off);
-    if (lp.g != 0 || !lp.act) return;
-    gat_dst_finish<T, NV>(GP, lp, node, x[0], x[1], x[2], x[3], dsum, lse2);
+    for (int off = 1 << P.g.lr_shift; off < kWave; off <<= 1) x[4][0] += xor_lane(x[4][0], off);
+    if (!lds_sum_waves<NV, 5>(lds, w, nw, lp.lane, 1 << P.g.lr_shift, x) || !lp.act) return;
+    gat_dst_finish<T, NV>(GP, lp, node, x[0], x[1], x[2], x[3], x[4][0], lse2);
 }
 
 template <class T, int LH, bool SEPV, int U>
@@ -407,14 +429,16 @@ static int run_gat_bwd(gnn_plan_t plan, GatBwdParams &GP, hipStream_t s) {
     const int LR = 1 << P.g.lr_shift;
     {
         const int64_t lb = ((int64_t)P.a_n_light * P.g.NHG + P.W - 1) / P.W;
-        const int64_t blocks = (int64_t)GP.a_n_slots * P.g.NHG + lb;
+        const int64_t blocks = gat_dst_heavy_blocks(GP) + lb;
         if (blocks >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
         const size_t lds = P.a_n_groups ? (size_t)P.W * LR * 5 * NV * sizeof(float) : 0;
         GNN_TRY(launch(plan, K_GAT_BWD_DST_MAIN, k_gat_bwd_dst_main<T, LH, SEPV, U>, dim3((unsigned)blocks),
                        dim3(64 * P.W), lds, s, GP));
-        if (P.a_n_heavy)
-            GNN_TRY(launch(plan, K_GAT_BWD_DST_MERGE, k_gat_bwd_dst_merge<T, LH>,
-                           dim3((unsigned)(((int64_t)P.a_n_heavy * P.g.NHG + 3) / 4)), dim3(256), 0, s, GP));
+        const int64_t mb = (int64_t)P.a_n_heavy * P.g.NHG;
+        if (mb >= (1ll << 31)) return GNN_ERR_INVALID_ARG;
+        if (mb)
+            GNN_TRY(launch(plan, K_GAT_BWD_DST_MERGE, k_gat_bwd_dst_merge<T, LH>, dim3((unsigned)mb), dim3(256),
+                           (size_t)4 * LR * 5 * NV * sizeof(float), s, GP));
     }
     {
         const int64_t lb = ((int64_t)P.b_n_light * P.g.NHG + P.W - 1) / P.W;

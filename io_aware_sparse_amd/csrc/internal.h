@@ -63,12 +63,13 @@ struct Buckets {
 };
 
 // The forward's heavy rows cut at the boundaries of 8 equal source-id ranges
-// and then into groups of at most C*W entries: every group reads sources of
-// one range only. Launch slot i*8 + r holds the i-th group of range r (-1
-// when range r has fewer), so with one block per slot and blocks dealt to the
-// 8 XCDs round-robin, each XCD gathers from one eighth of the table and its
-// L2 holds much more of what it reads. Partial slots stay per node and
-// contiguous (partial_ofs), so the merge is unchanged.
+// and then into groups of at most C entries, each streamed by one wave:
+// every group reads sources of one range only. Launch slot i*8 + r holds the
+// i-th group of range r (-1 when range r has fewer); the kernels give block b
+// the slots of range b % 8, and blocks are dealt to the 8 XCDs round-robin,
+// so each XCD gathers from one eighth of the table and its L2 holds much more
+// of what it reads. Partial slots stay per node and contiguous (partial_ofs),
+// so the merge is unchanged.
 struct XSplit {
     int32_t n_groups = 0, n_slots = 0;
     DevBuf groups, partial_ofs, order;

@@ -654,7 +654,7 @@ static int build_xsplit(gnn_plan_s *p, hipStream_t s) {
     XSplit &x = p->xsplit;
     if (b.n_heavy == 0 || !p->rows_sorted) return GNN_OK;
     const int32_t R = (int32_t)((p->n_nodes + 7) / 8);
-    const int64_t span = (int64_t)p->opts.chunk * p->opts.waves_per_group;
+    const int64_t span = p->opts.chunk;
     DevBuf pos;
     GNN_TRY(dev_alloc(pos, (size_t)b.n_heavy * 9 * 4));
     hipLaunchKernelGGL(k_range_bounds, grid1d((int64_t)b.n_heavy * 9), dim3(256), 0, s, p->indptr, p->indices,

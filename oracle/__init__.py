@@ -152,13 +152,13 @@ def bucketing(indptr, threshold: int, chunk: int, waves: int):
                 groups=groups.astype(np.int32), partial_ofs=partial_ofs.astype(np.int32))
 
 
-def xsplit(indptr, indices, heavy, n_nodes: int, chunk: int, waves: int):
+def xsplit(indptr, indices, heavy, n_nodes: int, chunk: int):
     """Source-range split of the heavy rows (plan option xcd_split).
 
     The node ids split into 8 ranges of R = ceil(N / 8) ids (range r holds
     sources r*R .. (r+1)*R - 1). For each heavy node in the given order, each
     range's part of its (ascending) entries, a contiguous run of len entries
-    starting at position a, becomes k = ceil(len / (chunk * waves)) groups
+    starting at position a, becomes k = ceil(len / chunk) groups
     (node, a + len*j // k, a + len*(j+1) // k), j = 0..k-1; empty parts give
     none. partial_ofs[k] .. partial_ofs[k+1] are node k's groups. The launch
     order puts the i-th group of range r at slot 8*i + r and -1 in the slots
@@ -169,7 +169,7 @@ def xsplit(indptr, indices, heavy, n_nodes: int, chunk: int, waves: int):
     ip = np.asarray(indptr, np.int64)
     ix = np.asarray(indices, np.int64)
     R = -(-int(n_nodes) // 8)
-    span = int(chunk) * int(waves)
+    span = int(chunk)
     groups, pofs, per_range = [], [0], [[] for _ in range(8)]
     for node in np.asarray(heavy, np.int64):
         e0, e1 = int(ip[node]), int(ip[node + 1])

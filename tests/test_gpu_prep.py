@@ -85,7 +85,7 @@ def test_buckets_and_csc(g, T, C, W, order):
     assert d["n_light"] + d["n_heavy"] == n
     # the source-range split of the heavy rows (built by default on sorted rows)
     if ref["heavy"].size:
-        xref = oracle.xsplit(rp, rx, ref["heavy"], n, C, W)
+        xref = oracle.xsplit(rp, rx, ref["heavy"], n, C)
         for k in ("groups", "partial_ofs", "order"):
             assert np.array_equal(d["xsplit_" + k], xref[k]), "xsplit_" + k
     else:
@@ -109,7 +109,7 @@ def test_xsplit(g, name, n):
         if heavy.size == 0:
             assert d["n_xsplit_groups"] == 0
         else:
-            xref = oracle.xsplit(rp, rx, heavy, n, C, W)
+            xref = oracle.xsplit(rp, rx, heavy, n, C)
             for k in ("groups", "partial_ofs", "order"):
                 assert np.array_equal(d["xsplit_" + k], xref[k]), ("xsplit_" + k, T)
         off = g.gnn_plan_export(g.gnn_plan_create(ip, ix, light_threshold=T, chunk=C, waves_per_group=W,

@@ -1,7 +1,7 @@
 """Pins of the oracle's source-range split of the heavy rows (plan option
 xcd_split): a hand-worked example, and the properties its definition fixes
 on random graphs (each heavy row covered exactly once in order, every group
-within one source range and at most C*W entries, near-equal groups inside a
+within one source range and at most C entries, near-equal groups inside a
 range's part, and the launch order's slot i*8 + r holding range r's i-th
 group)."""
 import numpy as np
@@ -13,7 +13,7 @@ import oracle
 def test_hand_worked_example():
     # N = 16, so R = 2 ids per range. Row 3 (entries 10..16) lists sources
     # 0 1 | 3 | 4 5 | 9 | 15 in ranges 0, 1, 2, 4, 7; row 7 (entries 17..21)
-    # lists source 2 five times (range 1). C * W = 2: the five entries of row 7
+    # lists source 2 five times (range 1). C = 2: the five entries of row 7
     # in range 1 make ceil(5/2) = 3 groups [17,18) [18,20) [20,22)
     # (17 + 5*j//3 for j = 0..3 gives 17, 18, 20, 22).
     rows = {0: [0, 1, 2, 3, 4], 1: [1, 2, 3], 2: [5, 6], 3: [0, 1, 3, 4, 5, 9, 15], 7: [2, 2, 2, 2, 2]}
@@ -23,7 +23,7 @@ def test_hand_worked_example():
     ip = np.concatenate([[0], np.cumsum(deg)])
     ix = np.concatenate([rows[r] for r in sorted(rows)]).astype(np.int32)
     assert ip[3] == 10 and ip[7] == 17 and ip[16] == 22
-    x = oracle.xsplit(ip, ix, np.array([3, 7]), 16, chunk=1, waves=2)
+    x = oracle.xsplit(ip, ix, np.array([3, 7]), 16, chunk=2)
     want_groups = [(3, 10, 12), (3, 12, 13), (3, 13, 15), (3, 15, 16), (3, 16, 17),
                    (7, 17, 18), (7, 18, 20), (7, 20, 22)]
     assert x["groups"].tolist() == [list(g) for g in want_groups]
@@ -46,9 +46,9 @@ def test_properties(seed, n, chunk, waves):
     rng = np.random.default_rng(seed)
     ip, ix = _sorted_random_graph(rng, n, hubs=min(5, n))
     heavy = oracle.bucketing(ip, 100, chunk, waves)["heavy"]
-    x = oracle.xsplit(ip, ix, heavy, n, chunk, waves)
+    x = oracle.xsplit(ip, ix, heavy, n, chunk)
     g, pofs, order = x["groups"].astype(np.int64), x["partial_ofs"], x["order"]
-    R, span = -(-n // 8), chunk * waves
+    R, span = -(-n // 8), chunk
     assert pofs[0] == 0 and pofs[-1] == len(g) and np.all(np.diff(pofs) >= 1)
     rng_of = np.empty(len(g), np.int64)
     for k, node in enumerate(heavy):
