@@ -298,3 +298,42 @@ def test_gatv2_bwd_deterministic(g):
     r2 = [t.clone() for t in g.gatv2_attn_bwd(pl, ip, ix, xd, xs, a, go, L) if t is not None]
     for x, y in zip(r1, r2):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("dtype,D,H", [("f32", 16, 8), ("bf16", 32, 4)])
+def test_heavy_groups_with_and_without_source_range_split(g, split, dtype, D, H):
+    """Heavy rows on sorted rows with one head group, the plan's source-range
+    groups in XCD order (xcd_split on) and the plain chunk groups (off): GT
+    forward and backward, GATv2 forward and backward, each against the
+    oracle."""
+    import torch
+    n = 3000
+    say("heavy groups", "split" if split else "plain", dtype, D, H)
+    ip, ix, rp, rx = _graph(g, 14, n)
+    opts = dict(light_threshold=12, chunk=7, waves_per_group=4, want_csc=True)
+    pl = g.gnn_plan_create(ip, ix, xcd_split=split, **opts)
+    d = g.gnn_plan_export(pl)
+    assert d["n_groups"] > 0 and d["rows_sorted"] == 1
+    assert (d["n_xsplit_groups"] > 0) == split
+    rng = np.random.default_rng(31 + D)
+    Q, K, V, dO = rand_feats(rng, n, H, D, dtype, k=4)
+    q, k, v, go = (dev_feat(x, dtype) for x in (Q, K, V, dO))
+    O, L = g.gnn_attn_fwd(pl, ip, ix, q, k, v)
+    ref = oracle.gt_fwd(rp, rx, Q, K, V)
+    _check("GT O", host(O), ref["O"], ref["SO"], dtype)
+    _check("GT LSE", host(L), ref["LSE"], ref["SL"], "f32")
+    dq, dk, dv = g.gnn_attn_bwd(pl, ip, ix, q, k, v, O, go, L)
+    rb = oracle.gt_bwd(rp, rx, Q, K, V, dO)
+    for nm, x in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        _check(f"GT {nm}", host(x), rb[nm], rb["S" + nm], dtype)
+    att = (rng.standard_normal((H, D)) / np.sqrt(D)).astype(np.float32)
+    a = torch.from_numpy(att).cuda()
+    GO, GL = g.gatv2_attn_fwd(pl, ip, ix, q, k, a)
+    rg = oracle.gatv2_fwd(rp, rx, Q, K, att, slope=0.2)
+    _check("GATv2 O", host(GO), rg["O"], rg["SO"], dtype)
+    gxd, gxs, _, gda = g.gatv2_attn_bwd(pl, ip, ix, q, k, a, go, GL)
+    rgb = oracle.gatv2_bwd(rp, rx, Q, K, att, dO, slope=0.2)
+    _check("GATv2 dXD", host(gxd), rgb["dXD"], rgb["SdXD"], dtype)
+    _check("GATv2 dXS", host(gxs), rgb["dXS"], rgb["SdXS"], dtype)
+    _check("GATv2 d_att", gda.cpu().numpy(), rgb["d_att"], rgb["Sd_att"], dtype)
